@@ -1,0 +1,193 @@
+"""CPU oracle for MXFP4 block quantization and MXFP4 attention.
+
+TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``mxfp4_block_quantized_amd``) never imports it, and it never imports the GPU
+library; the two share no code.
+
+The arithmetic lives in ``mxoracle.c`` (plain C, binary64, OpenMP over rows and
+blocks).  This module only builds it with gcc and marshals numpy arrays.
+What each function computes, with its sources, is documented in the C file:
+
+* the OCP scale rule and Universal Optimal Scaling (boundary 7.25) --
+  "MXAttention: Data-Free Optimal Scaling and Pre-Normalization Quantization
+  for MXFP4 Attention", abstract;
+* rounding onto the eight E2M1 magnitudes with an exact power-of-two scale --
+  "Quantization Error", section "Where the error comes from";
+* the online-softmax loop with one quantized probability operand feeding both
+  numerator and denominator -- "EFQ-Softmax", abstract, and the PNQ component
+  of the MXAttention abstract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxoracle.c")
+_LIB = os.path.join(_HERE, "_liboracle.so")
+
+F32, BF16 = 0, 1
+RULE_OCP, RULE_UOS = 0, 1
+MODE_FP16, MODE_OCP, MODE_UOS, MODE_UOS_PNQ = 0, 1, 2, 3
+BLOCK = 32
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``mxoracle.c`` into ``_liboracle.so`` with gcc."""
+    if force or not os.path.exists(_LIB):
+        cmd = [
+            "gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
+            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+            _SRC, "-o", _LIB + ".tmp", "-lm",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    lib.oracle_scale_exponent.argtypes = [ctypes.c_double, ci]
+    lib.oracle_scale_exponent.restype = ci
+    lib.oracle_round_e2m1.argtypes = [ctypes.c_double]
+    lib.oracle_round_e2m1.restype = ci
+    lib.oracle_quantize.argtypes = [P, ci, i64, ci, P, P]
+    lib.oracle_quantize.restype = ci
+    lib.oracle_quantize_t.argtypes = [P, ci, i64, i64, ci, P, P]
+    lib.oracle_quantize_t.restype = ci
+    lib.oracle_dequantize.argtypes = [P, P, i64, P]
+    lib.oracle_dequantize.restype = ci
+    lib.oracle_attn_rows.argtypes = [P, P, P, ci] + [ci] * 9 + [P, i64, P, P, P, P, P, P]
+    lib.oracle_attn_rows.restype = ci
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_input(x):
+    """Return (contiguous array, dtype code).  bf16 data is passed as its raw
+    uint16 bit pattern; fp32 as float32."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16:
+        return x, BF16
+    raise TypeError("oracle inputs are float32 arrays or bf16 bit patterns (uint16)")
+
+
+def scale_exponent(amax: float, rule: int) -> int:
+    """Scale exponent e of a block whose largest magnitude is ``amax``."""
+    return _load().oracle_scale_exponent(float(amax), int(rule))
+
+
+def round_e2m1(v: float) -> int:
+    """3-bit E2M1 magnitude code of a non-negative scaled value."""
+    return _load().oracle_round_e2m1(float(v))
+
+
+def quantize(x, rule: int):
+    """Blocks of 32 along the flattened contiguous axis.
+
+    Returns (codes uint8[n/2], scales uint8[n/32])."""
+    x, dt = _as_input(x)
+    n = x.size
+    codes = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // BLOCK, np.uint8)
+    rc = _load().oracle_quantize(_ptr(x), dt, n, int(rule), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle_quantize: n must be a multiple of 32")
+    return codes, scales
+
+
+def quantize_t(x, rule: int):
+    """Blocks of 32 along the rows of a [rows, cols] matrix, output
+    transposed: (codes [cols, rows_pad/2], scales [cols, rows_pad/32])."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    rp = (rows + BLOCK - 1) // BLOCK * BLOCK
+    codes = np.empty((cols, rp // 2), np.uint8)
+    scales = np.empty((cols, rp // BLOCK), np.uint8)
+    rc = _load().oracle_quantize_t(_ptr(x), dt, rows, cols, int(rule), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle_quantize_t: bad shape")
+    return codes, scales
+
+
+def dequantize(codes, scales):
+    """Binary64 values of packed codes under their E8M0 bytes."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    n = codes.size * 2
+    y = np.empty(n, np.float64)
+    rc = _load().oracle_dequantize(_ptr(codes), _ptr(scales), n, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_dequantize: bad sizes")
+    return y
+
+
+def attn_rows(q, k, v, *, causal: bool, mode: int, bc: int, rows,
+              want_p: bool = False, want_tiles: bool = False):
+    """Attention output rows, binary64.
+
+    q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (float32 or bf16 bits as uint16).
+    ``rows``: flattened (b*Hq + h)*Sq + i indices.  ``bc``: keys per KV
+    tile (the running-max schedule).  Returns a dict with ``o`` [n, D],
+    ``l`` [n], ``m`` [n] and, on request, ``p_codes``/``p_scales`` and
+    ``m_tiles``."""
+    q, dt = _as_input(q)
+    k, dt2 = _as_input(k)
+    v, dt3 = _as_input(v)
+    if not (dt == dt2 == dt3):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch")
+    rows = np.ascontiguousarray(rows, np.int64)
+    n = rows.size
+    o = np.empty((n, D), np.float64)
+    l_out = np.empty(n, np.float64)
+    m_out = np.empty(n, np.float64)
+    skv_pad = (Skv + BLOCK - 1) // BLOCK * BLOCK
+    ntiles = (Skv + bc - 1) // bc
+    pc = np.empty((n, skv_pad // 2), np.uint8) if want_p else None
+    ps = np.empty((n, skv_pad // BLOCK), np.uint8) if want_p else None
+    mt = np.empty((n, ntiles), np.float64) if want_tiles else None
+    rc = _load().oracle_attn_rows(
+        _ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+        int(mode), int(bc), _ptr(rows), n, _ptr(o), _ptr(l_out), _ptr(m_out),
+        _ptr(mt), _ptr(pc), _ptr(ps))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_rows failed ({rc})")
+    res = {"o": o, "l": l_out, "m": m_out}
+    if want_p:
+        res["p_codes"], res["p_scales"] = pc, ps
+    if want_tiles:
+        res["m_tiles"] = mt
+    return res
+
+
+def unpack_codes(codes):
+    """Split packed bytes into 4-bit codes (element 2j = low nibble)."""
+    codes = np.asarray(codes, np.uint8)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = codes & 0xF
+    out[..., 1::2] = codes >> 4
+    return out
