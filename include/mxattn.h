@@ -1,0 +1,189 @@
+/*
+ * mxattn.h -- C ABI of the MXFP4 block quantizer and MXFP4 attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *  - MXFP4 blocks: 32 consecutive elements share one power-of-two E8M0 scale
+ *    2^(X-127); each element is an E2M1 code (magnitudes 0, 0.5, 1, 1.5, 2,
+ *    3, 4, 6 plus a sign bit).  Rounding onto those magnitudes is the only
+ *    error; the scale applies exactly ("Quantization Error", section "Where
+ *    the error comes from"; OCP Microscaling Formats v1.0).
+ *  - Scale rules: OCP (the baseline) chooses the smallest exponent e with
+ *    amax < 8 * 2^e; Universal Optimal Scaling (UOS) chooses the smallest e
+ *    with amax <= 7.25 * 2^e ("MXAttention: Data-Free Optimal Scaling and
+ *    Pre-Normalization Quantization for MXFP4 Attention", abstract:
+ *    boundary Qmax = 7.25).  e is clamped to >= -127; an all-zero block gets
+ *    X = 0.  Elements round to the nearest magnitude, ties to the even code,
+ *    saturating at 6.
+ *  - Attention: QK^T and P~V as block-scaled FP4 contractions inside a
+ *    FlashAttention-style online softmax whose row-max update, history
+ *    rescaling, fp32 accumulation and final normalization are unchanged
+ *    ("EFQ-Softmax", abstract).  In UOS+PNQ mode the unnormalized
+ *    exponentials exp(s - m) are quantized in blocks of 32 keys before the
+ *    row sum, and the same P~ feeds both the numerator P~V and the
+ *    denominator P~1 (MXAttention abstract, Pre-Normalization
+ *    Quantization).  In the OCP and UOS modes P is quantized with the same
+ *    rule for P~V but the denominator sums the unquantized P.
+ *
+ * Layout conventions.
+ *  - Packed codes: element 2j in the low nibble of byte j, element 2j+1 in
+ *    the high nibble; bit 3 of a code is the sign.  Scales: one byte per 32
+ *    elements.
+ *  - Attention tensors are contiguous [B, H, S, D] (row-major, D fastest).
+ *    Query head h reads KV head h / (Hq / Hkv).  Softmax scale 1/sqrt(D).
+ *    Causal masking keeps keys j <= i and requires Sq == Skv.
+ *
+ * Ownership and errors.
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    where marked host.  The library never allocates, frees or synchronizes;
+ *    all work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream) and returns before it completes.
+ *  - Arguments are validated before any HIP call.  Functions return MX_OK or
+ *    a negative mx_status; a failed launch returns MX_ERR_HIP.  Device
+ *    pointers must be 16-byte aligned unless stated otherwise
+ *    (MX_ERR_ALIGN).
+ */
+#ifndef MXATTN_H
+#define MXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mx_status {
+    MX_OK = 0,
+    MX_ERR_ARG = -1,         /* null pointer, bad enum, bad size */
+    MX_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. D not 64/128) */
+    MX_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+    MX_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+    MX_ERR_ALIGN = -5        /* a device pointer is not 16-byte aligned */
+};
+
+enum mx_dtype { MX_F32 = 0, MX_BF16 = 1 };
+enum mxq_mode { MXQ_OCP = 0, MXQ_UOS = 1 };
+enum mxattn_mode { MXATTN_FP16 = 0, MXATTN_OCP = 1, MXATTN_UOS = 2, MXATTN_UOS_PNQ = 3 };
+
+/* Human-readable text of a status code (static storage). */
+const char *mx_strerror(int status);
+
+/*
+ * Block-quantize a flat tensor along its contiguous axis.
+ *  x      [n] elements of `dtype` (MX_F32 or MX_BF16)
+ *  n      element count, n % 32 == 0, n >= 0 (n == 0 is a no-op)
+ *  mode   MXQ_OCP or MXQ_UOS (scale rule)
+ *  codes  [n/2] bytes out;  scales [n/32] bytes out (E8M0)
+ * Inputs must be finite (NaN/Inf give unspecified codes).
+ */
+int mxq_quantize(const void *x, int64_t n, int dtype, int mode,
+                 uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * Block-quantize `batch` row-major matrices [rows][cols] along their ROWS
+ * (blocks of 32 consecutive rows in one column) and store them transposed:
+ *  codes_t  [batch][cols][rows_pad/2],  scales_t [batch][cols][rows_pad/32]
+ * rows_pad: output row length in elements; 0 means ceil(rows/32)*32;
+ * otherwise a multiple of 32 that is >= rows.  Rows beyond `rows` are
+ * quantized as zeros (codes 0, scale byte 0 for all-padding blocks).
+ * This is the layout of V~ (blocks along keys) in MXFP4 attention.
+ */
+int mxq_quantize_t(const void *x, int64_t batch, int64_t rows, int64_t cols,
+                   int dtype, int mode, int64_t rows_pad, uint8_t *codes_t,
+                   uint8_t *scales_t, void *stream);
+
+/*
+ * Dequantize n elements (n % 32 == 0) to `out_dtype` (MX_F32 or MX_BF16):
+ * y = sign * magnitude(code) * 2^(X-127).  Exact unless the value lies
+ * outside the output type's range (then +-inf) or X == 255 (NaN).
+ */
+int mxq_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n,
+                   int out_dtype, void *y, void *stream);
+
+/*
+ * Workspace needed by mxattn_fwd for these sizes and mode (bytes; 0 for
+ * invalid arguments).  The workspace holds the quantized operands (MX modes)
+ * or the 16-bit operands (FP16 mode).
+ */
+size_t mxattn_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                              int dtype, int mode);
+
+/*
+ * Byte offsets, inside the workspace, of the quantized operands of an MX
+ * mode (host array `off` of 6 entries):
+ *   off[0] Q~ codes  [B][Hq][Sq][D/2]        off[1] Q~ scales [B][Hq][Sq][D/32]
+ *   off[2] K~ codes  [B][Hkv][Skv][D/2]      off[3] K~ scales [B][Hkv][Skv][D/32]
+ *   off[4] V~^T codes  [B][Hkv][D][skv_ld/2] off[5] V~^T scales [B][Hkv][D][skv_ld/32]
+ * and *skv_ld (host) = the key length of each V~^T row (a multiple of the KV
+ * tile, zero-padded beyond Skv).  Returns MX_ERR_ARG for the FP16 mode.
+ */
+int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                            int dtype, int mode, size_t *off, int64_t *skv_ld);
+
+/*
+ * Keys per KV tile (Bc) of the attention kernel for this head size and mode.
+ * The running max -- and hence the scale of every P~ block -- is updated
+ * once per tile, in ascending key order, so a reference must use the same
+ * Bc to reproduce P~.  Returns a negative status for unsupported D.
+ */
+int mxattn_kv_tile(int D, int mode);
+
+/*
+ * Attention forward.
+ *  q [B][Hq][Sq][D], k and v [B][Hkv][Skv][D], contiguous, dtype MX_F32 or
+ *  MX_BF16.  D in {64, 128}; Hq % Hkv == 0; Sq, Skv >= 1; causal (0/1)
+ *  requires Sq == Skv.
+ *  o [B][Hq][Sq][D] fp32 out.
+ *  workspace: >= mxattn_workspace_bytes(...) bytes, 256-byte aligned,
+ *  overwritten.  Modes: MXATTN_FP16 (16-bit operands, no quantization),
+ *  MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ.
+ * In the MX modes the call first quantizes Q and K (blocks along D) and V
+ * (blocks along keys, transposed) into the workspace, then runs the fused
+ * attention kernel.  In FP16 mode, V (and, for fp32 inputs, Q and K) is
+ * first converted to fp16 in the workspace.
+ */
+int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
+               int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+               int mode, float *o, void *workspace, size_t ws_bytes,
+               void *stream);
+
+/*
+ * The two halves of mxattn_fwd, for callers that reuse prepared operands or
+ * time the attention kernel alone.
+ * mxattn_prepare: fills the workspace -- MX modes: Q~ and K~ (blocks along
+ * D) and V~^T (blocks along keys, transposed; see mxattn_workspace_layout);
+ * FP16 mode: fp16 V^T (and fp16 Q, K for fp32 inputs).
+ * mxattn_fwd_prepared: the fused attention kernel alone, reading the
+ * operands a previous mxattn_prepare with the same sizes, dtype and mode
+ * left in the workspace (q and k are read directly only in FP16 mode with
+ * bf16 inputs; they may be NULL in the MX modes).  Arguments as for
+ * mxattn_fwd.  mxattn_fwd == mxattn_prepare followed by mxattn_fwd_prepared.
+ */
+int mxattn_prepare(const void *q, const void *k, const void *v, int dtype,
+                   int B, int Hq, int Hkv, int Sq, int Skv, int D, int mode,
+                   void *workspace, size_t ws_bytes, void *stream);
+int mxattn_fwd_prepared(const void *q, const void *k, int dtype, int B,
+                        int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                        int mode, float *o, const void *workspace,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * mxattn_fwd plus a dump of the quantized probabilities P~ of selected rows
+ * (MX modes only; slower).  row_slot [B*Hq*Sq] int32: for query row
+ * (b*Hq + h)*Sq + i, the dump slot (>= 0) or -1.  p_codes
+ * [nslots][skv_ld/2] and p_scales [nslots][skv_ld/32] receive, for every
+ * key block a slot's row visits, its packed codes and E8M0 byte; blocks the
+ * row never visits (beyond the causal diagonal tile) are left untouched.
+ */
+int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
+                    int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                    int mode, float *o, void *workspace, size_t ws_bytes,
+                    const int32_t *row_slot, uint8_t *p_codes,
+                    uint8_t *p_scales, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXATTN_H */

@@ -1,0 +1,248 @@
+"""Python binding of ``libmxattn.so``: MXFP4 block quantization and MXFP4
+attention (OCP, UOS, UOS+PNQ and the unquantized FP16 mode) on gfx950.
+
+This module only marshals arguments: it takes PyTorch device tensors (used
+for memory and streams), passes their pointers to the C ABI declared in
+``include/mxattn.h`` and raises on any non-zero status.  Every step of the
+computation runs in the HIP kernels of ``csrc/``.  There is no CPU path: if
+the library is missing this module raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxattn.so")
+
+MX_F32, MX_BF16 = 0, 1
+MXQ_OCP, MXQ_UOS = 0, 1
+MXATTN_FP16, MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ = 0, 1, 2, 3
+MODES = {"fp16": MXATTN_FP16, "ocp": MXATTN_OCP, "uos": MXATTN_UOS, "uos_pnq": MXATTN_UOS_PNQ}
+RULES = {"ocp": MXQ_OCP, "uos": MXQ_UOS}
+
+# Symbols the header declares; the CPU tests check the library exports them.
+EXPORTS = (
+    "mx_strerror", "mxq_quantize", "mxq_quantize_t", "mxq_dequantize",
+    "mxattn_workspace_bytes", "mxattn_workspace_layout", "mxattn_kv_tile",
+    "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare", "mxattn_fwd_prepared",
+)
+
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({lib().mx_strerror(status).decode()})")
+        self.status = status
+
+
+def lib():
+    """Load ``libmxattn.so`` (built by ``build.py``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m mxfp4_block_quantized_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.mx_strerror.argtypes = [ci]
+    L.mx_strerror.restype = ctypes.c_char_p
+    L.mxq_quantize.argtypes = [P, i64, ci, ci, P, P, P]
+    L.mxq_quantize_t.argtypes = [P, i64, i64, i64, ci, ci, i64, P, P, P]
+    L.mxq_dequantize.argtypes = [P, P, i64, ci, P, P]
+    L.mxattn_workspace_bytes.argtypes = [ci] * 8
+    L.mxattn_workspace_bytes.restype = sz
+    L.mxattn_workspace_layout.argtypes = [ci] * 8 + [ctypes.POINTER(sz), ctypes.POINTER(i64)]
+    L.mxattn_kv_tile.argtypes = [ci, ci]
+    L.mxattn_fwd.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P]
+    L.mxattn_fwd_dump.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P, P, P, P]
+    L.mxattn_prepare.argtypes = [P, P, P] + [ci] * 8 + [P, sz, P]
+    L.mxattn_fwd_prepared.argtypes = [P, P] + [ci] * 9 + [P, P, sz, P]
+    for f in ("mxq_quantize", "mxq_quantize_t", "mxq_dequantize", "mxattn_workspace_layout",
+              "mxattn_kv_tile", "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare",
+              "mxattn_fwd_prepared"):
+        getattr(L, f).restype = ci
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MxError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MX_F32
+    if t.dtype == torch.bfloat16:
+        return MX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _mode(mode, table):
+    return table[mode] if isinstance(mode, str) else int(mode)
+
+
+# ------------------------------------------------------------ quantizer ----
+
+def quantize(x: torch.Tensor, mode="uos", codes=None, scales=None, stream=None):
+    """Blocks of 32 along the flattened contiguous axis of ``x`` (fp32 or
+    bf16, numel % 32 == 0).  Returns (codes uint8[n/2], scales uint8[n/32])."""
+    assert x.is_cuda and x.is_contiguous()
+    n = x.numel()
+    if codes is None:
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(n // 32, dtype=torch.uint8, device=x.device)
+    _check("mxq_quantize", lib().mxq_quantize(_ptr(x), n, _dtype_code(x), _mode(mode, RULES),
+                                              _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def quantize_t(x: torch.Tensor, mode="uos", rows_pad: int = 0, stream=None):
+    """Blocks of 32 along the rows of ``x`` [batch, rows, cols] (or [rows,
+    cols]); returns transposed (codes [batch, cols, rows_pad/2], scales
+    [batch, cols, rows_pad/32])."""
+    assert x.is_cuda and x.is_contiguous()
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    batch, rows, cols = x3.shape
+    rp = rows_pad or (rows + 31) // 32 * 32
+    codes = torch.empty((batch, cols, rp // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((batch, cols, rp // 32), dtype=torch.uint8, device=x.device)
+    _check("mxq_quantize_t", lib().mxq_quantize_t(
+        _ptr(x3), batch, rows, cols, _dtype_code(x), _mode(mode, RULES), rp,
+        _ptr(codes), _ptr(scales), _stream(stream)))
+    if x.dim() == 2:
+        return codes[0], scales[0]
+    return codes, scales
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32,
+               out=None, stream=None):
+    """Values of packed codes under their E8M0 bytes, as fp32 or bf16."""
+    n = codes.numel() * 2
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=codes.device)
+    _check("mxq_dequantize", lib().mxq_dequantize(_ptr(codes), _ptr(scales), n,
+                                                  _dtype_code(out), _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------ attention ----
+
+def kv_tile(D: int, mode="uos_pnq") -> int:
+    """Keys per KV tile: the running-max schedule the oracle must mirror."""
+    r = lib().mxattn_kv_tile(D, _mode(mode, MODES))
+    if r < 0:
+        raise MxError("mxattn_kv_tile", r)
+    return r
+
+
+def workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dtype, mode) -> int:
+    dt = MX_BF16 if dtype in (torch.bfloat16, "bf16", MX_BF16) else MX_F32
+    return lib().mxattn_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dt, _mode(mode, MODES))
+
+
+def workspace_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode):
+    """(offsets of Q~ codes, Q~ scales, K~ codes, K~ scales, V~^T codes,
+    V~^T scales), skv_ld — for reading the quantized operands back."""
+    dt = MX_BF16 if dtype in (torch.bfloat16, "bf16", MX_BF16) else MX_F32
+    off = (ctypes.c_size_t * 6)()
+    ld = ctypes.c_int64()
+    _check("mxattn_workspace_layout", lib().mxattn_workspace_layout(
+        B, Hq, Hkv, Sq, Skv, D, dt, _mode(mode, MODES), off, ctypes.byref(ld)))
+    return list(off), ld.value
+
+
+def alloc_workspace(q, k, mode):
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    nb = workspace_bytes(B, Hq, Hkv, Sq, Skv, D, q.dtype, mode)
+    if nb == 0:
+        raise ValueError("invalid attention shape")
+    # torch's caching allocator returns >= 512-byte aligned blocks
+    return torch.empty(nb, dtype=torch.uint8, device=q.device)
+
+
+def attn_fwd(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
+             stream=None):
+    """O = softmax(q k^T / sqrt(D)) v in the given mode; fp32 output.
+    q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D]; fp32 or bf16, contiguous, on the GPU."""
+    for t in (q, k, v):
+        assert t.is_cuda and t.is_contiguous()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(q, k, mode)
+    _check("mxattn_fwd", lib().mxattn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+        _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def attn_prepare(q, k, v, *, mode="uos_pnq", workspace=None, stream=None):
+    """First half of attn_fwd: quantize (or convert) the operands into the
+    workspace.  Returns the workspace."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if workspace is None:
+        workspace = alloc_workspace(q, k, mode)
+    _check("mxattn_prepare", lib().mxattn_prepare(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _mode(mode, MODES),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def attn_fwd_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None,
+                      stream=None):
+    """Second half of attn_fwd: the fused attention kernel on a workspace
+    filled by attn_prepare with the same shapes, dtype and mode."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    _check("mxattn_fwd_prepared", lib().mxattn_fwd_prepared(
+        _ptr(q), _ptr(k), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+        _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None,
+                  stream=None):
+    """attn_fwd plus the P~ codes / E8M0 bytes of the flattened query rows
+    ``rows`` ((b*Hq + h)*Sq + i).  Returns (o, p_codes [n, skv_ld/2],
+    p_scales [n, skv_ld/32], workspace); unvisited key blocks stay zero."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    rows = torch.as_tensor(rows, dtype=torch.int64)
+    n = rows.numel()
+    skv_ld = (Skv + 127) // 128 * 128
+    slot = torch.full((B * Hq * Sq,), -1, dtype=torch.int32)
+    slot[rows] = torch.arange(n, dtype=torch.int32)
+    slot = slot.to(q.device)
+    pc = torch.zeros((max(n, 1), skv_ld // 2), dtype=torch.uint8, device=q.device)
+    ps = torch.zeros((max(n, 1), skv_ld // 32), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(q, k, mode)
+    _check("mxattn_fwd_dump", lib().mxattn_fwd_dump(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+        _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _ptr(slot),
+        _ptr(pc), _ptr(ps), _stream(stream)))
+    return out, pc[:n], ps[:n], workspace

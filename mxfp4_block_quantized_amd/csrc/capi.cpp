@@ -1,0 +1,306 @@
+// C ABI of the MXFP4 quantizer and MXFP4 attention (see include/mxattn.h):
+// argument validation (always before any HIP call), workspace layout and
+// dispatch to the HIP launchers.
+#include "mxattn.h"
+
+#include <cstdint>
+#include <limits>
+
+#include "internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int to_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Byte layout of the workspace used by mxattn_fwd.
+struct Layout {
+  size_t off[6];  // MX: qc qs kc ks vc vs | FP16: vt, q16, k16
+  size_t total;
+  int64_t skv_ld;
+};
+
+int check_attn_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                     int causal, int mode) {
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
+  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_PNQ) return MX_ERR_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return MX_ERR_ARG;
+  if (causal != 0 && causal != 1) return MX_ERR_ARG;
+  if (Hq % Hkv != 0) return MX_ERR_ARG;
+  if (D != 64 && D != 128) return MX_ERR_UNSUPPORTED;
+  if (causal && Sq != Skv) return MX_ERR_UNSUPPORTED;
+  if (B > 65535 || Hq > 65535) return MX_ERR_UNSUPPORTED;
+  // element counts must fit the kernels' 64-bit indexing comfortably and
+  // the per-head row count must fit int32 tiles
+  if (static_cast<int64_t>(B) * Hq * Sq * D > (int64_t(1) << 40)) return MX_ERR_UNSUPPORTED;
+  return MX_OK;
+}
+
+Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, int mode) {
+  Layout L{};
+  const int64_t skv_ld = (static_cast<int64_t>(Skv) + mxk::kKvTile - 1) / mxk::kKvTile * mxk::kKvTile;
+  L.skv_ld = skv_ld;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = cur;
+    cur = round_up(cur + bytes, 256);
+    return o;
+  };
+  if (mode == MXATTN_FP16) {
+    L.off[0] = take(static_cast<size_t>(B) * Hkv * D * skv_ld * 2);  // V^T fp16
+    if (dtype == MX_F32) {
+      L.off[1] = take(static_cast<size_t>(B) * Hq * Sq * D * 2);     // Q fp16
+      L.off[2] = take(static_cast<size_t>(B) * Hkv * Skv * D * 2);   // K fp16
+    }
+  } else {
+    // one extra tile of zero rows after Q~ and K~ so the last tile's loads
+    // stay inside the buffer
+    const size_t q_rows = static_cast<size_t>(B) * Hq * Sq + mxk::kQTile;
+    const size_t k_rows = static_cast<size_t>(B) * Hkv * Skv + mxk::kKvTile;
+    L.off[0] = take(q_rows * D / 2);
+    L.off[1] = take(q_rows * D / 32);
+    L.off[2] = take(k_rows * D / 2);
+    L.off[3] = take(k_rows * D / 32);
+    L.off[4] = take(static_cast<size_t>(B) * Hkv * D * skv_ld / 2);
+    L.off[5] = take(static_cast<size_t>(B) * Hkv * D * skv_ld / 32);
+  }
+  L.total = cur;
+  return L;
+}
+
+// Validation shared by every attention entry point.
+int check_attn_call(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                    int Hkv, int Sq, int Skv, int D, int causal, int mode, const void* ws,
+                    size_t ws_bytes, bool need_qk, bool need_v, Layout* L) {
+  int st = check_attn_shape(dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode);
+  if (st != MX_OK) return st;
+  if ((need_qk && (!q || !k)) || (need_v && !v)) return MX_ERR_ARG;
+  if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
+    return MX_ERR_ALIGN;
+  *L = make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode);
+  if (!ws || ws_bytes < L->total) return MX_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+// Operand preparation into the workspace (arguments already validated).
+int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                int Hkv, int Sq, int Skv, int D, int mode, const Layout& L, void* ws,
+                hipStream_t s) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const mxk::Dtype dt = dtype == MX_BF16 ? mxk::Dtype::BF16 : mxk::Dtype::F32;
+  const int64_t nq = static_cast<int64_t>(B) * Hq * Sq * D;
+  const int64_t nk = static_cast<int64_t>(B) * Hkv * Skv * D;
+  hipError_t e;
+  if (mode == MXATTN_FP16) {
+    uint16_t* vt = reinterpret_cast<uint16_t*>(w + L.off[0]);
+    e = mxk::launch_v_to_f16t(v, static_cast<int64_t>(B) * Hkv, Skv, D, L.skv_ld, dt, vt, s);
+    if (e != hipSuccess) return MX_ERR_HIP;
+    if (dtype == MX_F32) {
+      e = mxk::launch_f32_to_f16(static_cast<const float*>(q), nq, nq,
+                                 reinterpret_cast<uint16_t*>(w + L.off[1]), s);
+      if (e != hipSuccess) return MX_ERR_HIP;
+      e = mxk::launch_f32_to_f16(static_cast<const float*>(k), nk, nk,
+                                 reinterpret_cast<uint16_t*>(w + L.off[2]), s);
+      if (e != hipSuccess) return MX_ERR_HIP;
+    }
+    return MX_OK;
+  }
+  const int uos = (mode == MXATTN_OCP) ? 0 : 1;
+  e = mxk::launch_quant_rows(q, nq, nq + static_cast<int64_t>(mxk::kQTile) * D, dt, uos,
+                             w + L.off[0], w + L.off[1], s);
+  if (e != hipSuccess) return MX_ERR_HIP;
+  e = mxk::launch_quant_rows(k, nk, nk + static_cast<int64_t>(mxk::kKvTile) * D, dt, uos,
+                             w + L.off[2], w + L.off[3], s);
+  if (e != hipSuccess) return MX_ERR_HIP;
+  e = mxk::launch_quant_cols(v, static_cast<int64_t>(B) * Hkv, Skv, D, L.skv_ld, dt, uos,
+                             w + L.off[4], w + L.off[5], s);
+  return to_status(e);
+}
+
+// The fused attention kernel on a prepared workspace.
+int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int Sq,
+                  int Skv, int D, int causal, int mode, float* o, const Layout& L,
+                  const void* ws, const int32_t* row_slot, uint8_t* p_codes,
+                  uint8_t* p_scales, hipStream_t s) {
+  const uint8_t* w = static_cast<const uint8_t*>(ws);
+  if (mode == MXATTN_FP16) {
+    mxk::F16AttnArgs a{};
+    if (dtype == MX_F32) {
+      a.q = w + L.off[1];
+      a.k = w + L.off[2];
+      a.qk_f16 = 1;
+    } else {
+      a.q = q;
+      a.k = k;
+      a.qk_f16 = 0;
+    }
+    a.vt = reinterpret_cast<const uint16_t*>(w + L.off[0]);
+    a.o = o;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Skv = Skv; a.D = D;
+    a.skv_ld = L.skv_ld;
+    a.causal = causal;
+    return to_status(mxk::launch_attn_f16(a, s));
+  }
+  mxk::MxAttnArgs a{};
+  a.qc = w + L.off[0]; a.qs = w + L.off[1];
+  a.kc = w + L.off[2]; a.ks = w + L.off[3];
+  a.vc = w + L.off[4]; a.vs = w + L.off[5];
+  a.o = o;
+  a.row_slot = row_slot;
+  a.p_codes = p_codes;
+  a.p_scales = p_scales;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Skv = Skv; a.D = D;
+  a.skv_ld = L.skv_ld;
+  a.causal = causal;
+  a.mode = mode;
+  return to_status(mxk::launch_attn_mx(a, s));
+}
+
+int attn_common(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                int Hkv, int Sq, int Skv, int D, int causal, int mode, float* o, void* ws,
+                size_t ws_bytes, const int32_t* row_slot, uint8_t* p_codes,
+                uint8_t* p_scales, bool dump, void* stream) {
+  Layout L;
+  int st = check_attn_call(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, ws, ws_bytes,
+                           true, true, &L);
+  if (st != MX_OK) return st;
+  if (!o) return MX_ERR_ARG;
+  if (!aligned(o, 16)) return MX_ERR_ALIGN;
+  if (dump && (mode == MXATTN_FP16 || !row_slot || !p_codes || !p_scales)) return MX_ERR_ARG;
+  if (dump && (!aligned(p_codes, 16) || !aligned(row_slot, 4))) return MX_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  st = run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, L, ws, s);
+  if (st != MX_OK) return st;
+  return run_attention(q, k, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, L, ws,
+                       dump ? row_slot : nullptr, dump ? p_codes : nullptr,
+                       dump ? p_scales : nullptr, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_strerror(int status) {
+  switch (status) {
+    case MX_OK: return "success";
+    case MX_ERR_ARG: return "invalid argument (null pointer, bad enum or size)";
+    case MX_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MX_ERR_WORKSPACE: return "workspace missing or too small";
+    case MX_ERR_HIP: return "HIP launch or runtime error";
+    case MX_ERR_ALIGN: return "device pointer not suitably aligned";
+    default: return "unknown status";
+  }
+}
+
+int mxq_quantize(const void* x, int64_t n, int dtype, int mode, uint8_t* codes,
+                 uint8_t* scales, void* stream) {
+  if (n < 0 || n % mxk::kBlock != 0) return MX_ERR_ARG;
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
+  if (mode != MXQ_OCP && mode != MXQ_UOS) return MX_ERR_ARG;
+  if (n == 0) return MX_OK;
+  if (!x || !codes || !scales) return MX_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return MX_ERR_ALIGN;
+  const mxk::Dtype dt = dtype == MX_BF16 ? mxk::Dtype::BF16 : mxk::Dtype::F32;
+  return to_status(mxk::launch_quant_rows(x, n, n, dt, mode == MXQ_UOS, codes, scales,
+                                          as_stream(stream)));
+}
+
+int mxq_quantize_t(const void* x, int64_t batch, int64_t rows, int64_t cols, int dtype,
+                   int mode, int64_t rows_pad, uint8_t* codes_t, uint8_t* scales_t,
+                   void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0) return MX_ERR_ARG;
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
+  if (mode != MXQ_OCP && mode != MXQ_UOS) return MX_ERR_ARG;
+  const int64_t min_pad = (rows + mxk::kBlock - 1) / mxk::kBlock * mxk::kBlock;
+  if (rows_pad == 0) rows_pad = min_pad;
+  if (rows_pad < min_pad || rows_pad % mxk::kBlock != 0) return MX_ERR_ARG;
+  if (batch == 0 || cols == 0 || rows_pad == 0) return MX_OK;
+  if (batch > 65535 || rows_pad / 64 + 1 > 65535) return MX_ERR_UNSUPPORTED;
+  if (!x || !codes_t || !scales_t) return MX_ERR_ARG;
+  if (!aligned(codes_t, 16)) return MX_ERR_ALIGN;
+  if (!aligned(x, dtype == MX_F32 ? 4 : 2)) return MX_ERR_ALIGN;
+  const mxk::Dtype dt = dtype == MX_BF16 ? mxk::Dtype::BF16 : mxk::Dtype::F32;
+  return to_status(mxk::launch_quant_cols(x, batch, rows, cols, rows_pad, dt, mode == MXQ_UOS,
+                                          codes_t, scales_t, as_stream(stream)));
+}
+
+int mxq_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, int out_dtype,
+                   void* y, void* stream) {
+  if (n < 0 || n % mxk::kBlock != 0) return MX_ERR_ARG;
+  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+  if (n == 0) return MX_OK;
+  if (!codes || !scales || !y) return MX_ERR_ARG;
+  if (!aligned(codes, 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
+  return to_status(mxk::launch_dequant(codes, scales, n, out_dtype == MX_BF16, y,
+                                       as_stream(stream)));
+}
+
+size_t mxattn_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                              int mode) {
+  if (check_attn_shape(dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode) != MX_OK) return 0;
+  return make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode).total;
+}
+
+int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                            int mode, size_t* off, int64_t* skv_ld) {
+  int st = check_attn_shape(dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode);
+  if (st != MX_OK) return st;
+  if (mode == MXATTN_FP16 || !off || !skv_ld) return MX_ERR_ARG;
+  const Layout L = make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode);
+  for (int i = 0; i < 6; ++i) off[i] = L.off[i];
+  *skv_ld = L.skv_ld;
+  return MX_OK;
+}
+
+int mxattn_kv_tile(int D, int mode) {
+  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_PNQ) return MX_ERR_ARG;
+  if (D != 64 && D != 128) return MX_ERR_UNSUPPORTED;
+  return mxk::kKvTile;
+}
+
+int mxattn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+               int Hkv, int Sq, int Skv, int D, int causal, int mode, float* o,
+               void* workspace, size_t ws_bytes, void* stream) {
+  return attn_common(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, workspace,
+                     ws_bytes, nullptr, nullptr, nullptr, false, stream);
+}
+
+int mxattn_prepare(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                   int Hkv, int Sq, int Skv, int D, int mode, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  Layout L;
+  int st = check_attn_call(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode, workspace,
+                           ws_bytes, true, true, &L);
+  if (st != MX_OK) return st;
+  return run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, L, workspace,
+                     as_stream(stream));
+}
+
+int mxattn_fwd_prepared(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
+                        int Sq, int Skv, int D, int causal, int mode, float* o,
+                        const void* workspace, size_t ws_bytes, void* stream) {
+  Layout L;
+  const bool need_qk = (mode == MXATTN_FP16 && dtype == MX_BF16);
+  int st = check_attn_call(q, k, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode,
+                           workspace, ws_bytes, need_qk, false, &L);
+  if (st != MX_OK) return st;
+  if (!o) return MX_ERR_ARG;
+  if (!aligned(o, 16)) return MX_ERR_ALIGN;
+  return run_attention(q, k, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, L, workspace,
+                       nullptr, nullptr, nullptr, as_stream(stream));
+}
+
+int mxattn_fwd_dump(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                    int Hkv, int Sq, int Skv, int D, int causal, int mode, float* o,
+                    void* workspace, size_t ws_bytes, const int32_t* row_slot,
+                    uint8_t* p_codes, uint8_t* p_scales, void* stream) {
+  return attn_common(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, workspace,
+                     ws_bytes, row_slot, p_codes, p_scales, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal launch interface between the C ABI (capi.cpp) and the HIP
+// kernels.  Host-side declarations only; every launcher enqueues on `stream`
+// and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace mxk {
+
+// E8M0 / E2M1 element block size.
+constexpr int kBlock = 32;
+
+// Keys per KV tile of both attention kernels (the running-max schedule).
+constexpr int kKvTile = 128;
+// Query rows per attention workgroup.
+constexpr int kQTile = 128;
+
+enum class Dtype : int { F32 = 0, BF16 = 1 };
+
+// Quantize n elements (n % 32 == 0) along the contiguous axis; elements in
+// [n, n_write) are treated as zero (used to zero-fill padding rows).
+hipError_t launch_quant_rows(const void* x, int64_t n, int64_t n_write, Dtype dt,
+                             int uos, uint8_t* codes, uint8_t* scales,
+                             hipStream_t stream);
+
+// Quantize batch x [rows][cols] along rows, transposed output with row
+// length rows_pad (multiple of 32, >= rows).
+hipError_t launch_quant_cols(const void* x, int64_t batch, int64_t rows,
+                             int64_t cols, int64_t rows_pad, Dtype dt, int uos,
+                             uint8_t* codes_t, uint8_t* scales_t,
+                             hipStream_t stream);
+
+// Dequantize n elements to fp32 (out_bf16 == 0) or bf16.
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                          int out_bf16, void* y, hipStream_t stream);
+
+// Operands of the MXFP4 attention kernel (all device pointers).
+struct MxAttnArgs {
+  const uint8_t* qc;   // [B*Hq*Sq (+pad)][D/2]
+  const uint8_t* qs;   // [B*Hq*Sq (+pad)][D/32]
+  const uint8_t* kc;   // [B*Hkv*Skv (+pad)][D/2]
+  const uint8_t* ks;   // [B*Hkv*Skv (+pad)][D/32]
+  const uint8_t* vc;   // [B*Hkv][D][skv_ld/2]
+  const uint8_t* vs;   // [B*Hkv][D][skv_ld/32]
+  float* o;            // [B][Hq][Sq][D]
+  const int32_t* row_slot;  // dump only: [B*Hq*Sq]
+  uint8_t* p_codes;         // dump only: [nslots][skv_ld/2]
+  uint8_t* p_scales;        // dump only: [nslots][skv_ld/32]
+  int B, Hq, Hkv, Sq, Skv, D;
+  int64_t skv_ld;
+  int causal;
+  int mode;  // 1 OCP, 2 UOS, 3 UOS+PNQ
+};
+hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
+
+// Operands of the 16-bit attention kernel.
+struct F16AttnArgs {
+  const void* q;       // [B][Hq][Sq][D], bf16 (q_is_f16 == 0) or fp16
+  const void* k;       // [B][Hkv][Skv][D], same type as q
+  const uint16_t* vt;  // fp16 [B*Hkv][D][skv_ld]
+  float* o;
+  int B, Hq, Hkv, Sq, Skv, D;
+  int64_t skv_ld;
+  int causal;
+  int qk_f16;  // 1: q/k are fp16, 0: bf16
+};
+hipError_t launch_attn_f16(const F16AttnArgs& a, hipStream_t stream);
+
+// FP16-mode operand preparation: V [batch][rows][cols] (bf16 or fp32) to
+// fp16 V^T [batch][cols][rows_ld] (zero beyond rows); and fp32 -> fp16
+// conversion of n elements (zero-filling [n, n_write)).
+hipError_t launch_v_to_f16t(const void* v, int64_t batch, int64_t rows,
+                            int64_t cols, int64_t rows_ld, Dtype dt,
+                            uint16_t* vt, hipStream_t stream);
+hipError_t launch_f32_to_f16(const float* x, int64_t n, int64_t n_write,
+                             uint16_t* y, hipStream_t stream);
+
+}  // namespace mxk

@@ -1,0 +1,272 @@
+// MXFP4 block quantizer and dequantizer kernels for gfx950.
+//
+// Format ("Quantization Error", section "Where the error comes from"; OCP
+// Microscaling Formats v1.0): 32 elements share an E8M0 scale 2^(X-127);
+// elements are E2M1 codes, rounded to nearest with ties to the even code and
+// saturating at 6.  Scale rules ("MXAttention ...", abstract): OCP puts the
+// block maximum into [4, 8) of the scaled domain, UOS into (3.625, 7.25]
+// (boundary Qmax = 7.25, inclusive).
+//
+// Both rules reduce to the exponent field Ef and mantissa field of the
+// block maximum |x|max:  X = max(0, Ef - 2 + up), with up = 1 only for UOS
+// and a mantissa above 1.8125 (fp32 field > 0x680000), i.e. exactly when
+// amax / 2^(Ef-129) > 7.25.  Zero and subnormal maxima give X = 0.
+//
+// Element rounding uses v_cvt_scalef32_pk_fp4_f32 (round to nearest even,
+// saturating, sign kept) on v = x * 2^-e, which is exact in fp32 for every
+// value that can round away from zero (fp32 denormals are kept).
+#include "internal.h"
+
+namespace mxk {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Largest |x| of a block, as the fp32 bit pattern, to the E8M0 byte.
+template <int UOS>
+__device__ __forceinline__ uint32_t e8m0_of_amax(uint32_t abits) {
+  int ef = static_cast<int>(abits >> 23);
+  int up = UOS ? ((abits & 0x7FFFFFu) > 0x680000u ? 1 : 0) : 0;
+  int x = ef - 2 + up;
+  return x < 0 ? 0u : static_cast<uint32_t>(x);
+}
+
+// 2^-e for the E8M0 byte X (e = X - 127): always a normal fp32.
+__device__ __forceinline__ float inv_scale_of(uint32_t X) {
+  return __uint_as_float((254u - X) << 23);
+}
+
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  uint32_t t = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
+  v = max(v, t);
+  t = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
+  return max(v, t);
+}
+
+// Eight consecutive elements as fp32 bit patterns.
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ x, int64_t o,
+                                      uint32_t f[8]) {
+  uint4 v = *reinterpret_cast<const uint4*>(x + o * 8);
+  f[0] = v.x << 16; f[1] = v.x & 0xFFFF0000u;
+  f[2] = v.y << 16; f[3] = v.y & 0xFFFF0000u;
+  f[4] = v.z << 16; f[5] = v.z & 0xFFFF0000u;
+  f[6] = v.w << 16; f[7] = v.w & 0xFFFF0000u;
+}
+__device__ __forceinline__ void load8(const float* __restrict__ x, int64_t o,
+                                      uint32_t f[8]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + o * 8);
+  uint4 a = p[0], b = p[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Pack 8 fp32 elements (bit patterns) under inverse scale `inv` into one
+// dword of codes: element 2j -> low nibble of byte j.
+__device__ __forceinline__ uint32_t pack8(const uint32_t f[8], float inv) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[0]) * inv,
+                                               __uint_as_float(f[1]) * inv, 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[2]) * inv,
+                                               __uint_as_float(f[3]) * inv, 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[4]) * inv,
+                                               __uint_as_float(f[5]) * inv, 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[6]) * inv,
+                                               __uint_as_float(f[7]) * inv, 1.0f, 3);
+  return r;
+}
+
+// Blocks along the contiguous axis.  Each lane owns 8 consecutive elements
+// (an "octet"); the 4 lanes of a DPP quad form one 32-element block.  Each
+// wave instruction therefore reads a contiguous 1 KiB (bf16) and writes a
+// contiguous 256 B of codes.
+template <typename In, int UOS, int UNROLL>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
+    const In* __restrict__ x, int64_t n_oct, int64_t n_oct_write,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  uint32_t f[UNROLL][8];
+  int64_t o[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    o[u] = (static_cast<int64_t>(blockIdx.x) * UNROLL + u) * kThreads + threadIdx.x;
+    if (o[u] < n_oct) {
+      load8(x, o[u], f[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[u][i] = 0u;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, f[u][i] & 0x7FFFFFFFu);
+    uint32_t X = e8m0_of_amax<UOS>(quad_max_u32(m));
+    uint32_t r = pack8(f[u], inv_scale_of(X));
+    if (o[u] < n_oct_write) {
+      codes[o[u]] = r;
+      if ((threadIdx.x & 3) == 0) scales[o[u] >> 2] = static_cast<uint8_t>(X);
+    }
+  }
+}
+
+// Blocks along ROWS of [rows][cols] matrices, transposed output.  One
+// workgroup stages a 64-row x 128-column tile in LDS (fp32, padded row to
+// avoid bank conflicts on column reads), then each thread quantizes one
+// 32-row block of one column and writes its 16 code bytes and scale byte.
+constexpr int kColTileR = 64;
+constexpr int kColTileC = 128;
+
+template <typename In>
+__device__ __forceinline__ float load1(const In* p);
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) {
+  return *p;
+}
+
+template <typename In, int UOS>
+__global__ __launch_bounds__(kThreads) void quant_cols_kernel(
+    const In* __restrict__ x, int64_t rows, int64_t cols, int64_t rows_pad,
+    uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+  __shared__ float tile[kColTileR][kColTileC + 1];
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kColTileC;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kColTileR;
+  const int64_t b = blockIdx.z;
+  const In* xb = x + b * rows * cols;
+  const int tc = threadIdx.x % kColTileC;
+  const int tr = threadIdx.x / kColTileC;  // 0..1
+#pragma unroll 4
+  for (int i = 0; i < kColTileR / 2; ++i) {
+    int r = tr + 2 * i;
+    int64_t gr = r0 + r, gc = c0 + tc;
+    tile[r][tc] = (gr < rows && gc < cols) ? load1<In>(xb + gr * cols + gc) : 0.0f;
+  }
+  __syncthreads();
+  const int64_t gc = c0 + tc;
+  const int kb = tr;  // which 32-row block of the tile
+  const int64_t gr0 = r0 + kb * kBlock;
+  if (gc >= cols || gr0 >= rows_pad) return;
+  uint32_t f[kBlock];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    f[i] = __float_as_uint(tile[kb * kBlock + i][tc]);
+    m = max(m, f[i] & 0x7FFFFFFFu);
+  }
+  uint32_t X = e8m0_of_amax<UOS>(m);
+  float inv = inv_scale_of(X);
+  uint4 out;
+  out.x = pack8(f + 0, inv);
+  out.y = pack8(f + 8, inv);
+  out.z = pack8(f + 16, inv);
+  out.w = pack8(f + 24, inv);
+  const int64_t col = b * cols + gc;
+  *reinterpret_cast<uint4*>(codes_t + col * (rows_pad / 2) + gr0 / 2) = out;
+  scales_t[col * (rows_pad / kBlock) + gr0 / kBlock] = static_cast<uint8_t>(X);
+}
+
+// Dequantize: each lane expands one dword of codes (8 elements).
+// Magnitudes times 2: {0,1,2,3,4,6,8,12} packed as nibbles.
+__device__ __forceinline__ float dq(uint32_t code, int ex) {
+  uint32_t m2 = (0xC8643210u >> (4u * (code & 7u))) & 0xFu;
+  float v = __builtin_amdgcn_ldexpf(static_cast<float>(m2), ex);
+  return (code & 8u) ? -v : v;
+}
+
+template <int OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(
+    const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    int64_t n_oct, void* __restrict__ y) {
+  int64_t o = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (o >= n_oct) return;
+  uint32_t c = codes[o];
+  const uint32_t X = scales[o >> 2];
+  int ex = static_cast<int>(X) - 128;  // magnitude*2 * 2^(X-128)
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (X == 255u) ? __builtin_nanf("") : dq((c >> (4 * i)) & 0xFu, ex);
+  if (OUT_BF16) {
+    uint4 w;
+    w.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
+    w.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
+    w.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
+    w.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
+    reinterpret_cast<uint4*>(y)[o] = w;
+  } else {
+    float4* p = reinterpret_cast<float4*>(y) + 2 * o;
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const void* x, int64_t n, int64_t n_write, Dtype dt,
+                             int uos, uint8_t* codes, uint8_t* scales,
+                             hipStream_t stream) {
+  if (n_write <= 0) return hipSuccess;
+  constexpr int U = 4;
+  const int64_t n_oct = n / 8, n_oct_w = n_write / 8;
+  const int64_t per_block = static_cast<int64_t>(kThreads) * U;
+  dim3 grid(static_cast<unsigned>((n_oct_w + per_block - 1) / per_block));
+  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
+  if (dt == Dtype::BF16) {
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    if (uos)
+      hipLaunchKernelGGL((quant_rows_kernel<uint16_t, 1, U>), grid, dim3(kThreads), 0, stream, xp, n_oct, n_oct_w, c32, scales);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<uint16_t, 0, U>), grid, dim3(kThreads), 0, stream, xp, n_oct, n_oct_w, c32, scales);
+  } else {
+    const float* xp = static_cast<const float*>(x);
+    if (uos)
+      hipLaunchKernelGGL((quant_rows_kernel<float, 1, U>), grid, dim3(kThreads), 0, stream, xp, n_oct, n_oct_w, c32, scales);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<float, 0, U>), grid, dim3(kThreads), 0, stream, xp, n_oct, n_oct_w, c32, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const void* x, int64_t batch, int64_t rows,
+                             int64_t cols, int64_t rows_pad, Dtype dt, int uos,
+                             uint8_t* codes_t, uint8_t* scales_t,
+                             hipStream_t stream) {
+  if (batch <= 0 || cols <= 0 || rows_pad <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((cols + kColTileC - 1) / kColTileC),
+            static_cast<unsigned>((rows_pad + kColTileR - 1) / kColTileR),
+            static_cast<unsigned>(batch));
+  if (dt == Dtype::BF16) {
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    if (uos)
+      hipLaunchKernelGGL((quant_cols_kernel<uint16_t, 1>), grid, dim3(kThreads), 0, stream, xp, rows, cols, rows_pad, codes_t, scales_t);
+    else
+      hipLaunchKernelGGL((quant_cols_kernel<uint16_t, 0>), grid, dim3(kThreads), 0, stream, xp, rows, cols, rows_pad, codes_t, scales_t);
+  } else {
+    const float* xp = static_cast<const float*>(x);
+    if (uos)
+      hipLaunchKernelGGL((quant_cols_kernel<float, 1>), grid, dim3(kThreads), 0, stream, xp, rows, cols, rows_pad, codes_t, scales_t);
+    else
+      hipLaunchKernelGGL((quant_cols_kernel<float, 0>), grid, dim3(kThreads), 0, stream, xp, rows, cols, rows_pad, codes_t, scales_t);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                          int out_bf16, void* y, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n_oct = n / 8;
+  dim3 grid(static_cast<unsigned>((n_oct + kThreads - 1) / kThreads));
+  const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
+  if (out_bf16)
+    hipLaunchKernelGGL((dequant_kernel<1>), grid, dim3(kThreads), 0, stream, c32, scales, n_oct, y);
+  else
+    hipLaunchKernelGGL((dequant_kernel<0>), grid, dim3(kThreads), 0, stream, c32, scales, n_oct, y);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

@@ -73,6 +73,8 @@ def _load():
     lib.oracle_dequantize.restype = ci
     lib.oracle_attn_rows.argtypes = [P, P, P, ci] + [ci] * 9 + [P, i64, P, P, P, P, P, P]
     lib.oracle_attn_rows.restype = ci
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ci
     _lib = lib
     return lib
 
@@ -90,6 +92,11 @@ def _as_input(x):
     if x.dtype == np.uint16:
         return x, BF16
     raise TypeError("oracle inputs are float32 arrays or bf16 bit patterns (uint16)")
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return _load().oracle_threads()
 
 
 def scale_exponent(amax: float, rule: int) -> int:

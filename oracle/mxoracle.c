@@ -413,3 +413,16 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
     free(vt);
     return 0;
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

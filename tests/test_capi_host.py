@@ -1,0 +1,89 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol the header declares, and rejects bad arguments before any HIP
+call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_block_quantized_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx[a-z_0-9]*)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(mx.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    L = mx.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror():
+    L = mx.lib()
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert len(L.mx_strerror(s)) > 3
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def test_quantize_rejects_bad_args():
+    L = mx.lib()
+    assert L.mxq_quantize(FAKE, 33, 1, 1, FAKE, FAKE, None) == -1      # n % 32
+    assert L.mxq_quantize(FAKE, -32, 1, 1, FAKE, FAKE, None) == -1
+    assert L.mxq_quantize(FAKE, 64, 5, 1, FAKE, FAKE, None) == -1      # dtype
+    assert L.mxq_quantize(FAKE, 64, 1, 9, FAKE, FAKE, None) == -1      # mode
+    assert L.mxq_quantize(None, 64, 1, 1, FAKE, FAKE, None) == -1      # null
+    assert L.mxq_quantize(ctypes.c_void_p((1 << 20) + 4), 64, 1, 1, FAKE, FAKE, None) == -5
+    assert L.mxq_quantize(None, 0, 1, 1, None, None, None) == 0        # empty is a no-op
+    assert L.mxq_quantize_t(FAKE, 1, 64, 8, 1, 1, 48, FAKE, FAKE, None) == -1  # rows_pad % 32
+    assert L.mxq_quantize_t(FAKE, 1, 64, 8, 1, 1, 32, FAKE, FAKE, None) == -1  # rows_pad < rows
+    assert L.mxq_dequantize(FAKE, FAKE, 31, 0, FAKE, None) == -1
+    assert L.mxq_dequantize(FAKE, FAKE, 64, 3, FAKE, None) == -1
+
+
+def test_attention_rejects_bad_args():
+    L = mx.lib()
+    P = FAKE
+    def fwd(dtype=1, B=1, Hq=2, Hkv=1, Sq=64, Skv=64, D=128, causal=0, mode=3, ws_bytes=1 << 40,
+            q=P, ws=P):
+        return L.mxattn_fwd(q, P, P, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, P, ws,
+                            ctypes.c_size_t(ws_bytes), None)
+    assert fwd(D=96) == -2
+    assert fwd(Hq=3, Hkv=2) == -1
+    assert fwd(causal=1, Skv=65) == -2
+    assert fwd(mode=4) == -1
+    assert fwd(dtype=2) == -1
+    assert fwd(Sq=0) == -1
+    assert fwd(q=None) == -1
+    assert fwd(ws_bytes=16) == -3
+    assert fwd(ws=None) == -3
+    assert fwd(ws=ctypes.c_void_p((1 << 20) + 16)) == -5
+    # dump entry: FP16 mode has no P~ to dump
+    assert L.mxattn_fwd_dump(P, P, P, 1, 1, 1, 1, 64, 64, 128, 0, 0, P, P,
+                             ctypes.c_size_t(1 << 40), P, P, P, None) == -1
+
+
+def test_workspace_and_tile_queries():
+    L = mx.lib()
+    assert L.mxattn_kv_tile(128, 3) == 128 and L.mxattn_kv_tile(64, 0) == 128
+    assert L.mxattn_kv_tile(96, 3) == -2
+    assert L.mxattn_workspace_bytes(1, 2, 1, 64, 64, 96, 1, 3) == 0
+    nb = L.mxattn_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
+    # Q~ + K~ + V~^T at 0.53125 bytes per element, plus padding
+    assert 3 * 40 * 32760 * 128 * 17 // 32 <= nb < 3 * 40 * 32768 * 128 * 17 // 32 + 4096 * 128
+    off, ld = mx.workspace_layout(1, 40, 40, 32760, 32760, 128, "bf16", "uos_pnq")
+    assert ld == 32768 and off == sorted(off) and all(o % 256 == 0 for o in off)
+    with pytest.raises(mx.MxError):
+        mx.workspace_layout(1, 2, 2, 64, 64, 128, "bf16", "fp16")
