@@ -31,12 +31,16 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ``libmxattn.so`` (always recompiles)."""
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-x", "hip", *sources(),
-           "-o", tmp]
+# Extra flags per source.  The attention kernels handle no NaNs (inputs
+# are finite; masking uses -inf), so max/min need no NaN-quieting
+# canonicalisation of the matrix-core results.
+EXTRA_FLAGS = {
+    "attn_mx.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "attn_f16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,6 +50,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into ``libmxattn.so`` (always recompiles)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        flags = [f for f in HIPCC_FLAGS if f != "-shared"] + EXTRA_FLAGS.get(src, [])
+        _run([hipcc, *flags, "-I", INCLUDE, "-I", CSRC, "-x", "hip", "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

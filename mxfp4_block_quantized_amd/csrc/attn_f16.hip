@@ -186,6 +186,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f16_kernel(F16AttnArgs a, fl
     __syncthreads();
   }
 
+  // Pin the accumulators before the per-lane store condition so that no
+  // matrix-core instruction is moved into that divergent region (an MFMA with
+  // part of EXEC disabled drops operands other lanes' results depend on).
+#pragma unroll
+  for (int u = 0; u < kQT; ++u)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(oacc[u][n]));
+
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     const float inv = 1.0f / xlane_sum4(lsum[u]);

@@ -78,16 +78,147 @@ __device__ __forceinline__ int p_block_e8m0(float xmax) {
   return X < 0 ? 0 : X;
 }
 
-struct Smem {
-  uint4 kc[kSub * 64];          // K~ operands, [subtile][lane]
-  uint8_t ks[kSub * 64];        // K~ scales, [subtile][lane]
-  uint4 vc[(128 / 16) * 64];    // V~^T operands, [channel tile][lane]
-  uint8_t vs[(128 / 16) * 64];  // V~^T scales
+// One pipeline stage of the LDS: a 128-key tile of K~ and V~^T, stored in
+// MFMA operand order so that every operand read is one contiguous ds_read
+// per lane.  Tiles arrive by direct global->LDS loads (global_load_lds):
+// lane l of a load instruction lands in slot l of a 64-slot row, 16 bytes
+// per slot for codes and one zero-extended byte per 4-byte slot for scales,
+// so the key permutation is done by choosing each lane's source address.
+struct Stage {
+  uint4 kc[kSub * 64];         // K~ operands, [subtile][lane]
+  uint4 vc[(128 / 16) * 64];   // V~^T operands, [channel tile][lane]
+  uint32_t ks[kSub * 64];      // K~ scales (low byte), [subtile][lane]
+  uint32_t vs[(128 / 16) * 64];
 };
+
+// Per-wave softmax state and accumulators for kQT query tiles.
+template <int D>
+struct WaveState {
+  v4f oacc[kQT][D / 16];
+  v4f lacc[kQT];
+  float m[kQT];
+  float lsum[kQT];
+};
+
+// Issue the loads of one KV tile (keys j0 .. j0+127) into a stage.  Wave w
+// fills K~ subtiles 2w, 2w+1 and V~^T channel tiles (NT/4)*w ...; for
+// D = 64 the lanes of the zero upper half of the contraction stay idle
+// (their slots were zeroed once).
+template <int D>
+__device__ __forceinline__ void issue_tile(Stage& st, const uint8_t* kc_g, const uint8_t* ks_g,
+                                           const uint8_t* vc_g, const uint8_t* vs_g,
+                                           int64_t skv_ld, int j0, int wave, int lane) {
+  constexpr int DC = D / 32;
+  constexpr int NT = D / 16;
+  const int rho = lane & 15, c = lane >> 4;
+  if (c < DC) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 2 * wave + i;
+      const int64_t key = j0 + 32 * (rho >> 2) + 4 * t + (rho & 3);
+      __builtin_amdgcn_global_load_lds(kc_g + key * (D / 2) + c * 16, &st.kc[t * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ks_g + key * DC + c, &st.ks[t * 64], 1, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NT / 4; ++i) {
+    const int n = (NT / 4) * wave + i;
+    const int64_t d = 16 * n + rho;
+    __builtin_amdgcn_global_load_lds(vc_g + d * (skv_ld / 2) + j0 / 2 + c * 16, &st.vc[n * 64], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vs_g + d * (skv_ld / 32) + j0 / 32 + c, &st.vs[n * 64], 1, 0, 0);
+  }
+}
+
+// One KV tile for this wave's kQT query tiles.  MASK: keys beyond klim[u]
+// (sequence end, causal diagonal) are excluded.
+template <int D, int UOS, int PNQ, int DUMP, bool MASK>
+__device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, const uint4 (&qop)[kQT],
+                                             const int (&qsc)[kQT], const int (&qrow)[kQT],
+                                             const int (&klim)[kQT], int j0, int lane, float sl2,
+                                             const MxAttnArgs& a, int64_t bh) {
+  constexpr int NT = D / 16;
+  const int grp = lane >> 4;
+  const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
+
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) {
+    // S^T = K~ Q~^T for this query tile
+    v4f s[kSub];
+#pragma unroll
+    for (int t = 0; t < kSub; ++t)
+      s[t] = mfma_fp4(st.kc[t * 64 + lane], qop[u], v4f{0, 0, 0, 0}, static_cast<int>(st.ks[t * 64 + lane]),
+                      qsc[u]);
+    if (MASK) {
+#pragma unroll
+      for (int t = 0; t < kSub; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j0 + grp * 32 + t * 4 + r > klim[u]) s[t][r] = -INFINITY;
+    }
+    // row max: in-lane over this lane's 32-key block, then across lanes
+    float bmax = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int t = 0; t < kSub; ++t)
+#pragma unroll
+      for (int r = (t == 0 ? 2 : 0); r < 4; r += 2)
+        bmax = __builtin_fmaxf(bmax, __builtin_fmaxf(s[t][r], s[t][r + 1]));
+    const float mnew = fmaxf(w.m[u], xlane_max4(bmax));
+    const float alpha = __builtin_amdgcn_exp2f((w.m[u] - mnew) * sl2);
+    w.m[u] = mnew;
+
+    // scale of this lane's P~ block, then the block in the scaled domain
+    const int X = p_block_e8m0<UOS>((bmax - mnew) * sl2);
+    const float ef = static_cast<float>(X - 127);
+    uint32_t pw[4];
+    float vsum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // dword q holds key subtiles 2q and 2q+1
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3] - mnew, sl2, -ef));
+        if (!PNQ) vsum += v[i];
+      }
+      uint32_t x = 0;
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[0], v[1], 1.0f, 0);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 1);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[4], v[5], 1.0f, 2);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[6], v[7], 1.0f, 3);
+      pw[q] = x;
+    }
+    const uint4 pop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+
+    if (DUMP && qrow[u] < a.Sq) {
+      const int slot = a.row_slot[bh * a.Sq + qrow[u]];
+      if (slot >= 0) {
+        *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) +
+                                  (j0 + grp * 32) / 2) = pop;
+        a.p_scales[static_cast<int64_t>(slot) * (a.skv_ld / 32) + (j0 + grp * 32) / 32] =
+            static_cast<uint8_t>(X);
+      }
+    }
+
+    // history rescale: alpha == 1 exactly leaves the history unchanged, so
+    // the multiplies are skipped when that holds for the whole wave
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) w.oacc[u][n] *= alpha;
+      if (PNQ) w.lacc[u] *= alpha;
+    }
+    if (PNQ) {
+      w.lacc[u] = mfma_fp4(ones, pop, w.lacc[u], 127, X);
+    } else {
+      w.lsum[u] = fmaf(w.lsum[u], alpha, __builtin_amdgcn_ldexpf(vsum, X - 127));
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      w.oacc[u][n] = mfma_fp4(st.vc[n * 64 + lane], pop, w.oacc[u][n], static_cast<int>(st.vs[n * 64 + lane]), X);
+  }
+}
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
 __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, float sl2) {
-  __shared__ Smem sm;
+  __shared__ Stage stage[2];
   constexpr int DC = D / 32;  // 16-byte chunks (32-element blocks) per row
   constexpr int NT = D / 16;  // output channel tiles
 
@@ -121,146 +252,76 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     }
   }
   if (D == 64) {  // upper half of the contraction is zero for D = 64
-    for (int i = tid; i < kSub * 32; i += kThreads) {
-      const int t = i / 32, l = 32 + i % 32;
-      sm.kc[t * 64 + l] = make_uint4(0, 0, 0, 0);
-      sm.ks[t * 64 + l] = 127;
+    for (int i = tid; i < 2 * kSub * 32; i += kThreads) {
+      const int sidx = i / (kSub * 32), t = (i / 32) % kSub, l = 32 + i % 32;
+      stage[sidx].kc[t * 64 + l] = make_uint4(0, 0, 0, 0);
+      stage[sidx].ks[t * 64 + l] = 127;
     }
   }
 
-  v4f oacc[kQT][NT];
-  v4f lacc[kQT];
-  float m[kQT], lsum[kQT];
+  WaveState<D> w;
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
-    m[t] = -INFINITY;
-    lsum[t] = 0.0f;
-    lacc[t] = v4f{0, 0, 0, 0};
+    w.m[t] = -INFINITY;
+    w.lsum[t] = 0.0f;
+    w.lacc[t] = v4f{0, 0, 0, 0};
 #pragma unroll
-    for (int n = 0; n < NT; ++n) oacc[t][n] = v4f{0, 0, 0, 0};
+    for (int n = 0; n < NT; ++n) w.oacc[t][n] = v4f{0, 0, 0, 0};
   }
-  const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
 
   int ntiles = (a.Skv + kKvTile - 1) / kKvTile;
-  if (CAUSAL) ntiles = min(ntiles, blockIdx.x + 1);  // Sq == Skv, kQTile == kKvTile
+  if (CAUSAL) ntiles = min(ntiles, static_cast<int>(blockIdx.x) + 1);  // Sq == Skv, kQTile == kKvTile
+  // only the last tile can hold keys past the end or past the causal diagonal
+  const bool mask_last = CAUSAL || (a.Skv % kKvTile != 0);
+  int klim[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) klim[t] = CAUSAL ? min(a.Skv - 1, qrow[t]) : a.Skv - 1;
 
   const uint8_t* kc_g = a.kc + bg * a.Skv * (D / 2);
   const uint8_t* ks_g = a.ks + bg * a.Skv * DC;
   const uint8_t* vc_g = a.vc + bg * D * (a.skv_ld / 2);
   const uint8_t* vs_g = a.vs + bg * D * (a.skv_ld / 32);
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int j0 = jt * kKvTile;
-    // ---- stage K~ and V~^T of this tile into LDS, in operand order ----
-    for (int i = tid; i < kKvTile * DC; i += kThreads) {
-      const int key = i / DC, c = i % DC;
-      const int t = (key & 31) >> 2;
-      const int rho = ((key >> 5) << 2) | (key & 3);
-      sm.kc[t * 64 + c * 16 + rho] =
-          *reinterpret_cast<const uint4*>(kc_g + static_cast<int64_t>(j0 + key) * (D / 2) + c * 16);
-      sm.ks[t * 64 + c * 16 + rho] = ks_g[static_cast<int64_t>(j0 + key) * DC + c];
-    }
-    for (int i = tid; i < D * 4; i += kThreads) {
-      const int d = i >> 2, c = i & 3;
-      sm.vc[(d >> 4) * 64 + c * 16 + (d & 15)] =
-          *reinterpret_cast<const uint4*>(vc_g + static_cast<int64_t>(d) * (a.skv_ld / 2) + j0 / 2 + c * 16);
-      sm.vs[(d >> 4) * 64 + c * 16 + (d & 15)] = vs_g[static_cast<int64_t>(d) * (a.skv_ld / 32) + j0 / 32 + c];
-    }
+  // Tiles 0 .. nfull-1 need no masking; a masked last tile (sequence end
+  // or causal diagonal) is handled after the loop.
+  const int nfull = mask_last ? ntiles - 1 : ntiles;
+  issue_tile<D>(stage[0], kc_g, ks_g, vc_g, vs_g, a.skv_ld, 0, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int jt = 0; jt < nfull; ++jt) {
+    if (jt + 1 < ntiles)  // the other stage was released by the last barrier
+      issue_tile<D>(stage[(jt + 1) & 1], kc_g, ks_g, vc_g, vs_g, a.skv_ld, (jt + 1) * kKvTile, wave, lane);
+    compute_tile<D, UOS, PNQ, DUMP, false>(w, stage[jt & 1], qop, qsc, qrow, klim, jt * kKvTile, lane, sl2, a, bh);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
     __syncthreads();
+  }
+  if (mask_last)
+    compute_tile<D, UOS, PNQ, DUMP, true>(w, stage[nfull & 1], qop, qsc, qrow, klim, nfull * kKvTile, lane, sl2, a, bh);
 
-    // ---- S^T = K~ Q~^T ----
-    v4f s[kQT][kSub];
+  // The epilogue stores under a per-lane condition.  Pin the accumulators
+  // here so that the matrix-core instructions producing them are not moved
+  // into that divergent region: an MFMA issued with part of EXEC disabled
+  // would drop the operands of the disabled lanes, which other lanes' results
+  // depend on.
 #pragma unroll
-    for (int t = 0; t < kSub; ++t) {
-      const uint4 kop = sm.kc[t * 64 + lane];
-      const int ksc = sm.ks[t * 64 + lane];
+  for (int u = 0; u < kQT; ++u) {
 #pragma unroll
-      for (int u = 0; u < kQT; ++u) s[u][t] = mfma_fp4(kop, qop[u], v4f{0, 0, 0, 0}, ksc, qsc[u]);
-    }
-
-    const bool need_mask = (j0 + kKvTile > a.Skv) || (CAUSAL && j0 + kKvTile > q0);
-#pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-      if (need_mask) {
-        const int klim = CAUSAL ? min(a.Skv - 1, qrow[u]) : a.Skv - 1;
-#pragma unroll
-        for (int t = 0; t < kSub; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = j0 + grp * 32 + t * 4 + r;
-            if (key > klim) s[u][t][r] = -INFINITY;
-          }
-      }
-      // row max: in-lane over this lane's 32-key block, then across lanes
-      float bmax = s[u][0][0];
-#pragma unroll
-      for (int t = 0; t < kSub; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[u][t][r]);
-      const float mnew = fmaxf(m[u], xlane_max4(bmax));
-      const float alpha = __builtin_amdgcn_exp2f((m[u] - mnew) * sl2);
-      m[u] = mnew;
-
-      // scale of this lane's P~ block, then the block in the scaled domain
-      const int X = p_block_e8m0<UOS>((bmax - mnew) * sl2);
-      const float ef = static_cast<float>(X - 127);
-      uint32_t pw[4];
-      float vsum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {  // dword w holds key subtiles 2w and 2w+1
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[i] = __builtin_amdgcn_exp2f(fmaf(s[u][2 * w + (i >> 2)][i & 3] - mnew, sl2, -ef));
-          if (!PNQ) vsum += v[i];
-        }
-        uint32_t x = 0;
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[0], v[1], 1.0f, 0);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 1);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[4], v[5], 1.0f, 2);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[6], v[7], 1.0f, 3);
-        pw[w] = x;
-      }
-      const uint4 pop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-
-      if (DUMP && qrow[u] < a.Sq) {
-        const int slot = a.row_slot[bh * a.Sq + qrow[u]];
-        if (slot >= 0) {
-          *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) +
-                                    (j0 + grp * 32) / 2) = pop;
-          a.p_scales[static_cast<int64_t>(slot) * (a.skv_ld / 32) + (j0 + grp * 32) / 32] =
-              static_cast<uint8_t>(X);
-        }
-      }
-
-      // history rescale, numerator and denominator
-#pragma unroll
-      for (int n = 0; n < NT; ++n) oacc[u][n] *= alpha;
-      if (PNQ) {
-        lacc[u] *= alpha;
-        lacc[u] = mfma_fp4(ones, pop, lacc[u], 127, X);
-      } else {
-        lsum[u] = fmaf(lsum[u], alpha, __builtin_amdgcn_ldexpf(vsum, X - 127));
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        oacc[u][n] = mfma_fp4(sm.vc[n * 64 + lane], pop, oacc[u][n], sm.vs[n * 64 + lane], X);
-    }
-    __syncthreads();
+    for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[u][n]));
+    asm volatile("" : "+v"(w.lacc[u]));
   }
 
   // ---- epilogue: O = O_acc / l ----
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
-    const float l = PNQ ? lacc[u][0] : xlane_sum4(lsum[u]);
+    const float l = PNQ ? w.lacc[u][0] : xlane_sum4(w.lsum[u]);
     const float inv = 1.0f / l;
     if (qrow[u] < a.Sq) {
       float* orow = a.o + (bh * a.Sq + qrow[u]) * D;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        float4 w = make_float4(oacc[u][n][0] * inv, oacc[u][n][1] * inv, oacc[u][n][2] * inv,
-                               oacc[u][n][3] * inv);
-        *reinterpret_cast<float4*>(orow + n * 16 + grp * 4) = w;
+        float4 v = make_float4(w.oacc[u][n][0] * inv, w.oacc[u][n][1] * inv, w.oacc[u][n][2] * inv,
+                               w.oacc[u][n][3] * inv);
+        *reinterpret_cast<float4*>(orow + n * 16 + grp * 4) = v;
       }
     }
   }

@@ -1,0 +1,77 @@
+"""ISA checks of the attention kernels (CPU only: hipcc cross-compiles).
+
+A matrix-core instruction is cross-lane: a lane's result depends on operands
+held by other lanes.  If the compiler moves one into a region entered under a
+partial EXEC mask (e.g. the per-row store condition of the epilogue), the
+disabled lanes' operands are dropped and valid rows come out wrong.  The
+kernels pin their accumulators before such regions; this test checks, on the
+generated gfx950 assembly, that no MFMA sits inside the epilogue's store
+region (after the last s_and_saveexec), and that the benchmarked kernels do
+not spill.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mxfp4_block_quantized_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+
+
+def compile_to_asm(src, tmp_path):
+    from mxfp4_block_quantized_amd import build as b
+    flags = [f for f in b.HIPCC_FLAGS if f not in ("-shared",)] + b.EXTRA_FLAGS.get(src, [])
+    out = tmp_path / (src + ".s")
+    cmd = [HIPCC, *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
+           os.path.join(CSRC, src), "-S", "--offload-device-only", "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernels(asm):
+    for m in re.finditer(r"^(_Z\S*attn_\S*kernel\S*?):", asm, re.M):
+        name = m.group(1)
+        end = asm.index(".Lfunc_end", m.end())
+        yield name, asm[m.end():end]
+
+
+def mfma_in_epilogue_region(body):
+    """MFMAs placed after the kernel's last s_and_saveexec, i.e. inside the
+    epilogue's per-row store region (the last divergent region of every
+    attention kernel)."""
+    lines = [l.strip() for l in body.splitlines()
+             if l.strip() and not l.strip().startswith((";", ".", "//"))]
+    saves = [i for i, t in enumerate(lines) if t.split()[0].startswith("s_and_saveexec")]
+    if not saves:
+        return []
+    return [t for t in lines[saves[-1]:] if t.split()[0].startswith("v_mfma")]
+
+
+@pytest.mark.parametrize("src", ["attn_mx.hip", "attn_f16.hip"])
+def test_no_mfma_under_partial_exec(src, tmp_path):
+    asm = compile_to_asm(src, tmp_path)
+    found = 0
+    for name, body in kernels(asm):
+        found += 1
+        assert not mfma_in_epilogue_region(body), name
+    assert found > 0
+
+
+@pytest.mark.parametrize("src", ["attn_mx.hip", "attn_f16.hip"])
+def test_no_register_spills_in_benchmarked_kernels(src, tmp_path):
+    asm = compile_to_asm(src, tmp_path)
+    for name, body in kernels(asm):
+        if "ELi1EEEv" in name and src == "attn_mx.hip":
+            continue  # the P~ dump variants (tests only) may spill
+        m = re.search(r"ScratchSize:\s*(\d+)", body)
+        if m is None:
+            meta = re.search(re.escape(name) + r"[\s\S]*?\.private_segment_fixed_size:\s*(\d+)", asm)
+            scratch = int(meta.group(1)) if meta else 0
+        else:
+            scratch = int(m.group(1))
+        assert scratch == 0, (name, scratch)
