@@ -96,7 +96,8 @@ template <int D>
 struct WaveState {
   v4f oacc[kQT][D / 16];
   v4f lacc[kQT];
-  float m[kQT];
+  float m[kQT];     // running row max (raw score units), -inf before the first tile
+  float mref[kQT];  // value subtracted from S on the matrix core
   float lsum[kQT];
 };
 
@@ -142,12 +143,15 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
 
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
-    // S^T = K~ Q~^T for this query tile
+    // d = S - mref on the matrix core: the accumulator input is -mref, the
+    // reference running max of this row (0 before the first tile), so the
+    // subtraction costs one rounding and no VALU work per element.
+    const float nm = -w.mref[u];
+    const v4f cneg = {nm, nm, nm, nm};
     v4f s[kSub];
 #pragma unroll
     for (int t = 0; t < kSub; ++t)
-      s[t] = mfma_fp4(st.kc[t * 64 + lane], qop[u], v4f{0, 0, 0, 0}, static_cast<int>(st.ks[t * 64 + lane]),
-                      qsc[u]);
+      s[t] = mfma_fp4(st.kc[t * 64 + lane], qop[u], cneg, static_cast<int>(st.ks[t * 64 + lane]), qsc[u]);
     if (MASK) {
 #pragma unroll
       for (int t = 0; t < kSub; ++t)
@@ -155,20 +159,24 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
         for (int r = 0; r < 4; ++r)
           if (j0 + grp * 32 + t * 4 + r > klim[u]) s[t][r] = -INFINITY;
     }
-    // row max: in-lane over this lane's 32-key block, then across lanes
-    float bmax = fmaxf(s[0][0], s[0][1]);
+    // row max: in-lane over this lane's 32-key block (a v_max3 chain), then
+    // across the four lanes holding this query
+    float bmax = s[0][0];
 #pragma unroll
-    for (int t = 0; t < kSub; ++t)
-#pragma unroll
-      for (int r = (t == 0 ? 2 : 0); r < 4; r += 2)
-        bmax = __builtin_fmaxf(bmax, __builtin_fmaxf(s[t][r], s[t][r + 1]));
-    const float mnew = fmaxf(w.m[u], xlane_max4(bmax));
-    const float alpha = __builtin_amdgcn_exp2f((w.m[u] - mnew) * sl2);
-    w.m[u] = mnew;
+    for (int i = 1; i + 1 < 4 * kSub; i += 2)
+      bmax = fmaxf(fmaxf(bmax, s[i >> 2][i & 3]), s[(i + 1) >> 2][(i + 1) & 3]);
+    bmax = fmaxf(bmax, s[kSub - 1][3]);
+    // delta = new max - mref.  Before the first tile the running max is -inf
+    // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
+    const float delta = fmaxf(w.m[u] - w.mref[u], xlane_max4(bmax));
+    const float alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);
+    w.m[u] = w.mref[u] + delta;
+    w.mref[u] = w.m[u];
 
-    // scale of this lane's P~ block, then the block in the scaled domain
-    const int X = p_block_e8m0<UOS>((bmax - mnew) * sl2);
-    const float ef = static_cast<float>(X - 127);
+    // scale of this lane's P~ block, then the block in the scaled domain:
+    // log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
+    const int X = p_block_e8m0<UOS>((bmax - delta) * sl2);
+    const float kofs = fmaf(delta, sl2, static_cast<float>(X - 127));
     uint32_t pw[4];
     float vsum = 0.0f;
 #pragma unroll
@@ -176,7 +184,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3] - mnew, sl2, -ef));
+        v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3], sl2, -kofs));
         if (!PNQ) vsum += v[i];
       }
       uint32_t x = 0;
@@ -263,6 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     w.m[t] = -INFINITY;
+    w.mref[t] = 0.0f;
     w.lsum[t] = 0.0f;
     w.lacc[t] = v4f{0, 0, 0, 0};
 #pragma unroll
