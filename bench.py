@@ -137,11 +137,11 @@ def bench_quantizer(torch, mx, reps=20):
 
 
 def cpu_baseline(q, k, v, c, name):
-    """The oracle (as it stands) on the first 8 heads' 256 seeded rows."""
+    """The oracle (as it stands) on the first 24 heads' 256 seeded rows."""
     import mxsynth
     import oracle
     rows_all = mxsynth.sample_rows(c["seed"], c["B"], c["Hq"], c["S"], 256)
-    heads = min(8, c["Hq"])
+    heads = min(24, c["Hq"])
     rows = rows_all[: heads * 256]
     t0 = time.perf_counter()
     oracle.attn_rows(q, k, v, causal=c["causal"], mode=oracle.MODE_UOS_PNQ, bc=128, rows=rows)
@@ -163,7 +163,12 @@ def main():
     ap.add_argument("--modes", default="uos_pnq,fp16,ocp,uos",
                     help="first mode is the headline; the rest run alongside")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="only the standalone quantizer (for profiling it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -181,12 +186,26 @@ def main():
 
     mx.lib()
     torch.cuda.set_device(0)
+    if args.no_attention:
+        if args.calibrate_copy:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
+        print(json.dumps({"quantizer": bench_quantizer(torch, mx, reps=3)}), flush=True)
+        return
     c = dict(mxsynth.CONFIGS[args.workload])
     log(f"[bench] generating {args.workload} inputs")
     q, k, v = mxsynth.make_attn_inputs(args.workload)
     to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
     qt, kt, vt = to(q), to(k), to(v)
     flops = attn_flops(c)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     modes = args.modes.split(",")
     results = {}
     for mode in modes:
