@@ -110,13 +110,27 @@ size_t mxattn_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                               int dtype, int mode);
 
 /*
- * Byte offsets, inside the workspace, of the quantized operands of an MX
- * mode (host array `off` of 6 entries):
- *   off[0] Q~ codes  [B][Hq][Sq][D/2]        off[1] Q~ scales [B][Hq][Sq][D/32]
- *   off[2] K~ codes  [B][Hkv][Skv][D/2]      off[3] K~ scales [B][Hkv][Skv][D/32]
- *   off[4] V~^T codes  [B][Hkv][D][skv_ld/2] off[5] V~^T scales [B][Hkv][D][skv_ld/32]
- * and *skv_ld (host) = the key length of each V~^T row (a multiple of the KV
- * tile, zero-padded beyond Skv).  Returns MX_ERR_ARG for the FP16 mode.
+ * Where the quantized operands of an MX mode lie inside the workspace (host
+ * array `off` of 6 entries):
+ *   off[0] Q~ codes [B][Hq][Sq][D/2]      off[1] Q~ scales [B][Hq][Sq][D/32]
+ *   off[2] KV tile images [B][Hkv][skv_ld/128][off[3]]
+ *   off[3] bytes per image (17408 for D = 128, 13312 for D = 64)
+ *   off[4] = off[5] = 0
+ * and *skv_ld (host) = Skv rounded up to a multiple of the 128-key tile.
+ * Image of KV tile T (keys 128T .. 128T+127), all offsets in bytes:
+ *   [0, 8192)           K~ codes, [subtile t < 8][lane l < 64][16]: lane l
+ *                       of subtile t holds key 128T + 32*((l%16)/4) + 4t
+ *                       + l%4, elements 32*(l/16) .. 32*(l/16)+31 (zero for
+ *                       D = 64 and l >= 32)
+ *   [8192, 8192+64D)    V~ codes, [channel tile n < D/16][lane l][16]: lane l
+ *                       of tile n holds channel 16n + l%16, keys 128T +
+ *                       32*(l/16) .. +31 (one 32-key block along keys)
+ *   [8192+64D, +512)    K~ scales [lane l][subtile t], E8M0
+ *   [8704+64D, +4D)     V~ scales [lane l][channel tile n], E8M0
+ *   then zero padding to the image size.
+ * Codes pack two E2M1 elements per byte, the lower-indexed one in the low
+ * nibble.  Keys at or past Skv are quantized as zeros (codes 0, scale 0).
+ * Returns MX_ERR_ARG for the FP16 mode.
  */
 int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                             int dtype, int mode, size_t *off, int64_t *skv_ld);
@@ -139,8 +153,8 @@ int mxattn_kv_tile(int D, int mode);
  *  overwritten.  Modes: MXATTN_FP16 (16-bit operands, no quantization),
  *  MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ.
  * In the MX modes the call first quantizes Q and K (blocks along D) and V
- * (blocks along keys, transposed) into the workspace, then runs the fused
- * attention kernel.  In FP16 mode, V (and, for fp32 inputs, Q and K) is
+ * (blocks along keys) into the workspace, K~ and V~ as KV tile images in
+ * matrix-core operand order, then runs the fused attention kernel.  In FP16 mode, V (and, for fp32 inputs, Q and K) is
  * first converted to fp16 in the workspace.
  */
 int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
@@ -151,8 +165,9 @@ int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
 /*
  * The two halves of mxattn_fwd, for callers that reuse prepared operands or
  * time the attention kernel alone.
- * mxattn_prepare: fills the workspace -- MX modes: Q~ and K~ (blocks along
- * D) and V~^T (blocks along keys, transposed; see mxattn_workspace_layout);
+ * mxattn_prepare: fills the workspace -- MX modes: Q~ (blocks along D) and
+ * K~ / V~ (blocks along D / along keys) as KV tile images (see
+ * mxattn_workspace_layout);
  * FP16 mode: fp16 V^T (and fp16 Q, K for fp32 inputs).
  * mxattn_fwd_prepared: the fused attention kernel alone, reading the
  * operands a previous mxattn_prepare with the same sizes, dtype and mode

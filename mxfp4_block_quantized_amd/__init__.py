@@ -158,8 +158,9 @@ def workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dtype, mode) -> int:
 
 
 def workspace_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode):
-    """(offsets of Q~ codes, Q~ scales, K~ codes, K~ scales, V~^T codes,
-    V~^T scales), skv_ld — for reading the quantized operands back."""
+    """([Q~ codes offset, Q~ scales offset, KV tile images offset, bytes per
+    image, 0, 0], skv_ld) — for reading the quantized operands back (image
+    layout in include/mxattn.h)."""
     dt = MX_BF16 if dtype in (torch.bfloat16, "bf16", MX_BF16) else MX_F32
     off = (ctypes.c_size_t * 6)()
     ld = ctypes.c_int64()

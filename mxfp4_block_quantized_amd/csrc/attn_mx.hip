@@ -12,24 +12,28 @@
 //
 // Mapping onto v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4, fp32 accum):
 // an operand lane l holds row (l % 16) and the 32 K-elements of K-block
-// (l / 16) plus that block's E8M0 scale; the accumulator lane l, register
-// r holds row 4*(l/16) + r, column l % 16.
+// (l / 16) plus that block's E8M0 scale (one byte of a register, picked by
+// the instruction's op_sel); the accumulator lane l, register r holds row
+// 4*(l/16) + r, column l % 16.
 //  * S^T = K~ Q~^T: A = 16 keys x 128 d, B = 128 d x 16 queries, one MFMA
 //    covers D = 128.  The 16 A-rows of key subtile t (0..7) of a 128-key tile
 //    are the keys 32*(row/4) + 4*t + row%4, so accumulator lane l holds, over
 //    t and r, exactly the 32 keys 32*(l/16) + 4*t + r: one whole P~ block of
 //    query l % 16.  Block maxima and the fp4 packing are therefore in-lane;
 //    only the row max needs two cross-lane swaps.
-//  * O^T = V~^T P~^T: A = 16 channels x 128 keys (V~ stored transposed,
-//    blocks along keys), B = P~ (128 keys x 16 queries) straight from the
-//    registers above, with one E8M0 byte per lane.  The accumulator keeps
-//    query l % 16 in every lane of a column, matching the softmax state.
+//  * O^T = V~^T P~^T: A = 16 channels x 128 keys, B = P~ (128 keys x 16
+//    queries) straight from the registers above, with one E8M0 byte per
+//    lane.  The accumulator keeps query l % 16 in every lane of a column,
+//    matching the softmax state.
+// The quantizer writes K~ and V~ as KV tile images already in these operand
+// orders, so a tile moves to LDS with contiguous 16-byte-per-lane direct
+// loads (global_load_lds) and every operand read is one ds_read per lane.
 //
 // P~ is formed in the scaled domain: for a block with scale exponent e,
 // v = exp2((s - m) * log2(e)/sqrt(D) - e) is rounded by
-// v_cvt_scalef32_pk_fp4_f32 (round to nearest even, saturating).  This keeps
-// blocks whose probabilities lie below fp32's normal range exact in the same
-// way the binary64 definition treats them.
+// v_cvt_scalef32_pk_fp4_f32 (round to nearest even,
+// saturating).  This keeps blocks whose probabilities lie below fp32's
+// normal range exact in the same way the binary64 definition treats them.
 #include "internal.h"
 
 namespace mxk {
@@ -38,18 +42,32 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQT = 2;                 // 16-query tiles per wave
-constexpr int kSub = kKvTile / 16;     // key subtiles per KV tile (8)
-static_assert(kQTile == kWaves * kQT * 16, "query tile = waves x q-tiles x 16");
+constexpr int kQT = 2;              // 16-query tiles per wave
+constexpr int kSub = kKvTile / 16;  // key subtiles per KV tile (8)
+constexpr int kStages = 3;          // LDS ring of KV tile images
+static_assert(kMxQTile == kWaves * kQT * 16, "query tile = waves x q-tiles x 16");
+static_assert(kMxQTile == 2 * kKvTile, "the causal tail below assumes two KV tiles per query tile");
 
-__device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, int sa, int sb) {
+template <int SEL_A>
+__device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, uint32_t sa, int sb) {
   v8i av = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
             static_cast<int>(a.w), 0, 0, 0, 0};
   v8i bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
             static_cast<int>(b.w), 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL_A,
+                                                          static_cast<int>(sa), 0, sb);
+}
+// A-scale taken from byte `sel` (a constant after unrolling) of `sa`.
+__device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, const uint4& b, v4f c, uint32_t sa,
+                                            int sel, int sb) {
+  switch (sel) {
+    case 0: return mfma_fp4<0>(a, b, c, sa, sb);
+    case 1: return mfma_fp4<1>(a, b, c, sa, sb);
+    case 2: return mfma_fp4<2>(a, b, c, sa, sb);
+    default: return mfma_fp4<3>(a, b, c, sa, sb);
+  }
 }
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (same query column)
@@ -66,30 +84,17 @@ __device__ __forceinline__ float xlane_sum4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// E8M0 byte of a P~ block from x = log2 of its largest element (x <= 0).
-// exp2 is taken 64 binades up so that maxima below fp32's normal range keep
-// their exponent; X = max(0, Ef - 66 + up).
+// Scale exponent e of a P~ block from x = log2 of its largest element,
+// clamped to the E8M0 range (e >= -127; the byte is e + 127).  With
+// E = floor(x) and mantissa 2^frac(x): OCP takes e = E - 2; UOS moves one
+// binade up when the mantissa exceeds 1.8125, i.e. frac(x) > log2(1.8125),
+// which is e = floor(x - log2(1.8125)) - 1.  A block with no unmasked key
+// (x = -inf) gets -127.
 template <int UOS>
-__device__ __forceinline__ int p_block_e8m0(float xmax) {
-  uint32_t bits = __float_as_uint(__builtin_amdgcn_exp2f(xmax + 64.0f));
-  int ef = static_cast<int>(bits >> 23);
-  int up = UOS ? ((bits & 0x7FFFFFu) > 0x680000u ? 1 : 0) : 0;
-  int X = ef - 66 + up;
-  return X < 0 ? 0 : X;
+__device__ __forceinline__ float p_block_exp(float x) {
+  constexpr float kOfs = UOS ? 1.85798099512757209f : 2.0f;  // log2(1.8125) + 1, or 2
+  return fmaxf(__builtin_floorf(x - kOfs), -127.0f);
 }
-
-// One pipeline stage of the LDS: a 128-key tile of K~ and V~^T, stored in
-// MFMA operand order so that every operand read is one contiguous ds_read
-// per lane.  Tiles arrive by direct global->LDS loads (global_load_lds):
-// lane l of a load instruction lands in slot l of a 64-slot row, 16 bytes
-// per slot for codes and one zero-extended byte per 4-byte slot for scales,
-// so the key permutation is done by choosing each lane's source address.
-struct Stage {
-  uint4 kc[kSub * 64];         // K~ operands, [subtile][lane]
-  uint4 vc[(128 / 16) * 64];   // V~^T operands, [channel tile][lane]
-  uint32_t ks[kSub * 64];      // K~ scales (low byte), [subtile][lane]
-  uint32_t vs[(128 / 16) * 64];
-};
 
 // Per-wave softmax state and accumulators for kQT query tiles.
 template <int D>
@@ -101,63 +106,78 @@ struct WaveState {
   float lsum[kQT];
 };
 
-// Issue the loads of one KV tile (keys j0 .. j0+127) into a stage.  Wave w
-// fills K~ subtiles 2w, 2w+1 and V~^T channel tiles (NT/4)*w ...; for
-// D = 64 the lanes of the zero upper half of the contraction stay idle
-// (their slots were zeroed once).
+// s_waitcnt on the vector-memory counter only (expcnt, lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// Issue the direct loads of one KV tile image into an LDS stage: wave w
+// moves the 1 KiB rows w, w + kWaves, ... of the image, lane l bytes
+// [16 l, 16 l + 16) of each.
 template <int D>
-__device__ __forceinline__ void issue_tile(Stage& st, const uint8_t* kc_g, const uint8_t* ks_g,
-                                           const uint8_t* vc_g, const uint8_t* vs_g,
-                                           int64_t skv_ld, int j0, int wave, int lane) {
-  constexpr int DC = D / 32;
-  constexpr int NT = D / 16;
-  const int rho = lane & 15, c = lane >> 4;
-  if (c < DC) {
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* src, int wave, int lane) {
+  constexpr int NL = img_bytes(D) / 1024;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = 2 * wave + i;
-      const int64_t key = j0 + 32 * (rho >> 2) + 4 * t + (rho & 3);
-      __builtin_amdgcn_global_load_lds(kc_g + key * (D / 2) + c * 16, &st.kc[t * 64], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(ks_g + key * DC + c, &st.ks[t * 64], 1, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NT / 4; ++i) {
-    const int n = (NT / 4) * wave + i;
-    const int64_t d = 16 * n + rho;
-    __builtin_amdgcn_global_load_lds(vc_g + d * (skv_ld / 2) + j0 / 2 + c * 16, &st.vc[n * 64], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vs_g + d * (skv_ld / 32) + j0 / 32 + c, &st.vs[n * 64], 1, 0, 0);
+  for (int i = 0; i < (NL + kWaves - 1) / kWaves; ++i) {
+    const int row = wave + i * kWaves;
+    if (row < NL)
+      __builtin_amdgcn_global_load_lds(src + row * 1024 + lane * 16, stage + row * 1024, 16, 0, 0);
   }
 }
 
-// One KV tile for this wave's kQT query tiles.  MASK: keys beyond klim[u]
-// (sequence end, causal diagonal) are excluded.
-template <int D, int UOS, int PNQ, int DUMP, bool MASK>
-__device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, const uint4 (&qop)[kQT],
+// Loads this wave issues per tile.
+template <int D>
+__device__ __forceinline__ int loads_per_tile(int wave) {
+  constexpr int NL = img_bytes(D) / 1024;
+  return NL / kWaves + (wave < NL % kWaves ? 1 : 0);
+}
+
+// One KV tile (keys j0 .. j0+127) for this wave's kQT query tiles.  MASK:
+// keys beyond klim[u] (sequence end, causal diagonal) are excluded.
+template <int D, int UOS, int PNQ, int DUMP>
+__device__ __forceinline__ void compute_tile(WaveState<D>& w, const uint8_t* st, const uint4 (&qop)[kQT],
                                              const int (&qsc)[kQT], const int (&qrow)[kQT],
-                                             const int (&klim)[kQT], int j0, int lane, float sl2,
+                                             const int (&klim)[kQT], bool mask, bool visit, int j0, int lane, float sl2,
                                              const MxAttnArgs& a, int64_t bh) {
   constexpr int NT = D / 16;
   const int grp = lane >> 4;
   const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
 
+  uint4 kop[kSub];
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) kop[t] = *reinterpret_cast<const uint4*>(st + kImgKc + t * 1024 + lane * 16);
+  const uint2 ksc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
+  uint32_t vsc[(NT + 3) / 4];
+  if (NT == 8) {
+    const uint2 v2 = *reinterpret_cast<const uint2*>(st + img_vs(D) + lane * 8);
+    vsc[0] = v2.x;
+    vsc[(NT + 3) / 4 - 1] = v2.y;
+  } else {
+    vsc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
+  }
+
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     // d = S - mref on the matrix core: the accumulator input is -mref, the
-    // reference running max of this row (0 before the first tile), so the
-    // subtraction costs one rounding and no VALU work per element.
+    // running max of the previous tiles (0 before the first), so the
+    // subtraction happens before the single rounding of the result and the
+    // elements near the maximum keep full relative precision.
     const float nm = -w.mref[u];
     const v4f cneg = {nm, nm, nm, nm};
     v4f s[kSub];
 #pragma unroll
     for (int t = 0; t < kSub; ++t)
-      s[t] = mfma_fp4(st.kc[t * 64 + lane], qop[u], cneg, static_cast<int>(st.ks[t * 64 + lane]), qsc[u]);
-    if (MASK) {
+      s[t] = mfma_fp4_sel(kop[t], qop[u], cneg, t < 4 ? ksc.x : ksc.y, t & 3, qsc[u]);
+    if (mask) {
+      int lim = klim[u] - (j0 + grp * 32);  // last unmasked key of this lane's block
+      asm volatile("" : "+v"(lim));  // keeps the compares inside this branch
 #pragma unroll
       for (int t = 0; t < kSub; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (j0 + grp * 32 + t * 4 + r > klim[u]) s[t][r] = -INFINITY;
+          s[t][r] = (t * 4 + r > lim) ? -INFINITY : s[t][r];
     }
     // row max: in-lane over this lane's 32-key block (a v_max3 chain), then
     // across the four lanes holding this query
@@ -169,14 +189,16 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
     // delta = new max - mref.  Before the first tile the running max is -inf
     // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
     const float delta = fmaxf(w.m[u] - w.mref[u], xlane_max4(bmax));
-    const float alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);
+    const float alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);  // 0 at first
     w.m[u] = w.mref[u] + delta;
     w.mref[u] = w.m[u];
 
-    // scale of this lane's P~ block, then the block in the scaled domain:
+    // scale of this lane's P~ block (the block holding the row maximum gets
+    // x = 0 exactly), then the block in the scaled domain:
     // log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
-    const int X = p_block_e8m0<UOS>((bmax - delta) * sl2);
-    const float kofs = fmaf(delta, sl2, static_cast<float>(X - 127));
+    const float e = p_block_exp<UOS>((bmax - delta) * sl2);
+    const int X = static_cast<int>(e) + 127;
+    const float kofs = fmaf(delta, sl2, e);
     uint32_t pw[4];
     float vsum = 0.0f;
 #pragma unroll
@@ -187,8 +209,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
         v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3], sl2, -kofs));
         if (!PNQ) vsum += v[i];
       }
-      uint32_t x = 0;
-      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[0], v[1], 1.0f, 0);
+      // all four bytes are written, so the chain may start from any value
+      uint32_t x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(v[0]), v[0], v[1], 1.0f, 0);
       x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 1);
       x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[4], v[5], 1.0f, 2);
       x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[6], v[7], 1.0f, 3);
@@ -196,7 +218,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
     }
     const uint4 pop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
 
-    if (DUMP && qrow[u] < a.Sq) {
+    if (DUMP && visit && qrow[u] < a.Sq) {
       const int slot = a.row_slot[bh * a.Sq + qrow[u]];
       if (slot >= 0) {
         *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) +
@@ -214,29 +236,40 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const Stage& st, c
       if (PNQ) w.lacc[u] *= alpha;
     }
     if (PNQ) {
-      w.lacc[u] = mfma_fp4(ones, pop, w.lacc[u], 127, X);
+      w.lacc[u] = mfma_fp4<0>(ones, pop, w.lacc[u], 127, X);
     } else {
       w.lsum[u] = fmaf(w.lsum[u], alpha, __builtin_amdgcn_ldexpf(vsum, X - 127));
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      w.oacc[u][n] = mfma_fp4(st.vc[n * 64 + lane], pop, w.oacc[u][n], static_cast<int>(st.vs[n * 64 + lane]), X);
+    for (int n = 0; n < NT; ++n) {
+      const uint4 vop = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
+      w.oacc[u][n] = mfma_fp4_sel(vop, pop, w.oacc[u][n], vsc[n >> 2], n & 3, X);
+    }
   }
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
-__global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, float sl2) {
-  __shared__ Stage stage[2];
-  constexpr int DC = D / 32;  // 16-byte chunks (32-element blocks) per row
+__global__ __launch_bounds__(kThreads, 1) void attn_mx_kernel(MxAttnArgs a, float sl2) {
+  constexpr int IMG = img_bytes(D);
+  // One LDS object per stage, so that the compiler can tell which stage a
+  // read touches and wait only for the direct loads into that stage.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[IMG];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[IMG];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[IMG];
+  static_assert(kStages == 3, "one LDS object per stage");
+  constexpr int DC = D / 32;  // 32-element blocks per Q~ row
   constexpr int NT = D / 16;  // output channel tiles
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nqb = (a.Sq + kMxQTile - 1) / kMxQTile;
+  // causal: the longest query tiles first
+  const int qb = CAUSAL ? nqb - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x);
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / (a.Hq / a.Hkv);
-  const int q0 = blockIdx.x * kQTile;
+  const int q0 = qb * kMxQTile;
+  const int qw0 = q0 + wave * (kQT * 16);  // first query row of this wave
   const int col = lane & 15;   // query column within a 16-query tile
   const int grp = lane >> 4;   // K-block / lane group
 
@@ -249,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   int qrow[kQT];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
-    qrow[t] = q0 + wave * (kQT * 16) + t * 16 + col;
+    qrow[t] = qw0 + t * 16 + col;
     const int64_t row = bh * a.Sq + qrow[t];  // rows past Sq land in zeroed padding
     if (grp < DC) {
       qop[t] = *reinterpret_cast<const uint4*>(a.qc + row * (D / 2) + grp * 16);
@@ -257,13 +290,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     } else {
       qop[t] = make_uint4(0, 0, 0, 0);
       qsc[t] = 127;
-    }
-  }
-  if (D == 64) {  // upper half of the contraction is zero for D = 64
-    for (int i = tid; i < 2 * kSub * 32; i += kThreads) {
-      const int sidx = i / (kSub * 32), t = (i / 32) % kSub, l = 32 + i % 32;
-      stage[sidx].kc[t * 64 + l] = make_uint4(0, 0, 0, 0);
-      stage[sidx].ks[t * 64 + l] = 127;
     }
   }
 
@@ -278,34 +304,51 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     for (int n = 0; n < NT; ++n) w.oacc[t][n] = v4f{0, 0, 0, 0};
   }
 
-  int ntiles = (a.Skv + kKvTile - 1) / kKvTile;
-  if (CAUSAL) ntiles = min(ntiles, static_cast<int>(blockIdx.x) + 1);  // Sq == Skv, kQTile == kKvTile
-  // only the last tile can hold keys past the end or past the causal diagonal
-  const bool mask_last = CAUSAL || (a.Skv % kKvTile != 0);
+  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles of the key sequence
+  // tiles this workgroup visits: all, or up to its last causal diagonal tile
+  const int ntiles = CAUSAL ? min(nt, (q0 + kMxQTile - 1) / kKvTile + 1) : nt;
+  // Tiles [0, nmain) are unmasked for every wave; the rest are computed
+  // masked.  A wave computes only the tiles up to its own last one: the
+  // sequence end, or its causal diagonal tile (its 32 rows lie in one KV
+  // tile); a wave whose rows all lie past Sq computes nothing.
+  const bool mask_last = a.Skv % kKvTile != 0;
+  const int nmain = CAUSAL ? min(q0 / kKvTile, nt) : (mask_last ? nt - 1 : nt);
+  const int last_w = qw0 >= a.Sq ? -1 : (CAUSAL ? min(qw0 / kKvTile, nt - 1) : nt - 1);
   int klim[kQT];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) klim[t] = CAUSAL ? min(a.Skv - 1, qrow[t]) : a.Skv - 1;
 
-  const uint8_t* kc_g = a.kc + bg * a.Skv * (D / 2);
-  const uint8_t* ks_g = a.ks + bg * a.Skv * DC;
-  const uint8_t* vc_g = a.vc + bg * D * (a.skv_ld / 2);
-  const uint8_t* vs_g = a.vs + bg * D * (a.skv_ld / 32);
+  const uint8_t* img = a.img + bg * nt * static_cast<int64_t>(IMG);
+  const int nl = loads_per_tile<D>(wave);
 
-  // Tiles 0 .. nfull-1 need no masking; a masked last tile (sequence end
-  // or causal diagonal) is handled after the loop.
-  const int nfull = mask_last ? ntiles - 1 : ntiles;
-  issue_tile<D>(stage[0], kc_g, ks_g, vc_g, vs_g, a.skv_ld, 0, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int jt = 0; jt < nfull; ++jt) {
-    if (jt + 1 < ntiles)  // the other stage was released by the last barrier
-      issue_tile<D>(stage[(jt + 1) & 1], kc_g, ks_g, vc_g, vs_g, a.skv_ld, (jt + 1) * kKvTile, wave, lane);
-    compute_tile<D, UOS, PNQ, DUMP, false>(w, stage[jt & 1], qop, qsc, qrow, klim, jt * kKvTile, lane, sl2, a, bh);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
-    __syncthreads();
+  // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  At the
+  // top of iteration jt the wave waits for its own loads of tile jt (the
+  // loads of tile jt+1 may stay in flight), then the barrier makes every
+  // wave's loads of tile jt visible and releases the stage of tile jt-1,
+  // which the loads of tile jt+2 then refill.
+  issue_tile<D>(lds0, img, wave, lane);
+  if (ntiles > 1) issue_tile<D>(lds1, img + IMG, wave, lane);
+  for (int jb = 0; jb < ntiles; jb += kStages) {
+#pragma unroll
+    for (int k = 0; k < kStages; ++k) {
+      const int jt = jb + k;
+      if (jt < ntiles) {
+        if (jt + 1 < ntiles) {
+          if (nl == 3) wait_vmcnt<3>(); else if (nl == 2) wait_vmcnt<2>(); else wait_vmcnt<1>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        uint8_t* nxt = k == 0 ? lds2 : k == 1 ? lds0 : lds1;  // stage of tile jt + 2
+        if (jt + 2 < ntiles) issue_tile<D>(nxt, img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
+        const uint8_t* st = k == 0 ? lds0 : k == 1 ? lds1 : lds2;
+        compute_tile<D, UOS, PNQ, DUMP>(w, st, qop, qsc, qrow, klim, jt >= nmain, jt <= last_w,
+                                        jt * kKvTile, lane, sl2, a, bh);
+      }
+    }
   }
-  if (mask_last)
-    compute_tile<D, UOS, PNQ, DUMP, true>(w, stage[nfull & 1], qop, qsc, qrow, klim, nfull * kKvTile, lane, sl2, a, bh);
 
   // The epilogue stores under a per-lane condition.  Pin the accumulators
   // here so that the matrix-core instructions producing them are not moved
@@ -338,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
 hipError_t launch_t(const MxAttnArgs& a, hipStream_t s) {
-  dim3 grid((a.Sq + kQTile - 1) / kQTile, a.Hq, a.B);
+  dim3 grid((a.Sq + kMxQTile - 1) / kMxQTile, a.Hq, a.B);
   const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
   hipLaunchKernelGGL((attn_mx_kernel<D, UOS, PNQ, CAUSAL, DUMP>), grid, dim3(kThreads), 0, s, a, sl2);
   return hipGetLastError();

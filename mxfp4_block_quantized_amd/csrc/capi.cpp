@@ -57,16 +57,15 @@ Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, in
       L.off[2] = take(static_cast<size_t>(B) * Hkv * Skv * D * 2);   // K fp16
     }
   } else {
-    // one extra tile of zero rows after Q~ and K~ so the last tile's loads
+    // one extra query tile of zero rows after Q~ so the last tile's loads
     // stay inside the buffer
-    const size_t q_rows = static_cast<size_t>(B) * Hq * Sq + mxk::kQTile;
-    const size_t k_rows = static_cast<size_t>(B) * Hkv * Skv + mxk::kKvTile;
+    const size_t q_rows = static_cast<size_t>(B) * Hq * Sq + mxk::kMxQTile;
     L.off[0] = take(q_rows * D / 2);
     L.off[1] = take(q_rows * D / 32);
-    L.off[2] = take(k_rows * D / 2);
-    L.off[3] = take(k_rows * D / 32);
-    L.off[4] = take(static_cast<size_t>(B) * Hkv * D * skv_ld / 2);
-    L.off[5] = take(static_cast<size_t>(B) * Hkv * D * skv_ld / 32);
+    L.off[2] = take(static_cast<size_t>(B) * Hkv * (skv_ld / mxk::kKvTile) * mxk::img_bytes(D));
+    L.off[3] = static_cast<size_t>(mxk::img_bytes(D));
+    L.off[4] = 0;
+    L.off[5] = 0;
   }
   L.total = cur;
   return L;
@@ -111,14 +110,11 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
     return MX_OK;
   }
   const int uos = (mode == MXATTN_OCP) ? 0 : 1;
-  e = mxk::launch_quant_rows(q, nq, nq + static_cast<int64_t>(mxk::kQTile) * D, dt, uos,
+  e = mxk::launch_quant_rows(q, nq, nq + static_cast<int64_t>(mxk::kMxQTile) * D, dt, uos,
                              w + L.off[0], w + L.off[1], s);
   if (e != hipSuccess) return MX_ERR_HIP;
-  e = mxk::launch_quant_rows(k, nk, nk + static_cast<int64_t>(mxk::kKvTile) * D, dt, uos,
-                             w + L.off[2], w + L.off[3], s);
-  if (e != hipSuccess) return MX_ERR_HIP;
-  e = mxk::launch_quant_cols(v, static_cast<int64_t>(B) * Hkv, Skv, D, L.skv_ld, dt, uos,
-                             w + L.off[4], w + L.off[5], s);
+  e = mxk::launch_quant_kv_images(k, v, static_cast<int64_t>(B) * Hkv, Skv, D, dt, uos,
+                                  w + L.off[2], s);
   return to_status(e);
 }
 
@@ -148,8 +144,7 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
   }
   mxk::MxAttnArgs a{};
   a.qc = w + L.off[0]; a.qs = w + L.off[1];
-  a.kc = w + L.off[2]; a.ks = w + L.off[3];
-  a.vc = w + L.off[4]; a.vs = w + L.off[5];
+  a.img = w + L.off[2];
   a.o = o;
   a.row_slot = row_slot;
   a.p_codes = p_codes;

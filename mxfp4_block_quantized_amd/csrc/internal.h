@@ -14,8 +14,19 @@ constexpr int kBlock = 32;
 
 // Keys per KV tile of both attention kernels (the running-max schedule).
 constexpr int kKvTile = 128;
-// Query rows per attention workgroup.
+// Query rows per workgroup of the 16-bit attention kernel.
 constexpr int kQTile = 128;
+// Query rows per workgroup of the MXFP4 attention kernel.
+constexpr int kMxQTile = 256;
+
+// KV tile image: the quantized K~ and V~ of one 128-key tile, stored in
+// matrix-core operand order so that the attention kernel moves it to LDS
+// with contiguous 16-byte-per-lane loads (layout in include/mxattn.h).
+constexpr int kImgKc = 0;     // K~ codes: 8 subtiles x 64 lanes x 16 B
+constexpr int kImgVc = 8192;  // V~ codes: D/16 channel tiles x 64 lanes x 16 B
+__host__ __device__ constexpr int img_ks(int D) { return kImgVc + 64 * D; }  // [lane][8]
+__host__ __device__ constexpr int img_vs(int D) { return img_ks(D) + 512; }  // [lane][D/16]
+__host__ __device__ constexpr int img_bytes(int D) { return (img_vs(D) + 4 * D + 1023) / 1024 * 1024; }
 
 enum class Dtype : int { F32 = 0, BF16 = 1 };
 
@@ -32,6 +43,13 @@ hipError_t launch_quant_cols(const void* x, int64_t batch, int64_t rows,
                              uint8_t* codes_t, uint8_t* scales_t,
                              hipStream_t stream);
 
+// Quantize K [batch][rows][D] (blocks along D) and V [batch][rows][D]
+// (blocks along rows) into KV tile images [batch][ntiles][img_bytes(D)],
+// ntiles = ceil(rows / kKvTile); rows past the end are quantized as zeros.
+hipError_t launch_quant_kv_images(const void* k, const void* v, int64_t batch, int rows,
+                                  int D, Dtype dt, int uos, uint8_t* img,
+                                  hipStream_t stream);
+
 // Dequantize n elements to fp32 (out_bf16 == 0) or bf16.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
                           int out_bf16, void* y, hipStream_t stream);
@@ -40,10 +58,7 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n
 struct MxAttnArgs {
   const uint8_t* qc;   // [B*Hq*Sq (+pad)][D/2]
   const uint8_t* qs;   // [B*Hq*Sq (+pad)][D/32]
-  const uint8_t* kc;   // [B*Hkv*Skv (+pad)][D/2]
-  const uint8_t* ks;   // [B*Hkv*Skv (+pad)][D/32]
-  const uint8_t* vc;   // [B*Hkv][D][skv_ld/2]
-  const uint8_t* vs;   // [B*Hkv][D][skv_ld/32]
+  const uint8_t* img;  // KV tile images [B*Hkv][skv_ld/128][img_bytes(D)]
   float* o;            // [B][Hq][Sq][D]
   const int32_t* row_slot;  // dump only: [B*Hq*Sq]
   uint8_t* p_codes;         // dump only: [nslots][skv_ld/2]

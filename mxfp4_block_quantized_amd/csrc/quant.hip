@@ -171,6 +171,113 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
   scales_t[col * (rows_pad / kBlock) + gr0 / kBlock] = static_cast<uint8_t>(X);
 }
 
+// KV tile images (layout in include/mxattn.h).  Rows at or past `rows` are
+// quantized as zeros (codes 0, E8M0 byte 0), as are the unused upper
+// contraction lanes of K~ for D = 64.
+//
+// K~: octet-per-lane as in quant_rows_kernel; block (row kr, d-block c)
+// lands in subtile t = (kr % 128 / 4) % 8, lane 16c + 4((kr % 128) / 32) +
+// kr % 4 of its tile, the operand order of the S^T product.
+template <typename In, int UOS, int D>
+__global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
+    const In* __restrict__ x, int rows, int ntiles, int blocks_per_batch,
+    uint8_t* __restrict__ img) {
+  constexpr int OPR = D / 8;  // octets per row
+  constexpr int IMG = img_bytes(D);
+  const int bgi = blockIdx.x / blocks_per_batch;
+  const int o = (blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
+  const int kr = o / OPR;
+  if (kr >= ntiles * kKvTile) return;  // whole quads: OPR is a multiple of 4
+  const int w = o % OPR;
+  uint32_t f[8];
+  if (kr < rows) {
+    load8(x + (static_cast<int64_t>(bgi) * rows + kr) * D, w, f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = 0u;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, f[i] & 0x7FFFFFFFu);
+  const uint32_t X = e8m0_of_amax<UOS>(quad_max_u32(m));
+  const uint32_t r = pack8(f, inv_scale_of(X));
+  const int c = w >> 2, part = w & 3;
+  const int kk = kr % kKvTile;
+  const int t = (kk >> 2) & 7;
+  const int l = 16 * c + 4 * (kk >> 5) + (kk & 3);
+  uint8_t* base = img + (static_cast<int64_t>(bgi) * ntiles + kr / kKvTile) * IMG;
+  *reinterpret_cast<uint32_t*>(base + kImgKc + t * 1024 + l * 16 + part * 4) = r;
+  if (part == 0) base[img_ks(D) + l * 8 + t] = static_cast<uint8_t>(X);
+  if (D == 64) {  // upper half of the contraction: zero operands
+    *reinterpret_cast<uint32_t*>(base + kImgKc + t * 1024 + (l + 32) * 16 + part * 4) = 0u;
+    if (part == 0) base[img_ks(D) + (l + 32) * 8 + t] = 0;
+  }
+  // zero the padding at the end of the image
+  constexpr int kPadOff = img_vs(D) + 4 * D;
+  const int pi = kk * OPR + w;
+  if (pi < (IMG - kPadOff) / 4) *reinterpret_cast<uint32_t*>(base + kPadOff + pi * 4) = 0u;
+}
+
+// V~: blocks of 32 consecutive rows per channel.  A thread owns one 32-row
+// block of 16 bytes' worth of channels (8 bf16 or 4 fp32): 32 row loads of
+// 16 bytes, each wave instruction covering whole rows.  Block (channel d,
+// row block kb) lands in channel tile d / 16, lane 16 (kb % 4) + d % 16 of
+// tile kb / 4, the operand order of the O^T product.
+template <typename In>
+__device__ __forceinline__ uint32_t lane_bits(const uint4& r, int ch);
+template <>
+__device__ __forceinline__ uint32_t lane_bits<uint16_t>(const uint4& r, int ch) {
+  const uint32_t wv = (ch >> 1) == 0 ? r.x : (ch >> 1) == 1 ? r.y : (ch >> 1) == 2 ? r.z : r.w;
+  return (ch & 1) ? (wv & 0xFFFF0000u) : (wv << 16);
+}
+template <>
+__device__ __forceinline__ uint32_t lane_bits<float>(const uint4& r, int ch) {
+  return ch == 0 ? r.x : ch == 1 ? r.y : ch == 2 ? r.z : r.w;
+}
+
+template <typename In, int UOS, int D>
+__global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
+    const In* __restrict__ x, int rows, int ntiles, int blocks_per_batch,
+    uint8_t* __restrict__ img) {
+  constexpr int CPT = 16 / static_cast<int>(sizeof(In));  // channels per thread
+  constexpr int NCG = D / CPT;
+  constexpr int NT = D / 16;
+  constexpr int IMG = img_bytes(D);
+  const int bgi = blockIdx.x / blocks_per_batch;
+  const int i = (blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
+  const int cg = i % NCG, kb = i / NCG;
+  if (kb >= ntiles * (kKvTile / kBlock)) return;
+  const In* src = x + (static_cast<int64_t>(bgi) * rows + kb * kBlock) * D + cg * CPT;
+  uint4 r[kBlock];
+#pragma unroll
+  for (int k = 0; k < kBlock; ++k)
+    r[k] = (kb * kBlock + k < rows) ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(k) * D)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+  uint8_t* base = img + (static_cast<int64_t>(bgi) * ntiles + kb / (kKvTile / kBlock)) * IMG;
+  const int c = kb % (kKvTile / kBlock);
+#pragma unroll
+  for (int ch = 0; ch < CPT; ++ch) {
+    uint32_t f[kBlock];
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock; ++k) {
+      f[k] = lane_bits<In>(r[k], ch);
+      m = max(m, f[k] & 0x7FFFFFFFu);
+    }
+    const uint32_t X = e8m0_of_amax<UOS>(m);
+    const float inv = inv_scale_of(X);
+    uint4 out;
+    out.x = pack8(f + 0, inv);
+    out.y = pack8(f + 8, inv);
+    out.z = pack8(f + 16, inv);
+    out.w = pack8(f + 24, inv);
+    const int d = cg * CPT + ch;
+    const int l = 16 * c + (d & 15);
+    *reinterpret_cast<uint4*>(base + kImgVc + (d >> 4) * 1024 + l * 16) = out;
+    base[img_vs(D) + l * NT + (d >> 4)] = static_cast<uint8_t>(X);
+  }
+}
+
 // Dequantize: each lane expands one dword of codes (8 elements).
 // Magnitudes times 2: {0,1,2,3,4,6,8,12} packed as nibbles.
 __device__ __forceinline__ float dq(uint32_t code, int ex) {
@@ -205,7 +312,39 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
   }
 }
 
+template <typename In, int UOS, int D>
+hipError_t launch_kv_images_t(const void* k, const void* v, int64_t batch, int rows,
+                              int ntiles, uint8_t* img, hipStream_t stream) {
+  const int kper = (ntiles * kKvTile * (D / 8) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((quant_kimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * kper)),
+                     dim3(kThreads), 0, stream, static_cast<const In*>(k), rows, ntiles, kper, img);
+  constexpr int CPT = 16 / static_cast<int>(sizeof(In));
+  const int vper = (ntiles * (kKvTile / kBlock) * (D / CPT) + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((quant_vimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * vper)),
+                     dim3(kThreads), 0, stream, static_cast<const In*>(v), rows, ntiles, vper, img);
+  return hipGetLastError();
+}
+
+template <typename In, int UOS>
+hipError_t launch_kv_images_d(const void* k, const void* v, int64_t batch, int rows, int D,
+                              int ntiles, uint8_t* img, hipStream_t stream) {
+  return D == 64 ? launch_kv_images_t<In, UOS, 64>(k, v, batch, rows, ntiles, img, stream)
+                 : launch_kv_images_t<In, UOS, 128>(k, v, batch, rows, ntiles, img, stream);
+}
+
 }  // namespace
+
+hipError_t launch_quant_kv_images(const void* k, const void* v, int64_t batch, int rows,
+                                  int D, Dtype dt, int uos, uint8_t* img,
+                                  hipStream_t stream) {
+  if (batch <= 0 || rows <= 0) return hipSuccess;
+  const int ntiles = (rows + kKvTile - 1) / kKvTile;
+  if (dt == Dtype::BF16)
+    return uos ? launch_kv_images_d<uint16_t, 1>(k, v, batch, rows, D, ntiles, img, stream)
+               : launch_kv_images_d<uint16_t, 0>(k, v, batch, rows, D, ntiles, img, stream);
+  return uos ? launch_kv_images_d<float, 1>(k, v, batch, rows, D, ntiles, img, stream)
+             : launch_kv_images_d<float, 0>(k, v, batch, rows, D, ntiles, img, stream);
+}
 
 hipError_t launch_quant_rows(const void* x, int64_t n, int64_t n_write, Dtype dt,
                              int uos, uint8_t* codes, uint8_t* scales,

@@ -67,3 +67,40 @@ def flips(gpu_codes, gpu_scales, ref_codes, ref_scales, nkeys):
     diff = gv != rv
     sdiff = gpu_scales[:, :nb] != ref_scales[:, :nb]
     return float(diff.mean()), float(sdiff.mean()), int(diff.sum())
+
+
+def decode_kv_images(w, off, B, Hkv, Skv, D):
+    """Read the KV tile images of a workspace (layout documented in
+    include/mxattn.h) back into plain arrays: K~ codes [B*Hkv][rows][D/2],
+    K~ scales [B*Hkv][rows][D/32], V~^T codes [B*Hkv][D][rows/2], V~^T
+    scales [B*Hkv][D][rows/32] with rows = Skv rounded up to 128, plus the
+    K~ bytes of the unused contraction lanes (D = 64), which must be zero."""
+    BG, IMG = B * Hkv, off[3]
+    nt = (Skv + 127) // 128
+    NT = D // 16
+    ks_off = 8192 + 64 * D
+    vs_off = ks_off + 512
+    im = w[off[2]:off[2] + BG * nt * IMG].reshape(BG, nt, IMG)
+    T, t, l = np.meshgrid(np.arange(nt), np.arange(8), np.arange(64), indexing="ij")
+    krow = T * 128 + 32 * ((l % 16) // 4) + 4 * t + l % 4
+    kblk = l // 16
+    kc = im[:, :, :8192].reshape(BG, nt, 8, 64, 16)
+    ksc = im[:, :, ks_off:ks_off + 512].reshape(BG, nt, 64, 8)
+    k_codes = np.zeros((BG, nt * 128, 4, 16), np.uint8)
+    k_scales = np.zeros((BG, nt * 128, 4), np.uint8)
+    k_codes[:, krow, kblk, :] = kc[:, T, t, l, :]
+    k_scales[:, krow, kblk] = ksc[:, T, l, t]
+    dc = D // 32
+    unused = np.concatenate([k_codes[:, :, dc:, :].ravel(), k_scales[:, :, dc:].ravel()])
+    T, n, l = np.meshgrid(np.arange(nt), np.arange(NT), np.arange(64), indexing="ij")
+    ch = 16 * n + l % 16
+    vblk = T * 4 + l // 16
+    vc = im[:, :, 8192:8192 + 64 * D].reshape(BG, nt, NT, 64, 16)
+    vsc = im[:, :, vs_off:vs_off + 4 * D].reshape(BG, nt, 64, NT)
+    vt_codes = np.zeros((BG, D, nt * 4, 16), np.uint8)
+    vt_scales = np.zeros((BG, D, nt * 4), np.uint8)
+    vt_codes[:, ch, vblk, :] = vc[:, T, n, l, :]
+    vt_scales[:, ch, vblk] = vsc[:, T, l, n]
+    pad = im[:, :, vs_off + 4 * D:]
+    return (k_codes[:, :, :dc, :].reshape(BG, nt * 128, D // 2), k_scales[:, :, :dc],
+            vt_codes.reshape(BG, D, nt * 64), vt_scales, unused, pad)

@@ -84,6 +84,10 @@ def test_workspace_and_tile_queries():
     # Q~ + K~ + V~^T at 0.53125 bytes per element, plus padding
     assert 3 * 40 * 32760 * 128 * 17 // 32 <= nb < 3 * 40 * 32768 * 128 * 17 // 32 + 4096 * 128
     off, ld = mx.workspace_layout(1, 40, 40, 32760, 32760, 128, "bf16", "uos_pnq")
-    assert ld == 32768 and off == sorted(off) and all(o % 256 == 0 for o in off)
+    assert ld == 32768 and off[0] < off[1] < off[2] and off[3:] == [17408, 0, 0]
+    assert all(o % 256 == 0 for o in off[:3])
+    assert off[2] + 40 * 256 * 17408 <= nb
+    off64, _ = mx.workspace_layout(1, 2, 2, 100, 100, 64, "f32", "ocp")
+    assert off64[3] == 13312
     with pytest.raises(mx.MxError):
         mx.workspace_layout(1, 2, 2, 64, 64, 128, "bf16", "fp16")

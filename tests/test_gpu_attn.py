@@ -11,8 +11,8 @@ import functools
 import numpy as np
 import pytest
 
-from common import (FLIP_MAX, MAX_ABS, MEAN_ABS, MODE_IDS, RULE_IDS, RULE_OF_MODE, flips, gpu,
-                    mxsynth, np_u8, oracle, to_torch)
+from common import (FLIP_MAX, MAX_ABS, MEAN_ABS, MODE_IDS, RULE_IDS, RULE_OF_MODE,
+                    decode_kv_images, flips, gpu, mxsynth, np_u8, oracle, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,18 +27,22 @@ def check_workspace(mx, ws, q, k, v, mode):
                                       "bf16" if q.dtype == np.uint16 else "f32", mode)
     w = np_u8(ws)
     rule = RULE_IDS[RULE_OF_MODE[mode]]
-    for x, oc, os_ in ((q, off[0], off[1]), (k, off[2], off[3])):
-        rc, rs = oracle.quantize(x, rule)
-        assert np.array_equal(w[oc:oc + rc.size], rc)
-        assert np.array_equal(w[os_:os_ + rs.size], rs)
-    pad = (Skv + 31) // 32 * 32
-    vc = w[off[4]:off[4] + B * Hkv * D * skv_ld // 2].reshape(B * Hkv, D, skv_ld // 2)
-    vs = w[off[5]:off[5] + B * Hkv * D * skv_ld // 32].reshape(B * Hkv, D, skv_ld // 32)
+    rc, rs = oracle.quantize(q, rule)
+    assert np.array_equal(w[off[0]:off[0] + rc.size], rc)
+    assert np.array_equal(w[off[1]:off[1] + rs.size], rs)
+    kc, ks, vc, vs, unused, pad = decode_kv_images(w, off, B, Hkv, Skv, D)
+    assert skv_ld == kc.shape[1]
+    assert not unused.any() and not pad.any()
+    pad32 = (Skv + 31) // 32 * 32
     for bg in range(B * Hkv):
+        rc, rs = oracle.quantize(k.reshape(B * Hkv, Skv, D)[bg], rule)
+        assert np.array_equal(kc[bg][:Skv], rc.reshape(Skv, D // 2))
+        assert np.array_equal(ks[bg][:Skv], rs.reshape(Skv, D // 32))
+        assert not kc[bg][Skv:].any() and not ks[bg][Skv:].any()
         rc, rs = oracle.quantize_t(v.reshape(B * Hkv, Skv, D)[bg], rule)
-        assert np.array_equal(vc[bg][:, :pad // 2], rc)
-        assert np.array_equal(vs[bg][:, :pad // 32], rs)
-        assert not vc[bg][:, pad // 2:].any() and not vs[bg][:, pad // 32:].any()
+        assert np.array_equal(vc[bg][:, :pad32 // 2], rc)
+        assert np.array_equal(vs[bg][:, :pad32 // 32], rs)
+        assert not vc[bg][:, pad32 // 2:].any() and not vs[bg][:, pad32 // 32:].any()
 
 
 def run_case(q, k, v, causal, mode, rows=None, check_ws=True, label=""):
