@@ -42,13 +42,13 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQT = 2;              // 16-query tiles per wave
 constexpr int kSub = kKvTile / 16;  // key subtiles per KV tile (8)
 constexpr int kStages = 3;          // LDS ring of KV tile images
 static_assert(kMxQTile == kWaves * kQT * 16, "query tile = waves x q-tiles x 16");
-static_assert(kMxQTile == 2 * kKvTile, "the causal tail below assumes two KV tiles per query tile");
+static_assert(kMxQTile % kKvTile == 0, "query tiles start on KV tile boundaries");
 
 template <int SEL_A>
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, uint32_t sa, int sb) {
@@ -134,21 +134,151 @@ __device__ __forceinline__ int loads_per_tile(int wave) {
   return NL / kWaves + (wave < NL % kWaves ? 1 : 0);
 }
 
-// One KV tile (keys j0 .. j0+127) for this wave's kQT query tiles.  MASK:
-// keys beyond klim[u] (sequence end, causal diagonal) are excluded.
+// S^T of one 16-query tile on the matrix core: d = S - mref, with -mref
+// (the running max of the previous tiles, 0 before the first) as the
+// accumulator input, so the subtraction happens before the single rounding
+// of the result and elements near the maximum keep full relative precision.
+__device__ __forceinline__ void s_tile(v4f (&s)[kSub], const uint4 (&kop)[kSub], const uint2& ksc,
+                                       const uint4& qop, int qsc, float mref) {
+  const v4f cneg = {-mref, -mref, -mref, -mref};
+#pragma unroll
+  for (int t = 0; t < kSub; ++t)
+    s[t] = mfma_fp4_sel(kop[t], qop, cneg, t < 4 ? ksc.x : ksc.y, t & 3, qsc);
+}
+
+// Keys past `lim` (relative to this lane's 32-key block) are excluded.
+__device__ __forceinline__ void mask_tile(v4f (&s)[kSub], int lim) {
+  asm volatile("" : "+v"(lim));  // keeps the compares inside the caller's branch
+#pragma unroll
+  for (int t = 0; t < kSub; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[t][r] = (t * 4 + r > lim) ? -INFINITY : s[t][r];
+}
+
+// Online-softmax step of one query tile: row max, history factor alpha,
+// this lane's P~ block scale (X, e) and the offset kofs of the scaled
+// domain; rescales the history when any row's max moved.
+struct TileStats {
+  float alpha, kofs;
+  int X;
+};
+template <int D, int UOS, int PNQ>
+__device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
+  constexpr int NT = D / 16;
+  // row max: in-lane over this lane's 32-key block (a v_max3 chain), then
+  // across the four lanes holding this query
+  float bmax = s[0][0];
+#pragma unroll
+  for (int i = 1; i + 1 < 4 * kSub; i += 2)
+    bmax = fmaxf(fmaxf(bmax, s[i >> 2][i & 3]), s[(i + 1) >> 2][(i + 1) & 3]);
+  bmax = fmaxf(bmax, s[kSub - 1][3]);
+  // delta = new max - mref.  Before the first tile the running max is -inf
+  // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
+  const float delta = fmaxf(w.m[u] - w.mref[u], xlane_max4(bmax));
+  TileStats r;
+  r.alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);  // 0 at first
+  w.m[u] = w.mref[u] + delta;
+  w.mref[u] = w.m[u];
+  // scale of this lane's P~ block (the block holding the row maximum gets
+  // x = 0 exactly); in the scaled domain
+  // log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
+  const float e = p_block_exp<UOS>((bmax - delta) * sl2);
+  r.X = static_cast<int>(e) + 127;
+  r.kofs = fmaf(delta, sl2, e);
+  // history rescale: alpha == 1 exactly leaves the history unchanged, so
+  // the multiplies are skipped when that holds for the whole wave
+  if (__builtin_amdgcn_ballot_w64(r.alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) w.oacc[u][n] *= r.alpha;
+    if (PNQ) w.lacc[u] *= r.alpha;
+  }
+  return r;
+}
+
+// P~ block of this lane: v = exp2(d*c - kofs) rounded to E2M1 (nearest
+// even, saturating), packed in MFMA operand order; vsum = sum of v.
+template <int PNQ>
+__device__ __forceinline__ uint4 p_tile(const v4f (&s)[kSub], float sl2, float kofs, float& vsum) {
+  uint32_t pw[4];
+  vsum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // dword q holds key subtiles 2q and 2q+1
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3], sl2, -kofs));
+      if (!PNQ) vsum += v[i];
+    }
+    // all four bytes are written, so the chain may start from any value
+    uint32_t x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(v[0]), v[0], v[1], 1.0f, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[4], v[5], 1.0f, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[6], v[7], 1.0f, 3);
+    pw[q] = x;
+  }
+  return make_uint4(pw[0], pw[1], pw[2], pw[3]);
+}
+
+// Denominator and O^T += V~^T P~^T for one query tile.
+template <int D, int PNQ>
+__device__ __forceinline__ void pv_tile(WaveState<D>& w, int u, const uint4& pop, const TileStats& ts,
+                                        float vsum, const uint4 (&vop)[D / 16], const uint32_t* vsc) {
+  constexpr int NT = D / 16;
+  if (PNQ) {
+    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
+    w.lacc[u] = mfma_fp4<0>(ones, pop, w.lacc[u], 127, ts.X);
+  } else {
+    w.lsum[u] = fmaf(w.lsum[u], ts.alpha, __builtin_amdgcn_ldexpf(vsum, ts.X - 127));
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) w.oacc[u][n] = mfma_fp4_sel(vop[n], pop, w.oacc[u][n], vsc[n >> 2], n & 3, ts.X);
+}
+
+template <int DUMP>
+__device__ __forceinline__ void dump_tile(const MxAttnArgs& a, int64_t bh, int qrow, bool visit, int j0,
+                                          int grp, const uint4& pop, int X) {
+  if (DUMP && visit && qrow < a.Sq) {
+    const int slot = a.row_slot[bh * a.Sq + qrow];
+    if (slot >= 0) {
+      *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) + (j0 + grp * 32) / 2) = pop;
+      a.p_scales[static_cast<int64_t>(slot) * (a.skv_ld / 32) + (j0 + grp * 32) / 32] = static_cast<uint8_t>(X);
+    }
+  }
+}
+
+// Interleave n matrix-core instructions with the vector work around them
+// (k VALU instructions after each), so that the transcendental unit runs
+// while the matrix core is busy.
+template <int N, int K>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);  // VALU
+  }
+}
+
+// One KV tile (keys j0 .. j0+127) for this wave's two query tiles, as a
+// two-stage software pipeline: S^T of query tile 1 runs on the matrix core
+// while P~ of query tile 0 is formed, and O^T of tile 0 while P~ of tile 1
+// is formed.  mask: keys beyond klim[u] (sequence end, causal diagonal) are
+// excluded.  visit: the rows reach this tile (only the P~ dump uses it).
 template <int D, int UOS, int PNQ, int DUMP>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, const uint8_t* st, const uint4 (&qop)[kQT],
                                              const int (&qsc)[kQT], const int (&qrow)[kQT],
-                                             const int (&klim)[kQT], bool mask, bool visit, int j0, int lane, float sl2,
-                                             const MxAttnArgs& a, int64_t bh) {
+                                             const int (&klim)[kQT], bool mask, bool visit, int j0, int lane,
+                                             float sl2, const MxAttnArgs& a, int64_t bh) {
+  static_assert(kQT == 2, "two query tiles per wave");
   constexpr int NT = D / 16;
   const int grp = lane >> 4;
-  const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
 
   uint4 kop[kSub];
 #pragma unroll
   for (int t = 0; t < kSub; ++t) kop[t] = *reinterpret_cast<const uint4*>(st + kImgKc + t * 1024 + lane * 16);
   const uint2 ksc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
+  uint4 vop[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) vop[n] = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
   uint32_t vsc[(NT + 3) / 4];
   if (NT == 8) {
     const uint2 v2 = *reinterpret_cast<const uint2*>(st + img_vs(D) + lane * 8);
@@ -158,98 +288,33 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const uint8_t* st,
     vsc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
   }
 
-#pragma unroll
-  for (int u = 0; u < kQT; ++u) {
-    // d = S - mref on the matrix core: the accumulator input is -mref, the
-    // running max of the previous tiles (0 before the first), so the
-    // subtraction happens before the single rounding of the result and the
-    // elements near the maximum keep full relative precision.
-    const float nm = -w.mref[u];
-    const v4f cneg = {nm, nm, nm, nm};
-    v4f s[kSub];
-#pragma unroll
-    for (int t = 0; t < kSub; ++t)
-      s[t] = mfma_fp4_sel(kop[t], qop[u], cneg, t < 4 ? ksc.x : ksc.y, t & 3, qsc[u]);
-    if (mask) {
-      int lim = klim[u] - (j0 + grp * 32);  // last unmasked key of this lane's block
-      asm volatile("" : "+v"(lim));  // keeps the compares inside this branch
-#pragma unroll
-      for (int t = 0; t < kSub; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s[t][r] = (t * 4 + r > lim) ? -INFINITY : s[t][r];
-    }
-    // row max: in-lane over this lane's 32-key block (a v_max3 chain), then
-    // across the four lanes holding this query
-    float bmax = s[0][0];
-#pragma unroll
-    for (int i = 1; i + 1 < 4 * kSub; i += 2)
-      bmax = fmaxf(fmaxf(bmax, s[i >> 2][i & 3]), s[(i + 1) >> 2][(i + 1) & 3]);
-    bmax = fmaxf(bmax, s[kSub - 1][3]);
-    // delta = new max - mref.  Before the first tile the running max is -inf
-    // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
-    const float delta = fmaxf(w.m[u] - w.mref[u], xlane_max4(bmax));
-    const float alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);  // 0 at first
-    w.m[u] = w.mref[u] + delta;
-    w.mref[u] = w.m[u];
+  v4f s0[kSub], s1[kSub];
+  s_tile(s0, kop, ksc, qop[0], qsc[0], w.mref[0]);
+  if (mask) mask_tile(s0, klim[0] - (j0 + grp * 32));
+  const TileStats t0 = tile_stats<D, UOS, PNQ>(w, 0, s0, sl2);
 
-    // scale of this lane's P~ block (the block holding the row maximum gets
-    // x = 0 exactly), then the block in the scaled domain:
-    // log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
-    const float e = p_block_exp<UOS>((bmax - delta) * sl2);
-    const int X = static_cast<int>(e) + 127;
-    const float kofs = fmaf(delta, sl2, e);
-    uint32_t pw[4];
-    float vsum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {  // dword q holds key subtiles 2q and 2q+1
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3], sl2, -kofs));
-        if (!PNQ) vsum += v[i];
-      }
-      // all four bytes are written, so the chain may start from any value
-      uint32_t x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(v[0]), v[0], v[1], 1.0f, 0);
-      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 1);
-      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[4], v[5], 1.0f, 2);
-      x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[6], v[7], 1.0f, 3);
-      pw[q] = x;
-    }
-    const uint4 pop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+  float vsum0, vsum1;
+  s_tile(s1, kop, ksc, qop[1], qsc[1], w.mref[1]);
+  uint4 pop0 = p_tile<PNQ>(s0, sl2, t0.kofs, vsum0);
+  interleave_mfma_valu<kSub, 8>();
+  // keep P~ of tile 0 here, beside the S^T products of tile 1, instead of
+  // letting the compiler sink it next to its matrix-core use
+  asm volatile("" : "+v"(pop0.x), "+v"(pop0.y), "+v"(pop0.z), "+v"(pop0.w), "+v"(vsum0));
+  dump_tile<DUMP>(a, bh, qrow[0], visit, j0, grp, pop0, t0.X);
 
-    if (DUMP && visit && qrow[u] < a.Sq) {
-      const int slot = a.row_slot[bh * a.Sq + qrow[u]];
-      if (slot >= 0) {
-        *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) +
-                                  (j0 + grp * 32) / 2) = pop;
-        a.p_scales[static_cast<int64_t>(slot) * (a.skv_ld / 32) + (j0 + grp * 32) / 32] =
-            static_cast<uint8_t>(X);
-      }
-    }
+  if (mask) mask_tile(s1, klim[1] - (j0 + grp * 32));
+  const TileStats t1 = tile_stats<D, UOS, PNQ>(w, 1, s1, sl2);
 
-    // history rescale: alpha == 1 exactly leaves the history unchanged, so
-    // the multiplies are skipped when that holds for the whole wave
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) w.oacc[u][n] *= alpha;
-      if (PNQ) w.lacc[u] *= alpha;
-    }
-    if (PNQ) {
-      w.lacc[u] = mfma_fp4<0>(ones, pop, w.lacc[u], 127, X);
-    } else {
-      w.lsum[u] = fmaf(w.lsum[u], alpha, __builtin_amdgcn_ldexpf(vsum, X - 127));
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint4 vop = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
-      w.oacc[u][n] = mfma_fp4_sel(vop, pop, w.oacc[u][n], vsc[n >> 2], n & 3, X);
-    }
-  }
+  pv_tile<D, PNQ>(w, 0, pop0, t0, vsum0, vop, vsc);
+  const uint4 pop1 = p_tile<PNQ>(s1, sl2, t1.kofs, vsum1);
+  interleave_mfma_valu<NT + PNQ, 6>();
+  dump_tile<DUMP>(a, bh, qrow[1], visit, j0, grp, pop1, t1.X);
+
+  pv_tile<D, PNQ>(w, 1, pop1, t1, vsum1, vop, vsc);
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
-__global__ __launch_bounds__(kThreads, 1) void attn_mx_kernel(MxAttnArgs a, float sl2) {
+__global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, float sl2) {
   constexpr int IMG = img_bytes(D);
   // One LDS object per stage, so that the compiler can tell which stage a
   // read touches and wait only for the direct loads into that stage.
@@ -334,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mx_kernel(MxAttnArgs a, floa
       const int jt = jb + k;
       if (jt < ntiles) {
         if (jt + 1 < ntiles) {
-          if (nl == 3) wait_vmcnt<3>(); else if (nl == 2) wait_vmcnt<2>(); else wait_vmcnt<1>();
+          if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else wait_vmcnt<3>();
         } else {
           wait_vmcnt<0>();
         }

@@ -17,7 +17,7 @@ constexpr int kKvTile = 128;
 // Query rows per workgroup of the 16-bit attention kernel.
 constexpr int kQTile = 128;
 // Query rows per workgroup of the MXFP4 attention kernel.
-constexpr int kMxQTile = 256;
+constexpr int kMxQTile = 128;
 
 // KV tile image: the quantized K~ and V~ of one 128-key tile, stored in
 // matrix-core operand order so that the attention kernel moves it to LDS
