@@ -190,7 +190,9 @@ __device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4
   if (__builtin_amdgcn_ballot_w64(r.alpha != 1.0f) != 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) w.oacc[u][n] *= r.alpha;
-    if (PNQ) w.lacc[u] *= r.alpha;
+    // the four lanes of a lacc column hold the same sum; only element 0 is
+    // read at the end, so only it is kept rescaled (the others stay finite)
+    if (PNQ) w.lacc[u][0] *= r.alpha;
   }
   return r;
 }
@@ -299,7 +301,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const uint8_t* st,
   interleave_mfma_valu<kSub, 8>();
   // keep P~ of tile 0 here, beside the S^T products of tile 1, instead of
   // letting the compiler sink it next to its matrix-core use
-  asm volatile("" : "+v"(pop0.x), "+v"(pop0.y), "+v"(pop0.z), "+v"(pop0.w), "+v"(vsum0));
+  asm volatile("" : "+v"(pop0.x), "+v"(pop0.y), "+v"(pop0.z), "+v"(pop0.w));
+  if (!PNQ) asm volatile("" : "+v"(vsum0));
   dump_tile<DUMP>(a, bh, qrow[0], visit, j0, grp, pop0, t0.X);
 
   if (mask) mask_tile(s1, klim[1] - (j0 + grp * 32));

@@ -22,6 +22,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Streamed data (read or written once) goes through nontemporal vector
+// accesses, so that it does not displace reused lines in the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // Largest |x| of a block, as the fp32 bit pattern, to the E8M0 byte.
 template <int UOS>
 __device__ __forceinline__ uint32_t e8m0_of_amax(uint32_t abits) {
@@ -49,7 +53,8 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
 // Eight consecutive elements as fp32 bit patterns.
 __device__ __forceinline__ void load8(const uint16_t* __restrict__ x, int64_t o,
                                       uint32_t f[8]) {
-  uint4 v = *reinterpret_cast<const uint4*>(x + o * 8);
+  const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + o * 8));
+  const uint4 v = make_uint4(vv[0], vv[1], vv[2], vv[3]);
   f[0] = v.x << 16; f[1] = v.x & 0xFFFF0000u;
   f[2] = v.y << 16; f[3] = v.y & 0xFFFF0000u;
   f[4] = v.z << 16; f[5] = v.z & 0xFFFF0000u;
@@ -57,8 +62,9 @@ __device__ __forceinline__ void load8(const uint16_t* __restrict__ x, int64_t o,
 }
 __device__ __forceinline__ void load8(const float* __restrict__ x, int64_t o,
                                       uint32_t f[8]) {
-  const uint4* p = reinterpret_cast<const uint4*>(x + o * 8);
-  uint4 a = p[0], b = p[1];
+  const u32x4* p = reinterpret_cast<const u32x4*>(x + o * 8);
+  const u32x4 av = __builtin_nontemporal_load(p), bv = __builtin_nontemporal_load(p + 1);
+  const uint4 a = make_uint4(av[0], av[1], av[2], av[3]), b = make_uint4(bv[0], bv[1], bv[2], bv[3]);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     uint32_t X = e8m0_of_amax<UOS>(quad_max_u32(m));
     uint32_t r = pack8(f[u], inv_scale_of(X));
     if (o[u] < n_oct_write) {
-      codes[o[u]] = r;
+      __builtin_nontemporal_store(r, codes + o[u]);
       if ((threadIdx.x & 3) == 0) scales[o[u] >> 2] = static_cast<uint8_t>(X);
     }
   }
@@ -251,8 +257,12 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
   uint4 r[kBlock];
 #pragma unroll
   for (int k = 0; k < kBlock; ++k)
-    r[k] = (kb * kBlock + k < rows) ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(k) * D)
-                                    : make_uint4(0u, 0u, 0u, 0u);
+    if (kb * kBlock + k < rows) {
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(k) * D));
+      r[k] = make_uint4(t[0], t[1], t[2], t[3]);
+    } else {
+      r[k] = make_uint4(0u, 0u, 0u, 0u);
+    }
   uint8_t* base = img + (static_cast<int64_t>(bgi) * ntiles + kb / (kKvTile / kBlock)) * IMG;
   const int c = kb % (kKvTile / kBlock);
 #pragma unroll
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     int64_t n_oct, void* __restrict__ y) {
   int64_t o = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (o >= n_oct) return;
-  uint32_t c = codes[o];
+  uint32_t c = __builtin_nontemporal_load(codes + o);
   const uint32_t X = scales[o >> 2];
   int ex = static_cast<int>(X) - 128;  // magnitude*2 * 2^(X-128)
   float v[8];
@@ -304,7 +314,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     w.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
     w.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
     w.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
-    reinterpret_cast<uint4*>(y)[o] = w;
+    const u32x4 wv = {w.x, w.y, w.z, w.w};
+    __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(y) + o);
   } else {
     float4* p = reinterpret_cast<float4*>(y) + 2 * o;
     p[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -350,7 +361,7 @@ hipError_t launch_quant_rows(const void* x, int64_t n, int64_t n_write, Dtype dt
                              int uos, uint8_t* codes, uint8_t* scales,
                              hipStream_t stream) {
   if (n_write <= 0) return hipSuccess;
-  constexpr int U = 4;
+  constexpr int U = 2;
   const int64_t n_oct = n / 8, n_oct_w = n_write / 8;
   const int64_t per_block = static_cast<int64_t>(kThreads) * U;
   dim3 grid(static_cast<unsigned>((n_oct_w + per_block - 1) / per_block));
