@@ -331,10 +331,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nqb = (a.Sq + kMxQTile - 1) / kMxQTile;
-  // causal: the longest query tiles first
-  const int qb = CAUSAL ? nqb - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x);
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin
+  // over the 8 XCDs (each with its own L2), workgroup i to XCD i % 8.  Each
+  // XCD is given a contiguous run of the head-major (head, query tile) list,
+  // so a head's K~/V~ tile images are fetched from HBM by one XCD (two at a
+  // run boundary) instead of all eight.
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int gi = (nwg >> 3) * xcd + min(xcd, nwg & 7) + (static_cast<int>(blockIdx.x) >> 3);
+  const int hb = gi / nqb;
+  // causal: the longest query tiles of a head first
+  const int qb = CAUSAL ? nqb - 1 - gi % nqb : gi % nqb;
+  const int h = hb % a.Hq;
+  const int b = hb / a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const int q0 = qb * kMxQTile;
   const int qw0 = q0 + wave * (kQT * 16);  // first query row of this wave
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
 hipError_t launch_t(const MxAttnArgs& a, hipStream_t s) {
-  dim3 grid((a.Sq + kMxQTile - 1) / kMxQTile, a.Hq, a.B);
+  dim3 grid(static_cast<unsigned>((a.Sq + kMxQTile - 1) / kMxQTile) * a.Hq * a.B);
   const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
   hipLaunchKernelGGL((attn_mx_kernel<D, UOS, PNQ, CAUSAL, DUMP>), grid, dim3(kThreads), 0, s, a, sl2);
   return hipGetLastError();
