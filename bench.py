@@ -153,7 +153,7 @@ def bench_quantizer(torch, mx, reps=20):
     return res
 
 
-def cpu_baseline(q, k, v, c, name, rows_per_head=1536):
+def cpu_baseline(q, k, v, c, name, rows_per_head=2048):
     """The oracle (as it stands) on a bounded, seeded sample of query rows of
     every head (about 10-20 s of CPU work at the DiT14 shape)."""
     import mxsynth
