@@ -136,10 +136,12 @@ int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                             int dtype, int mode, size_t *off, int64_t *skv_ld);
 
 /*
- * Keys per KV tile (Bc) of the attention kernel for this head size and mode.
- * The running max -- and hence the scale of every P~ block -- is updated
- * once per tile, in ascending key order, so a reference must use the same
- * Bc to reproduce P~.  Returns a negative status for unsupported D.
+ * Keys per KV tile (Bc) of the attention kernel for this head size and mode
+ * (128 in the MX modes, 64 in the FP16 mode).  The running max -- and hence
+ * the scale of every P~ block -- is updated once per tile, in ascending key
+ * order, so a reference must use the same Bc to reproduce P~ (the FP16 mode
+ * has no P~; there Bc only changes rounding).  Returns a negative status for
+ * unsupported D.
  */
 int mxattn_kv_tile(int D, int mode);
 
@@ -168,11 +170,12 @@ int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
  * mxattn_prepare: fills the workspace -- MX modes: Q~ (blocks along D) and
  * K~ / V~ (blocks along D / along keys) as KV tile images (see
  * mxattn_workspace_layout);
- * FP16 mode: fp16 V^T (and fp16 Q, K for fp32 inputs).
+ * FP16 mode: K and V^T as 16-bit tile images of 64 keys (K bf16 for bf16
+ * inputs, else fp16; V fp16), and fp16 Q for fp32 inputs.
  * mxattn_fwd_prepared: the fused attention kernel alone, reading the
  * operands a previous mxattn_prepare with the same sizes, dtype and mode
- * left in the workspace (q and k are read directly only in FP16 mode with
- * bf16 inputs; they may be NULL in the MX modes).  Arguments as for
+ * left in the workspace (q is read directly only in FP16 mode with bf16
+ * inputs; k is not read; both may be NULL otherwise).  Arguments as for
  * mxattn_fwd.  mxattn_fwd == mxattn_prepare followed by mxattn_fwd_prepared.
  */
 int mxattn_prepare(const void *q, const void *k, const void *v, int dtype,

@@ -19,7 +19,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Byte layout of the workspace used by mxattn_fwd.
 struct Layout {
-  size_t off[6];  // MX: qc qs kc ks vc vs | FP16: vt, q16, k16
+  size_t off[6];  // MX: qc qs images img-bytes | FP16: images, q16
   size_t total;
   int64_t skv_ld;
 };
@@ -51,11 +51,9 @@ Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, in
     return o;
   };
   if (mode == MXATTN_FP16) {
-    L.off[0] = take(static_cast<size_t>(B) * Hkv * D * skv_ld * 2);  // V^T fp16
-    if (dtype == MX_F32) {
-      L.off[1] = take(static_cast<size_t>(B) * Hq * Sq * D * 2);     // Q fp16
-      L.off[2] = take(static_cast<size_t>(B) * Hkv * Skv * D * 2);   // K fp16
-    }
+    const size_t nt = (static_cast<size_t>(Skv) + mxk::kF16KvTile - 1) / mxk::kF16KvTile;
+    L.off[0] = take(static_cast<size_t>(B) * Hkv * nt * mxk::f16_img_bytes(D));  // K / V^T images
+    if (dtype == MX_F32) L.off[1] = take(static_cast<size_t>(B) * Hq * Sq * D * 2);  // Q fp16
   } else {
     // one extra query tile of zero rows after Q~ so the last tile's loads
     // stay inside the buffer
@@ -93,18 +91,13 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
   uint8_t* w = static_cast<uint8_t*>(ws);
   const mxk::Dtype dt = dtype == MX_BF16 ? mxk::Dtype::BF16 : mxk::Dtype::F32;
   const int64_t nq = static_cast<int64_t>(B) * Hq * Sq * D;
-  const int64_t nk = static_cast<int64_t>(B) * Hkv * Skv * D;
   hipError_t e;
   if (mode == MXATTN_FP16) {
-    uint16_t* vt = reinterpret_cast<uint16_t*>(w + L.off[0]);
-    e = mxk::launch_v_to_f16t(v, static_cast<int64_t>(B) * Hkv, Skv, D, L.skv_ld, dt, vt, s);
+    e = mxk::launch_f16_images(k, v, static_cast<int64_t>(B) * Hkv, Skv, D, dt, w + L.off[0], s);
     if (e != hipSuccess) return MX_ERR_HIP;
     if (dtype == MX_F32) {
       e = mxk::launch_f32_to_f16(static_cast<const float*>(q), nq, nq,
                                  reinterpret_cast<uint16_t*>(w + L.off[1]), s);
-      if (e != hipSuccess) return MX_ERR_HIP;
-      e = mxk::launch_f32_to_f16(static_cast<const float*>(k), nk, nk,
-                                 reinterpret_cast<uint16_t*>(w + L.off[2]), s);
       if (e != hipSuccess) return MX_ERR_HIP;
     }
     return MX_OK;
@@ -128,14 +121,12 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
     mxk::F16AttnArgs a{};
     if (dtype == MX_F32) {
       a.q = w + L.off[1];
-      a.k = w + L.off[2];
       a.qk_f16 = 1;
     } else {
       a.q = q;
-      a.k = k;
       a.qk_f16 = 0;
     }
-    a.vt = reinterpret_cast<const uint16_t*>(w + L.off[0]);
+    a.img = w + L.off[0];
     a.o = o;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Skv = Skv; a.D = D;
     a.skv_ld = L.skv_ld;
@@ -255,7 +246,7 @@ int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int 
 int mxattn_kv_tile(int D, int mode) {
   if (mode < MXATTN_FP16 || mode > MXATTN_UOS_PNQ) return MX_ERR_ARG;
   if (D != 64 && D != 128) return MX_ERR_UNSUPPORTED;
-  return mxk::kKvTile;
+  return mode == MXATTN_FP16 ? mxk::kF16KvTile : mxk::kKvTile;
 }
 
 int mxattn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
@@ -280,10 +271,10 @@ int mxattn_fwd_prepared(const void* q, const void* k, int dtype, int B, int Hq, 
                         int Sq, int Skv, int D, int causal, int mode, float* o,
                         const void* workspace, size_t ws_bytes, void* stream) {
   Layout L;
-  const bool need_qk = (mode == MXATTN_FP16 && dtype == MX_BF16);
   int st = check_attn_call(q, k, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode,
-                           workspace, ws_bytes, need_qk, false, &L);
+                           workspace, ws_bytes, false, false, &L);
   if (st != MX_OK) return st;
+  if (mode == MXATTN_FP16 && dtype == MX_BF16 && !q) return MX_ERR_ARG;  // read directly
   if (!o) return MX_ERR_ARG;
   if (!aligned(o, 16)) return MX_ERR_ALIGN;
   return run_attention(q, k, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, L, workspace,

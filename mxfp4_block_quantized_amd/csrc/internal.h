@@ -18,6 +18,8 @@ constexpr int kKvTile = 128;
 constexpr int kQTile = 128;
 // Query rows per workgroup of the MXFP4 attention kernel.
 constexpr int kMxQTile = 128;
+// Keys per KV tile of the 16-bit (FP16-mode) attention kernel.
+constexpr int kF16KvTile = 64;
 
 // KV tile image: the quantized K~ and V~ of one 128-key tile, stored in
 // matrix-core operand order so that the attention kernel moves it to LDS
@@ -27,6 +29,12 @@ constexpr int kImgVc = 8192;  // V~ codes: D/16 channel tiles x 64 lanes x 16 B
 __host__ __device__ constexpr int img_ks(int D) { return kImgVc + 64 * D; }  // [lane][8]
 __host__ __device__ constexpr int img_vs(int D) { return img_ks(D) + 512; }  // [lane][D/16]
 __host__ __device__ constexpr int img_bytes(int D) { return (img_vs(D) + 4 * D + 1023) / 1024 * 1024; }
+
+// 16-bit tile image of the FP16 mode (64 keys): K as [subtile 4][step D/32]
+// [lane 64][8 x 16-bit], then V^T (fp16) as [channel tile D/16][key group 2]
+// [lane 64][8 x fp16].
+__host__ __device__ constexpr int f16_img_vc(int D) { return kF16KvTile * D * 2; }
+__host__ __device__ constexpr int f16_img_bytes(int D) { return 2 * kF16KvTile * D * 2; }
 
 enum class Dtype : int { F32 = 0, BF16 = 1 };
 
@@ -72,9 +80,8 @@ hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
 // Operands of the 16-bit attention kernel.
 struct F16AttnArgs {
-  const void* q;       // [B][Hq][Sq][D], bf16 (q_is_f16 == 0) or fp16
-  const void* k;       // [B][Hkv][Skv][D], same type as q
-  const uint16_t* vt;  // fp16 [B*Hkv][D][skv_ld]
+  const void* q;       // [B][Hq][Sq][D], bf16 (qk_f16 == 0) or fp16
+  const uint8_t* img;  // 16-bit tile images [B*Hkv][ceil(Skv/64)][f16_img_bytes(D)]
   float* o;
   int B, Hq, Hkv, Sq, Skv, D;
   int64_t skv_ld;
@@ -83,12 +90,12 @@ struct F16AttnArgs {
 };
 hipError_t launch_attn_f16(const F16AttnArgs& a, hipStream_t stream);
 
-// FP16-mode operand preparation: V [batch][rows][cols] (bf16 or fp32) to
-// fp16 V^T [batch][cols][rows_ld] (zero beyond rows); and fp32 -> fp16
-// conversion of n elements (zero-filling [n, n_write)).
-hipError_t launch_v_to_f16t(const void* v, int64_t batch, int64_t rows,
-                            int64_t cols, int64_t rows_ld, Dtype dt,
-                            uint16_t* vt, hipStream_t stream);
+// FP16-mode operand preparation: K and V [batch][rows][D] (bf16 or fp32)
+// into 16-bit tile images (K kept as bf16 for bf16 inputs, else fp16; V^T
+// fp16), rows past the end zero; and fp32 -> fp16 conversion of n elements
+// (zero-filling [n, n_write)).
+hipError_t launch_f16_images(const void* k, const void* v, int64_t batch, int rows, int D,
+                             Dtype dt, uint8_t* img, hipStream_t stream);
 hipError_t launch_f32_to_f16(const float* x, int64_t n, int64_t n_write,
                              uint16_t* y, hipStream_t stream);
 

@@ -77,7 +77,7 @@ def test_attention_rejects_bad_args():
 
 def test_workspace_and_tile_queries():
     L = mx.lib()
-    assert L.mxattn_kv_tile(128, 3) == 128 and L.mxattn_kv_tile(64, 0) == 128
+    assert L.mxattn_kv_tile(128, 3) == 128 and L.mxattn_kv_tile(64, 0) == 64
     assert L.mxattn_kv_tile(96, 3) == -2
     assert L.mxattn_workspace_bytes(1, 2, 1, 64, 64, 96, 1, 3) == 0
     nb = L.mxattn_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
