@@ -2,8 +2,10 @@
 // the MXFP4 modes are compared against.  Same FlashAttention loop as the FP4
 // kernel (running max per KV tile, fp32 accumulation, O / l at the end,
 // "EFQ-Softmax" abstract), with S^T = K Q^T on bf16 (or fp16) matrix cores
-// and O^T = V^T P^T on fp16 matrix cores: P = exp(s - m) is rounded to fp16
-// for the numerator; the denominator sums the fp32 P.  Without a P~
+// and O^T = V^T P^T on fp16 matrix cores: P = exp(s - m) is rounded to fp16,
+// and the denominator sums that same fp16 P on the matrix core (an MFMA
+// against an all-ones operand), so numerator and denominator carry the same
+// rounding.  Without a P~
 // quantization the tile size only changes rounding, so this mode uses
 // 64-key tiles (kF16KvTile), which keeps a 2-stage ring of 32 KiB tiles at
 // two workgroups per CU.
@@ -58,12 +60,6 @@ __device__ __forceinline__ float xlane_max4(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float xlane_sum4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
   v2f f = {x, y};
@@ -83,26 +79,25 @@ template <int D>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* src, int wave, int lane) {
   constexpr int NL = f16_img_bytes(D) / 1024;
   static_assert(NL % kWaves == 0, "whole rows per wave");
+  // uniform base + 32-bit lane offset: one address register for every load
+  const uint32_t lofs = static_cast<uint32_t>(wave * 1024 + lane * 16);
 #pragma unroll
-  for (int i = 0; i < NL / kWaves; ++i) {
-    const int row = wave + i * kWaves;
-    __builtin_amdgcn_global_load_lds(src + row * 1024 + lane * 16, stage + row * 1024, 16, 0, 0);
-  }
+  for (int i = 0; i < NL / kWaves; ++i)
+    __builtin_amdgcn_global_load_lds(src + lofs + i * kWaves * 1024, stage + (wave + i * kWaves) * 1024, 16, 0, 0);
 }
 
 template <int D>
 struct F16State {
   v4f oacc[kQT][D / 16];
+  v4f lacc[kQT];    // row sums of P (every element of a column holds its query's sum)
   float m[kQT];     // running row max (raw score units)
-  float lsum[kQT];  // per-lane partial sums of p
 };
 
-// P of one query tile: row max, history factor, fp16 P operands; rescales
-// the history when any row's max moved.
+// P of one query tile: row max, history factor alpha (returned), fp16 P
+// operands and the running denominator.
 template <int D>
-__device__ __forceinline__ void softmax_tile(F16State<D>& w, int u, const v4f (&s)[kSub], float sl2,
-                                             uint4 (&pop)[kGrp]) {
-  constexpr int NT = D / 16;
+__device__ __forceinline__ float softmax_tile(F16State<D>& w, int u, const v4f (&s)[kSub], float sl2,
+                                              uint4 (&pop)[kGrp]) {
   float bmax = s[0][0];
 #pragma unroll
   for (int i = 1; i + 1 < 4 * kSub; i += 2)
@@ -112,22 +107,24 @@ __device__ __forceinline__ void softmax_tile(F16State<D>& w, int u, const v4f (&
   const float alpha = __builtin_amdgcn_exp2f((w.m[u] - mnew) * sl2);  // 0 on the first tile
   w.m[u] = mnew;
   const float ofs = mnew * sl2;
-  float psum = 0.0f;
 #pragma unroll
   for (int G = 0; G < kGrp; ++G) {
     float p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * G + (i >> 2)][i & 3], sl2, -ofs));
-      psum += p[i];
-    }
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * G + (i >> 2)][i & 3], sl2, -ofs));
     pop[G] = make_uint4(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
                         pack_f16x2(p[6], p[7]));
   }
-  w.lsum[u] = fmaf(w.lsum[u], alpha, psum);
+  return alpha;
+}
+
+// History rescale: skipped when alpha == 1 exactly for the whole wave.
+template <int D>
+__device__ __forceinline__ void rescale_tile(F16State<D>& w, int u, float alpha) {
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) w.oacc[u][n] *= alpha;
+    for (int n = 0; n < D / 16; ++n) w.oacc[u][n] *= alpha;
+    w.lacc[u][0] *= alpha;  // only element 0 is read at the end
   }
 }
 
@@ -141,6 +138,42 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+template <int D, int QK_F16>
+__device__ __forceinline__ void s_tile(v4f (&s)[kSub], const uint4 (&kop)[kSub][D / 32], const uint4 (&qop)[D / 32]) {
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) {
+    s[t] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) s[t] = mfma_qk<QK_F16>(kop[t][kk], qop[kk], s[t]);
+  }
+}
+
+// Keys past `lim` (relative to the tile) are excluded.
+__device__ __forceinline__ void mask_tile(v4f (&s)[kSub], int lim, int grp) {
+  asm volatile("" : "+v"(lim));  // keeps the compares inside the caller's branch
+#pragma unroll
+  for (int t = 0; t < kSub; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = (t >> 1) * 32 + grp * 8 + (t & 1) * 4 + r;
+      s[t][r] = key > lim ? -INFINITY : s[t][r];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_tile(F16State<D>& w, int u, const uint4 (&pop)[kGrp], const uint8_t* vst,
+                                        int lane) {
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // fp16 1.0
+#pragma unroll
+  for (int G = 0; G < kGrp; ++G) w.lacc[u] = mfma_pv(ones, pop[G], w.lacc[u]);
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+    for (int G = 0; G < kGrp; ++G)
+      w.oacc[u][n] = mfma_pv(*reinterpret_cast<const uint4*>(vst + (n * kGrp + G) * 1024 + lane * 16),
+                             pop[G], w.oacc[u][n]);
+}
+
 // One KV tile (keys j0 .. j0+kT-1) for the wave's two query tiles.
 template <int D, int QK_F16>
 __device__ __forceinline__ void compute_tile(F16State<D>& w, const uint8_t* st, const uint4 (&qop)[kQT][D / 32],
@@ -149,50 +182,34 @@ __device__ __forceinline__ void compute_tile(F16State<D>& w, const uint8_t* st, 
   constexpr int KK = D / 32;
   constexpr int NT = D / 16;
   const int grp = lane >> 4;
-  v4f s[kQT][kSub];
+  uint4 kop[kSub][KK];
 #pragma unroll
-  for (int t = 0; t < kSub; ++t) {
+  for (int t = 0; t < kSub; ++t)
 #pragma unroll
-    for (int u = 0; u < kQT; ++u) s[u][t] = v4f{0, 0, 0, 0};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint4 kop = *reinterpret_cast<const uint4*>(st + (t * KK + kk) * 1024 + lane * 16);
-#pragma unroll
-      for (int u = 0; u < kQT; ++u) s[u][t] = mfma_qk<QK_F16>(kop, qop[u][kk], s[u][t]);
-    }
-  }
-  if (mask) {
-#pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-      int lim = klim[u] - j0;
-      asm volatile("" : "+v"(lim));  // keeps the compares inside this branch
-#pragma unroll
-      for (int t = 0; t < kSub; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = (t >> 1) * 32 + grp * 8 + (t & 1) * 4 + r;
-          s[u][t][r] = key > lim ? -INFINITY : s[u][t][r];
-        }
-    }
-  }
-  uint4 pop0[kGrp], pop1[kGrp];
-  softmax_tile<D>(w, 0, s[0], sl2, pop0);
-  // O^T of query tile 0 on the matrix core while P of tile 1 is formed
+    for (int kk = 0; kk < KK; ++kk)
+      kop[t][kk] = *reinterpret_cast<const uint4*>(st + (t * KK + kk) * 1024 + lane * 16);
   const uint8_t* vst = st + f16_img_vc(D);
+  v4f s0[kSub], s1[kSub];
+  uint4 pop0[kGrp], pop1[kGrp];
+  s_tile<D, QK_F16>(s0, kop, qop[0]);
+  if (mask) mask_tile(s0, klim[0] - j0, grp);
+  // S^T of query tile 1 on the matrix core while P of tile 0 is formed
+  s_tile<D, QK_F16>(s1, kop, qop[1]);
+  float alpha0 = softmax_tile<D>(w, 0, s0, sl2, pop0);
+  interleave_mfma_valu<kSub * KK, 6>();
+  // keep P of tile 0 here, beside the S^T products of tile 1
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int G = 0; G < kGrp; ++G)
-      w.oacc[0][n] = mfma_pv(*reinterpret_cast<const uint4*>(vst + (n * kGrp + G) * 1024 + lane * 16),
-                             pop0[G], w.oacc[0][n]);
-  softmax_tile<D>(w, 1, s[1], sl2, pop1);
-  interleave_mfma_valu<NT * kGrp, 4>();
-#pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int G = 0; G < kGrp; ++G)
-      w.oacc[1][n] = mfma_pv(*reinterpret_cast<const uint4*>(vst + (n * kGrp + G) * 1024 + lane * 16),
-                             pop1[G], w.oacc[1][n]);
+  for (int G = 0; G < kGrp; ++G)
+    asm volatile("" : "+v"(pop0[G].x), "+v"(pop0[G].y), "+v"(pop0[G].z), "+v"(pop0[G].w));
+  asm volatile("" : "+v"(alpha0));
+  rescale_tile<D>(w, 0, alpha0);
+  if (mask) mask_tile(s1, klim[1] - j0, grp);
+  // O^T of query tile 0 while P of tile 1 is formed
+  pv_tile<D>(w, 0, pop0, vst, lane);
+  const float alpha1 = softmax_tile<D>(w, 1, s1, sl2, pop1);
+  interleave_mfma_valu<(NT + 1) * kGrp, 6>();
+  rescale_tile<D>(w, 1, alpha1);
+  pv_tile<D>(w, 1, pop1, vst, lane);
 }
 
 template <int D, int QK_F16, int CAUSAL>
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f16_kernel(F16AttnArgs a, fl
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
     w.m[u] = -INFINITY;
-    w.lsum[u] = 0.0f;
+    w.lacc[u] = v4f{0, 0, 0, 0};
 #pragma unroll
     for (int n = 0; n < NT; ++n) w.oacc[u][n] = v4f{0, 0, 0, 0};
   }
@@ -281,13 +298,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f16_kernel(F16AttnArgs a, fl
   // matrix-core instruction is moved into that divergent region (an MFMA with
   // part of EXEC disabled drops operands other lanes' results depend on).
 #pragma unroll
-  for (int u = 0; u < kQT; ++u)
+  for (int u = 0; u < kQT; ++u) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[u][n]));
+    asm volatile("" : "+v"(w.lacc[u]));
+  }
 
 #pragma unroll
   for (int u = 0; u < kQT; ++u) {
-    const float inv = 1.0f / xlane_sum4(w.lsum[u]);
+    const float inv = 1.0f / w.lacc[u][0];
     if (qrow[u] < a.Sq) {
       float* orow = a.o + (bh * a.Sq + qrow[u]) * D;
 #pragma unroll
