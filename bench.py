@@ -11,7 +11,8 @@ value      = attention TFLOP/s of the whole step, 4*B*H*Sq*Skv*D / time
              (halved when causal);
 roofline   = the fused attention kernel alone, timed with stream events,
              against the 10.1 PFLOP/s dense FP4 MFMA peak;
-alongside  = the FP16, OCP and UOS modes on the same inputs;
+alongside  = the UOS+EFQ (exp-free P~), FP16, OCP and UOS modes on the same
+             inputs;
 quantizer  = the standalone quantize / dequantize of the 8192 x 28672 bf16
              roundtrip tensor, GB/s against 8 TB/s HBM;
 cpu_baseline = the binary64 oracle on a bounded row sample, host cores.
@@ -176,7 +177,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit14", choices=["dit14", "dit13", "llm_prefill"])
-    ap.add_argument("--modes", default="uos_pnq,fp16,ocp,uos",
+    ap.add_argument("--modes", default="uos_pnq,uos_efq,fp16,ocp,uos",
                     help="first mode is the headline; the rest run alongside")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-attention", action="store_true",

@@ -64,7 +64,14 @@ enum mx_status {
 
 enum mx_dtype { MX_F32 = 0, MX_BF16 = 1 };
 enum mxq_mode { MXQ_OCP = 0, MXQ_UOS = 1 };
-enum mxattn_mode { MXATTN_FP16 = 0, MXATTN_OCP = 1, MXATTN_UOS = 2, MXATTN_UOS_PNQ = 3 };
+enum mxattn_mode {
+  MXATTN_FP16 = 0,
+  MXATTN_OCP = 1,
+  MXATTN_UOS = 2,
+  MXATTN_UOS_PNQ = 3,
+  /* UOS operands; P~ by the exp-free EFQ rule (see mxattn_fwd); PNQ denominator */
+  MXATTN_UOS_EFQ = 4
+};
 
 /* Human-readable text of a status code (static storage). */
 const char *mx_strerror(int status);
@@ -153,7 +160,14 @@ int mxattn_kv_tile(int D, int mode);
  *  o [B][Hq][Sq][D] fp32 out.
  *  workspace: >= mxattn_workspace_bytes(...) bytes, 256-byte aligned,
  *  overwritten.  Modes: MXATTN_FP16 (16-bit operands, no quantization),
- *  MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ.
+ *  MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ, MXATTN_UOS_EFQ.  MXATTN_UOS_EFQ
+ *  ("EFQ-Softmax", abstract; constants are a reading, not the page's):
+ *  UOS operands and PNQ denominator, with each P~ block generated without
+ *  exp: z = log2 of the unnormalized probability, block exponent e = the
+ *  smallest e >= -127 with z_max - e < (7.5 - beta)/2 - 2^-10, code =
+ *  clamp(round-half-even(2 (z - e) + beta), 0, 7), beta = 1.8678023 (the
+ *  least-squares fit of this rule to the E2M1 rounding boundaries of
+ *  codes 2..7).
  * In the MX modes the call first quantizes Q and K (blocks along D) and V
  * (blocks along keys) into the workspace, K~ and V~ as KV tile images in
  * matrix-core operand order, then runs the fused attention kernel.  In FP16 mode, V (and, for fp32 inputs, Q and K) is

@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libmxattn.so")
 
 MX_F32, MX_BF16 = 0, 1
 MXQ_OCP, MXQ_UOS = 0, 1
-MXATTN_FP16, MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ = 0, 1, 2, 3
-MODES = {"fp16": MXATTN_FP16, "ocp": MXATTN_OCP, "uos": MXATTN_UOS, "uos_pnq": MXATTN_UOS_PNQ}
+MXATTN_FP16, MXATTN_OCP, MXATTN_UOS, MXATTN_UOS_PNQ, MXATTN_UOS_EFQ = 0, 1, 2, 3, 4
+MODES = {"fp16": MXATTN_FP16, "ocp": MXATTN_OCP, "uos": MXATTN_UOS, "uos_pnq": MXATTN_UOS_PNQ,
+         "uos_efq": MXATTN_UOS_EFQ}
 RULES = {"ocp": MXQ_OCP, "uos": MXQ_UOS}
 
 # Symbols the header declares; the CPU tests check the library exports them.

@@ -96,6 +96,25 @@ __device__ __forceinline__ float p_block_exp(float x) {
   return fmaxf(__builtin_floorf(x - kOfs), -127.0f);
 }
 
+// Exp-free P~ (UOS+EFQ mode; "EFQ-Softmax", abstract: exponent-only block
+// scale from the local maximum, scores mapped to a residual domain,
+// nonnegative E2M1 codes by one affine rule).  The page prints no constants;
+// the reading implemented: on the log2 residual r = z - e of a block,
+// code = clamp(round-half-even(2 r + beta), 0, 7) -- two codes per binade,
+// as the E2M1 grid has above 1 -- with beta the least-squares fit of the
+// rule's boundaries (c + 1/2 - beta)/2 to the E2M1 rounding boundaries
+// log2((mag_c + mag_c+1)/2), c = 2..6:
+//   beta = mean_c (c + 1/2 - 2 log2((mag_c + mag_c+1)/2)) = 1.8678023...
+// and e the smallest exponent >= -127 with z_max - e < rho,
+//   rho = (7.5 - beta)/2 - 2^-10,
+// so that the block maximum stays below code 8 even after fp32 rounding.
+constexpr float kEfqBeta = 1.8678023484890818f;
+constexpr float kEfqRho = 2.8151222632554591f;
+
+__device__ __forceinline__ float efq_block_exp(float x) {
+  return fmaxf(__builtin_floorf(x - kEfqRho) + 1.0f, -127.0f);
+}
+
 // Per-wave softmax state and accumulators for kQT query tiles.
 template <int D>
 struct WaveState {
@@ -162,6 +181,8 @@ struct TileStats {
   float alpha, kofs;
   int X;
 };
+// PNQ: 0 = denominator from the unquantized p (OCP, UOS); 1 = PNQ; 2 = PNQ
+// with the exp-free EFQ codes.
 template <int D, int UOS, int PNQ>
 __device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
   constexpr int NT = D / 16;
@@ -182,9 +203,11 @@ __device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4
   // scale of this lane's P~ block (the block holding the row maximum gets
   // x = 0 exactly); in the scaled domain
   // log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
-  const float e = p_block_exp<UOS>((bmax - delta) * sl2);
+  const float x = (bmax - delta) * sl2;
+  const float e = PNQ == 2 ? efq_block_exp(x) : p_block_exp<UOS>(x);
   r.X = static_cast<int>(e) + 127;
-  r.kofs = fmaf(delta, sl2, e);
+  // EFQ: 2 r + beta = d * 2c + (beta - 2 (delta c + e)); else the exp2 offset
+  r.kofs = PNQ == 2 ? kEfqBeta - 2.0f * fmaf(delta, sl2, e) : fmaf(delta, sl2, e);
   // history rescale: alpha == 1 exactly leaves the history unchanged, so
   // the multiplies are skipped when that holds for the whole wave
   if (__builtin_amdgcn_ballot_w64(r.alpha != 1.0f) != 0) {
@@ -199,10 +222,33 @@ __device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4
 
 // P~ block of this lane: v = exp2(d*c - kofs) rounded to E2M1 (nearest
 // even, saturating), packed in MFMA operand order; vsum = sum of v.
+// EFQ (PNQ == 2): code = rne(d * 2c + kofs) by v_cvt_pk_u8_f32 (round half
+// to even, saturating at 0; below 7.5 by the choice of e), even and odd
+// elements into the bytes of two words, one shift-or per 8 codes.
 template <int PNQ>
 __device__ __forceinline__ uint4 p_tile(const v4f (&s)[kSub], float sl2, float kofs, float& vsum) {
   uint32_t pw[4];
   vsum = 0.0f;
+  if (PNQ == 2) {
+    const float c2 = 2.0f * sl2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = fmaf(s[2 * q + (i >> 2)][i & 3], c2, kofs);
+      // all four bytes of each word are written, so the chains may start anywhere
+      uint32_t a = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 0, __float_as_uint(t[0]));
+      a = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 1, a);
+      a = __builtin_amdgcn_cvt_pk_u8_f32(t[4], 2, a);
+      a = __builtin_amdgcn_cvt_pk_u8_f32(t[6], 3, a);
+      uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 0, __float_as_uint(t[1]));
+      b = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 1, b);
+      b = __builtin_amdgcn_cvt_pk_u8_f32(t[5], 2, b);
+      b = __builtin_amdgcn_cvt_pk_u8_f32(t[7], 3, b);
+      pw[q] = a | (b << 4);
+    }
+    return make_uint4(pw[0], pw[1], pw[2], pw[3]);
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {  // dword q holds key subtiles 2q and 2q+1
     float v[8];
@@ -477,7 +523,8 @@ hipError_t pick_mode(const MxAttnArgs& a, hipStream_t s) {
   switch (a.mode) {
     case 1: return pick_causal<D, 0, 0>(a, s);
     case 2: return pick_causal<D, 1, 0>(a, s);
-    default: return pick_causal<D, 1, 1>(a, s);
+    case 3: return pick_causal<D, 1, 1>(a, s);
+    default: return pick_causal<D, 1, 2>(a, s);
   }
 }
 

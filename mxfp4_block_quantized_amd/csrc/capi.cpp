@@ -27,7 +27,7 @@ struct Layout {
 int check_attn_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                      int causal, int mode) {
   if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
-  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_PNQ) return MX_ERR_ARG;
+  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_EFQ) return MX_ERR_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return MX_ERR_ARG;
   if (causal != 0 && causal != 1) return MX_ERR_ARG;
   if (Hq % Hkv != 0) return MX_ERR_ARG;
@@ -244,7 +244,7 @@ int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int 
 }
 
 int mxattn_kv_tile(int D, int mode) {
-  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_PNQ) return MX_ERR_ARG;
+  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_EFQ) return MX_ERR_ARG;
   if (D != 64 && D != 128) return MX_ERR_UNSUPPORTED;
   return mode == MXATTN_FP16 ? mxk::kF16KvTile : mxk::kKvTile;
 }

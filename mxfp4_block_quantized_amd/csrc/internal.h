@@ -74,7 +74,7 @@ struct MxAttnArgs {
   int B, Hq, Hkv, Sq, Skv, D;
   int64_t skv_ld;
   int causal;
-  int mode;  // 1 OCP, 2 UOS, 3 UOS+PNQ
+  int mode;  // 1 OCP, 2 UOS, 3 UOS+PNQ, 4 UOS+EFQ
 };
 hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 

@@ -32,7 +32,7 @@ _LIB = os.path.join(_HERE, "_liboracle.so")
 
 F32, BF16 = 0, 1
 RULE_OCP, RULE_UOS = 0, 1
-MODE_FP16, MODE_OCP, MODE_UOS, MODE_UOS_PNQ = 0, 1, 2, 3
+MODE_FP16, MODE_OCP, MODE_UOS, MODE_UOS_PNQ, MODE_UOS_EFQ = 0, 1, 2, 3, 4
 BLOCK = 32
 
 _lib = None
@@ -75,6 +75,14 @@ def _load():
     lib.oracle_attn_rows.restype = ci
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ci
+    lib.oracle_efq_beta.argtypes = []
+    lib.oracle_efq_beta.restype = ctypes.c_double
+    lib.oracle_efq_rho.argtypes = []
+    lib.oracle_efq_rho.restype = ctypes.c_double
+    lib.oracle_efq_exponent.argtypes = [ctypes.c_double]
+    lib.oracle_efq_exponent.restype = ci
+    lib.oracle_efq_code.argtypes = [ctypes.c_double]
+    lib.oracle_efq_code.restype = ci
     _lib = lib
     return lib
 
@@ -102,6 +110,26 @@ def threads() -> int:
 def scale_exponent(amax: float, rule: int) -> int:
     """Scale exponent e of a block whose largest magnitude is ``amax``."""
     return _load().oracle_scale_exponent(float(amax), int(rule))
+
+
+def efq_beta() -> float:
+    """Offset of the EFQ affine code rule (least-squares fit, see mxoracle.c)."""
+    return _load().oracle_efq_beta()
+
+
+def efq_rho() -> float:
+    """Largest residual the EFQ block maximum may take."""
+    return _load().oracle_efq_rho()
+
+
+def efq_exponent(zmax: float) -> int:
+    """EFQ block exponent from the block's largest log2 probability."""
+    return _load().oracle_efq_exponent(float(zmax))
+
+
+def efq_code(r: float) -> int:
+    """EFQ code (0..7) of a log2 residual r = z - e_b."""
+    return _load().oracle_efq_code(float(r))
 
 
 def round_e2m1(v: float) -> int:

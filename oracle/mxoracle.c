@@ -39,6 +39,16 @@
  *    ascending order; P~ blocks are 32 keys aligned at key 0; in the OCP and
  *    UOS modes the row sum uses the unquantized p, in UOS+PNQ the quantized
  *    p~.  Query head h reads KV head h / (Hq / Hkv).  Causal: key j <= i.
+ *  - UOS+EFQ mode ([EFQ] abstract: exponent-only block scale from the local
+ *    maximum, scores mapped to a residual domain, nonnegative E2M1 codes by
+ *    one affine rule; the same P~ in numerator and denominator).  The rule's
+ *    constants are not on the pages; reading: in log2 units
+ *    z = (s - m) * log2(e), e_b = the smallest exponent >= -127 with
+ *    z_max - e_b < rho, r = z - e_b, code = clamp(rne(2 r + beta), 0, 7),
+ *    p~ = E2M1(code) * 2^e_b.  "2 codes per binade" matches the E2M1 grid
+ *    above 1; beta is the least-squares fit of the five rounding boundaries
+ *    of codes 2..7 (log2 of the midpoints 1.25 .. 5); rho = (7.5 - beta)/2
+ *    - 2^-10 keeps the block maximum below code 8.  Q, K, V use UOS.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +65,7 @@
 #define ORC_MODE_OCP 1
 #define ORC_MODE_UOS 2
 #define ORC_MODE_UOS_PNQ 3
+#define ORC_MODE_UOS_EFQ 4
 
 #define ORC_BLOCK 32
 
@@ -74,6 +85,50 @@ static double load_elem(const void *base, int dtype, int64_t idx)
 
 /* 2^e exactly (e well inside binary64's normal range here). */
 static double pow2i(int e) { return ldexp(1.0, e); }
+
+/* EFQ affine-rule offset beta: least-squares fit of round(2 r + beta) to the
+ * E2M1 rounding boundaries between codes c and c+1 (c = 2..6), which lie at
+ * r = log2((mag[c] + mag[c+1]) / 2); the rule puts them at (c + 1/2 - beta)/2. */
+double oracle_efq_beta(void)
+{
+    double sum = 0.0;
+    for (int c = 2; c <= 6; ++c)
+        sum += (double)c + 0.5 - 2.0 * log2(0.5 * (E2M1_MAG[c] + E2M1_MAG[c + 1]));
+    return sum / 5.0;
+}
+
+/* Largest residual the block maximum may take: 2 r + beta stays below 7.5
+ * (code 7 at most), with a 2^-10 margin. */
+double oracle_efq_rho(void)
+{
+    return 0.5 * (7.5 - oracle_efq_beta()) - ldexp(1.0, -10);
+}
+
+/* EFQ block exponent: the smallest e in [-127, 127] with zmax - e < rho
+ * (zmax = log2 of the block's largest unnormalized probability; -inf for a
+ * block without a visible key gives -127). */
+int oracle_efq_exponent(double zmax)
+{
+    const double rho = oracle_efq_rho();
+    for (int e = -127; e < 127; ++e)
+        if (zmax - (double)e < rho)
+            return e;
+    return 127;
+}
+
+/* EFQ code of one residual r = z - e_b: round half to even of 2 r + beta,
+ * clamped to [0, 7]. */
+int oracle_efq_code(double r)
+{
+    if (r == -INFINITY)
+        return 0;
+    double c = nearbyint(2.0 * r + oracle_efq_beta());
+    if (c < 0.0)
+        c = 0.0;
+    if (c > 7.0)
+        c = 7.0;
+    return (int)c;
+}
 
 /* Scale exponent of one block, by its definition: the smallest e >= -127
  * whose scaled block maximum lies inside the rule's range.
@@ -245,13 +300,14 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1)
         return -1;
     if (Hq % Hkv != 0 || D % ORC_BLOCK != 0 || bc < ORC_BLOCK ||
-        bc % ORC_BLOCK != 0 || mode < 0 || mode > 3)
+        bc % ORC_BLOCK != 0 || mode < 0 || mode > 4)
         return -1;
     if (causal && Sq != Skv)
         return -1;
     const int quantized = (mode != ORC_MODE_FP16);
     const int rule = (mode == ORC_MODE_OCP) ? ORC_RULE_OCP : ORC_RULE_UOS;
-    const int pnq = (mode == ORC_MODE_UOS_PNQ);
+    const int efq = (mode == ORC_MODE_UOS_EFQ);
+    const int pnq = (mode == ORC_MODE_UOS_PNQ) || efq;
     const int group = Hq / Hkv;
     const int64_t skv_pad = ((int64_t)Skv + ORC_BLOCK - 1) / ORC_BLOCK * ORC_BLOCK;
     const int64_t ntiles = ((int64_t)Skv + bc - 1) / bc;
@@ -363,7 +419,23 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
                     if (quantized) {
                         for (int64_t b0 = 0; b0 < tlen; b0 += ORC_BLOCK) {
                             uint8_t code[ORC_BLOCK];
-                            uint8_t sb = quantize_block(p + b0, rule, code);
+                            uint8_t sb;
+                            if (efq) {
+                                /* exp-free: codes from the log2 residuals */
+                                double z[ORC_BLOCK], zmax = -INFINITY;
+                                for (int ii = 0; ii < ORC_BLOCK; ++ii) {
+                                    int64_t jj = b0 + ii;
+                                    z[ii] = (jj < nvalid) ? (s[jj] - mnew) / log(2.0) : -INFINITY;
+                                    if (z[ii] > zmax)
+                                        zmax = z[ii];
+                                }
+                                int eb = oracle_efq_exponent(zmax);
+                                for (int ii = 0; ii < ORC_BLOCK; ++ii)
+                                    code[ii] = (uint8_t)oracle_efq_code(z[ii] - (double)eb);
+                                sb = (uint8_t)(eb + 127);
+                            } else {
+                                sb = quantize_block(p + b0, rule, code);
+                            }
                             for (int ii = 0; ii < ORC_BLOCK; ++ii)
                                 pt[b0 + ii] = dequant_code(code[ii], sb);
                             if (pc && ps) {

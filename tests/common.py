@@ -16,9 +16,9 @@ import mxsynth  # noqa: E402
 import oracle  # noqa: E402
 
 MODE_IDS = {"fp16": oracle.MODE_FP16, "ocp": oracle.MODE_OCP, "uos": oracle.MODE_UOS,
-            "uos_pnq": oracle.MODE_UOS_PNQ}
+            "uos_pnq": oracle.MODE_UOS_PNQ, "uos_efq": oracle.MODE_UOS_EFQ}
 RULE_IDS = {"ocp": oracle.RULE_OCP, "uos": oracle.RULE_UOS}
-RULE_OF_MODE = {"ocp": "ocp", "uos": "uos", "uos_pnq": "uos"}
+RULE_OF_MODE = {"ocp": "ocp", "uos": "uos", "uos_pnq": "uos", "uos_efq": "uos"}
 
 # Output tolerance of the attention parity tests (O is O(1)).
 MAX_ABS = 2e-3

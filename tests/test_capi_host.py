@@ -63,7 +63,7 @@ def test_attention_rejects_bad_args():
     assert fwd(D=96) == -2
     assert fwd(Hq=3, Hkv=2) == -1
     assert fwd(causal=1, Skv=65) == -2
-    assert fwd(mode=4) == -1
+    assert fwd(mode=5) == -1
     assert fwd(dtype=2) == -1
     assert fwd(Sq=0) == -1
     assert fwd(q=None) == -1

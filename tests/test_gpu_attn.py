@@ -16,8 +16,8 @@ from common import (FLIP_MAX, MAX_ABS, MEAN_ABS, MODE_IDS, RULE_IDS, RULE_OF_MOD
 
 pytestmark = pytest.mark.gpu
 
-ALL_MODES = ["fp16", "ocp", "uos", "uos_pnq"]
-MX_MODES = ["ocp", "uos", "uos_pnq"]
+ALL_MODES = ["fp16", "ocp", "uos", "uos_pnq", "uos_efq"]
+MX_MODES = ["ocp", "uos", "uos_pnq", "uos_efq"]
 
 
 def check_workspace(mx, ws, q, k, v, mode):
@@ -113,7 +113,7 @@ def test_d64_bf16(mode):
 
 
 @pytest.mark.parametrize("shape", [(1, 1), (5, 1), (1, 1000), (33, 33), (129, 129)])
-@pytest.mark.parametrize("mode", ["fp16", "uos_pnq", "ocp"])
+@pytest.mark.parametrize("mode", ["fp16", "uos_pnq", "ocp", "uos_efq"])
 def test_edge_lengths(shape, mode):
     Sq, Skv = shape
     q, k, v = bf16_qkv(14, 1, 2, 2, Sq, Skv, 128)
@@ -136,17 +136,17 @@ def test_llm_like_small(mode):
 
 
 def test_v_ones_pnq_gives_one():
-    """Under PNQ numerator and denominator sum the same P~, so O = 1 up to
-    fp32 accumulation rounding; the non-PNQ modes divide sum(P~) by sum(P)
-    and miss 1 by far more."""
+    """Under PNQ (and EFQ, which shares its denominator) numerator and
+    denominator sum the same P~, so O = 1 up to fp32 accumulation rounding;
+    the non-PNQ modes divide sum(P~) by sum(P) and miss 1 by far more."""
     torch, mx = gpu()
     q, k, v = bf16_qkv(15, 1, 2, 2, 190, 190, 128, scale=2.0)
     v[:] = mxsynth.f32_to_bf16_bits(np.ones(1, np.float32))[0]
     qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
     dev = {m: (mx.attn_fwd(qt, kt, vt, mode=m) - 1.0).abs().max().item()
-           for m in ("uos_pnq", "uos", "ocp")}
+           for m in ("uos_pnq", "uos_efq", "uos", "ocp")}
     print("max |O - 1|:", dev)
-    assert dev["uos_pnq"] <= 1e-6
+    assert dev["uos_pnq"] <= 1e-6 and dev["uos_efq"] <= 1e-6
     assert dev["uos"] > 1e-3 and dev["ocp"] > 1e-3
 
 
