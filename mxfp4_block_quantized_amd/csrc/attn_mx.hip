@@ -1,4 +1,5 @@
-// Fused MXFP4 attention forward for gfx950 (OCP, UOS and UOS+PNQ modes).
+// Fused MXFP4 attention forward for gfx950 (OCP, UOS, UOS+PNQ and UOS+EFQ
+// modes).
 //
 // What it computes ("MXAttention: Data-Free Optimal Scaling and
 // Pre-Normalization Quantization for MXFP4 Attention", abstract;
@@ -34,6 +35,9 @@
 // v_cvt_scalef32_pk_fp4_f32 (round to nearest even,
 // saturating).  This keeps blocks whose probabilities lie below fp32's
 // normal range exact in the same way the binary64 definition treats them.
+// The UOS+EFQ mode skips the exp: the code of each score is an affine
+// function of its log2 residual to the block's exponent, rounded and
+// clamped by v_cvt_pk_u8_f32 (efq_block_exp, tile_stats, p_tile).
 #include "internal.h"
 
 namespace mxk {
