@@ -15,6 +15,9 @@ alongside  = the UOS+EFQ (exp-free P~), FP16, OCP and UOS modes on the same
              inputs;
 quantizer  = the standalone quantize / dequantize of the 8192 x 28672 bf16
              roundtrip tensor, GB/s against 8 TB/s HBM;
+gemm       = the W4A4 product (mxgemm) on the DiT feed-forward up-projection
+             (32760 tokens x 5120 -> 13824, UOS operands, bf16 output), alone
+             and with the activation quantization, against 10.1 PFLOP/s;
 cpu_baseline = the binary64 oracle on a bounded row sample, host cores.
 """
 from __future__ import annotations
@@ -154,6 +157,44 @@ def bench_quantizer(torch, mx, reps=20):
     return res
 
 
+def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
+    import mxsynth
+    g = mxsynth.GEMM_CONFIGS[name]
+    M, N, K = g["M"], g["N"], g["K"]
+    log(f"[bench] gemm: generating {name} operands")
+    x, w = mxsynth.make_gemm_inputs(name)
+    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
+    xt, wt = to(x), to(w)
+    del x, w
+    wc, ws = mx.quantize(wt, "uos")   # the weight is quantized once, ahead of time
+    xc = torch.empty(M * K // 2, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(M * K // 32, dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * M * N * K
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    mx.quantize(xt, "uos", xc, xs)
+    gemm_ms = timed(lambda: mx.gemm(xc, xs, wc, ws, M, N, K, out=y))
+    lin_ms = timed(lambda: (mx.quantize(xt, "uos", xc, xs), mx.gemm(xc, xs, wc, ws, M, N, K, out=y)))
+    return {"workload": f"{name}: x [{M}, {K}] bf16 (N(0,1), 1% channels x20) times UOS-MXFP4 "
+                        f"weight [{N}, {K}] (Student-t(3)*0.02, 0.1% x50), bf16 output",
+            "flops": flops,
+            "gemm_ms": gemm_ms, "gemm_tflops": flops / gemm_ms / 1e9,
+            "gemm_frac_fp4_peak": flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS,
+            "linear_w4a4_ms": lin_ms, "linear_w4a4_tflops": flops / lin_ms / 1e9}
+
+
 def cpu_baseline(q, k, v, c, name, rows_per_head=2048):
     """The oracle (as it stands) on a bounded, seeded sample of query rows of
     every head (about 10-20 s of CPU work at the DiT14 shape)."""
@@ -180,6 +221,7 @@ def main():
     ap.add_argument("--modes", default="uos_pnq,uos_efq,fp16,ocp,uos",
                     help="first mode is the headline; the rest run alongside")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
                     help="only the standalone quantizer (for profiling it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -269,6 +311,9 @@ def main():
     if not args.no_quantizer:
         out["quantizer"] = bench_quantizer(torch, mx)
         log(f"[bench] quantizer: {out['quantizer']}")
+    if not args.no_gemm:
+        out["gemm"] = bench_gemm(torch, mx)
+        log(f"[bench] gemm: {out['gemm']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, c, args.workload)

@@ -214,6 +214,33 @@ int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
                     const int32_t *row_slot, uint8_t *p_codes,
                     uint8_t *p_scales, void *stream);
 
+/*
+ * W4A4 product of two MXFP4 operands ("MXCode: Vector Quantization for
+ * MX-Native Inference at Scale", abstract: MX-native W4A4 operands; the
+ * 32-element blocks and E8M0 scales of the OCP MX format):
+ *
+ *   y[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k],   accumulated in fp32.
+ *
+ *   a_codes  [M][K/2], a_scales [M][K/32]: a [M][K] exactly as mxq_quantize
+ *            writes a row-major tensor (blocks of 32 along K, element 2j in
+ *            the low nibble of byte j, one E8M0 byte per block).  For a
+ *            linear layer: the activations, one row per token.
+ *   b_codes  [N][K/2], b_scales [N][K/32]: likewise b [N][K] (the weight,
+ *            one row per output feature).
+ *   y        [M][N] row-major: fp32 (out_dtype MX_F32) or bf16 (MX_BF16,
+ *            rounded to nearest even).
+ *
+ * M, N >= 1; K >= 128 with K % 128 == 0, else MX_ERR_UNSUPPORTED (the
+ * matrix instruction consumes 128 K-elements, four blocks, at a time).
+ * M, N < 2^31.  All pointers are device memory owned by the caller; codes
+ * and y must be 16-byte aligned and scales 4-byte aligned (MX_ERR_ALIGN);
+ * a NULL pointer or bad out_dtype gives MX_ERR_ARG.  Asynchronous on
+ * stream; allocates nothing; y must not overlap the operands.
+ */
+int mxgemm(const uint8_t *a_codes, const uint8_t *a_scales,
+           const uint8_t *b_codes, const uint8_t *b_scales, int64_t M,
+           int64_t N, int64_t K, int out_dtype, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxattn.so")
 
-SOURCES = ["capi.cpp", "quant.hip", "attn_mx.hip", "attn_f16.hip"]
+SOURCES = ["capi.cpp", "quant.hip", "attn_mx.hip", "attn_f16.hip", "gemm_mx.hip"]
 HEADERS = ["internal.h"]
 
 HIPCC_FLAGS = [

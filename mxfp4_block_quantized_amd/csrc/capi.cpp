@@ -1,4 +1,5 @@
-// C ABI of the MXFP4 quantizer and MXFP4 attention (see include/mxattn.h):
+// C ABI of the MXFP4 quantizer, MXFP4 attention and the W4A4 product (see
+// include/mxattn.h):
 // argument validation (always before any HIP call), workspace layout and
 // dispatch to the HIP launchers.
 #include "mxattn.h"
@@ -290,3 +291,20 @@ int mxattn_fwd_dump(const void* q, const void* k, const void* v, int dtype, int 
 }
 
 }  // extern "C"
+
+int mxgemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int out_dtype, void* y,
+           void* stream) {
+  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+  if (M < 1 || N < 1 || K < 1) return MX_ERR_ARG;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return MX_ERR_ARG;
+  if (K % 128 != 0) return MX_ERR_UNSUPPORTED;
+  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
+  // workgroup count (256 x 256 output tiles) must fit a 1-D grid
+  if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(y, 16) ||
+      !aligned(a_scales, 4) || !aligned(b_scales, 4))
+    return MX_ERR_ALIGN;
+  return to_status(mxk::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K,
+                                       out_dtype == MX_BF16, y, as_stream(stream)));
+}

@@ -78,6 +78,13 @@ struct MxAttnArgs {
 };
 hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
+// W4A4 product y[M][N] = a[M][K] b[N][K]^T of MXFP4 operands (codes
+// [rows][K/2], E8M0 [rows][K/32]); K % 128 == 0; fp32 (out_bf16 == 0) or
+// bf16 output.
+hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
+                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, int out_bf16,
+                          void* y, hipStream_t stream);
+
 // Operands of the 16-bit attention kernel.
 struct F16AttnArgs {
   const void* q;       // [B][Hq][Sq][D], bf16 (qk_f16 == 0) or fp16

@@ -18,6 +18,7 @@ import numpy as np
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "tiny_attn", "tiny_quant",
     "roundtrip_tensor", "llm_prefill", "video_dit", "sample_rows", "CONFIGS",
+    "w4a4_operands", "GEMM_CONFIGS", "make_gemm_inputs",
 ]
 
 
@@ -172,3 +173,44 @@ def make_attn_inputs(name: str):
     if name == "llm_prefill":
         return llm_prefill(c["seed"], c["B"], c["Hq"], c["Hkv"], c["S"], c["D"])
     return video_dit(c["seed"], c["Hq"], c["grid"], c["D"])
+
+
+def w4a4_operands(seed: int, M: int, N: int, K: int):
+    """Operands of a linear layer of the video DiT: activations x [M, K] (one
+    row per latent token) and weight w [N, K] (one row per output feature),
+    bf16 bits.  x is N(0, 1) with round(0.01 K) outlier channels, chosen
+    with ``rng.choice(K, n, replace=False)``, scaled by 20 (the outlier
+    recipe of the attention inputs); w is Student-t(3) * 0.02 with a
+    Bernoulli(0.001) mask of entries scaled by 50 (the roundtrip tensor's
+    recipe).  Draw order: outlier channels, x in row chunks, w in row chunks."""
+    rng = np.random.default_rng(seed)
+    ch = rng.choice(K, max(1, round(0.01 * K)), replace=False)
+    gain = np.ones(K, np.float32)
+    gain[ch] = 20.0
+    x = np.empty((M, K), np.uint16)
+    step = max(1, (1 << 23) // K)
+    for r0 in range(0, M, step):
+        r1 = min(M, r0 + step)
+        x[r0:r1] = f32_to_bf16_bits(_normal(rng, (r1 - r0, K)) * gain)
+    w = np.empty((N, K), np.uint16)
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        t = rng.standard_t(3, size=(r1 - r0, K)).astype(np.float32) * np.float32(0.02)
+        mask = rng.random(size=(r1 - r0, K), dtype=np.float32) < np.float32(0.001)
+        t[mask] *= np.float32(50.0)
+        w[r0:r1] = f32_to_bf16_bits(t)
+    return x, w
+
+
+# Linear layers of the video DiT (hidden 5120 = 40 heads x 128, feed-forward
+# 13824) over the 32760 latent tokens of the dit14 attention workload.
+GEMM_CONFIGS = {
+    "dit14_ffn_up": dict(M=32760, N=13824, K=5120, seed=6),
+    "dit14_ffn_down": dict(M=32760, N=5120, K=13824, seed=7),
+}
+
+
+def make_gemm_inputs(name: str):
+    """(x, w) for a named workload of ``GEMM_CONFIGS``."""
+    c = GEMM_CONFIGS[name]
+    return w4a4_operands(c["seed"], c["M"], c["N"], c["K"])

@@ -16,7 +16,10 @@ What each function computes, with its sources, is documented in the C file:
   "Quantization Error", section "Where the error comes from";
 * the online-softmax loop with one quantized probability operand feeding both
   numerator and denominator -- "EFQ-Softmax", abstract, and the PNQ component
-  of the MXAttention abstract.
+  of the MXAttention abstract;
+* the W4A4 product of two MXFP4 operands quantized along the contraction
+  ("MXCode", abstract: MX-native W4A4 operands), here in numpy: the
+  operands are decoded by ``dequantize`` and multiplied in binary64.
 """
 from __future__ import annotations
 
@@ -226,3 +229,48 @@ def unpack_codes(codes):
     out[..., 0::2] = codes & 0xF
     out[..., 1::2] = codes >> 4
     return out
+
+
+def gemm_q(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, rows=None,
+           n_chunk: int = 2048):
+    """W4A4 product of MXFP4 operands in binary64.
+
+    The operands are stored as ``mxq_quantize`` writes row-major tensors:
+    ``a`` [M, K] and ``b`` [N, K] with blocks of 32 along K (codes [rows,
+    K/2], E8M0 bytes [rows, K/32]).  Returns ``(y, yabs)`` with
+    y[m, n] = sum_k deq(a)[m, k] deq(b)[n, k] and yabs the same sum of
+    absolute products (the scale of any rounding bound).  ``rows`` picks a
+    subset of m (all when None).  A library matmul serves as the sum; the
+    decode is ``dequantize``."""
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    a_codes = np.asarray(a_codes, np.uint8).reshape(M, K // 2)
+    a_scales = np.asarray(a_scales, np.uint8).reshape(M, K // BLOCK)
+    b_codes = np.asarray(b_codes, np.uint8).reshape(N, K // 2)
+    b_scales = np.asarray(b_scales, np.uint8).reshape(N, K // BLOCK)
+    rows = np.arange(M) if rows is None else np.asarray(rows, np.int64)
+    A = dequantize(a_codes[rows], a_scales[rows]).reshape(rows.size, K)
+    Aabs = np.abs(A)
+    y = np.empty((rows.size, N), np.float64)
+    yabs = np.empty((rows.size, N), np.float64)
+    for n0 in range(0, N, n_chunk):
+        n1 = min(N, n0 + n_chunk)
+        Bt = dequantize(b_codes[n0:n1], b_scales[n0:n1]).reshape(n1 - n0, K).T
+        y[:, n0:n1] = A @ Bt
+        yabs[:, n0:n1] = Aabs @ np.abs(Bt)
+    return y, yabs
+
+
+def gemm(a, b, rule: int, rows=None):
+    """Quantize ``a`` [M, K] and ``b`` [N, K] along K with ``rule``, then
+    ``gemm_q``.  Returns (y, yabs, (a_codes, a_scales), (b_codes, b_scales))."""
+    a, _ = _as_input(a)
+    b, _ = _as_input(b)
+    M, K = a.shape
+    N, Kb = b.shape
+    if Kb != K:
+        raise ValueError("K mismatch")
+    qa = quantize(a, rule)
+    qb = quantize(b, rule)
+    y, yabs = gemm_q(qa[0], qa[1], qb[0], qb[1], M, N, K, rows=rows)
+    return y, yabs, qa, qb

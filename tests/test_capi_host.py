@@ -91,3 +91,20 @@ def test_workspace_and_tile_queries():
     assert off64[3] == 13312
     with pytest.raises(mx.MxError):
         mx.workspace_layout(1, 2, 2, 64, 64, 128, "bf16", "fp16")
+
+
+def test_gemm_rejects_bad_args():
+    L = mx.lib()
+    P = FAKE
+    def g(M=64, N=64, K=256, dt=0, a=P, sa=P, y=P):
+        return L.mxgemm(a, sa, P, P, M, N, K, dt, y, None)
+    assert g(K=96) == -2           # K % 128
+    assert g(K=0) == -1
+    assert g(M=0) == -1
+    assert g(N=-3) == -1
+    assert g(dt=4) == -1           # out dtype
+    assert g(a=None) == -1
+    assert g(y=None) == -1
+    assert g(M=1 << 31) == -2
+    assert g(y=ctypes.c_void_p((1 << 20) + 8)) == -5   # y not 16-byte aligned
+    assert g(sa=ctypes.c_void_p((1 << 20) + 2)) == -5  # scales not 4-byte aligned
