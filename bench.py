@@ -184,9 +184,11 @@ def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    work = mx.gemm_workspace(M, N, K)
     mx.quantize(xt, "uos", xc, xs)
-    gemm_ms = timed(lambda: mx.gemm(xc, xs, wc, ws, M, N, K, out=y))
-    lin_ms = timed(lambda: (mx.quantize(xt, "uos", xc, xs), mx.gemm(xc, xs, wc, ws, M, N, K, out=y)))
+    gemm_ms = timed(lambda: mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=work))
+    lin_ms = timed(lambda: (mx.quantize(xt, "uos", xc, xs),
+                            mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=work)))
     return {"workload": f"{name}: x [{M}, {K}] bf16 (N(0,1), 1% channels x20) times UOS-MXFP4 "
                         f"weight [{N}, {K}] (Student-t(3)*0.02, 0.1% x50), bf16 output",
             "flops": flops,

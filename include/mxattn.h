@@ -230,16 +230,24 @@ int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
  *   y        [M][N] row-major: fp32 (out_dtype MX_F32) or bf16 (MX_BF16,
  *            rounded to nearest even).
  *
- * M, N >= 1; K >= 128 with K % 128 == 0, else MX_ERR_UNSUPPORTED (the
+ *   workspace: at least mxgemm_workspace_bytes(M, N, K) bytes of device
+ *            memory, 256-byte aligned, that the call overwrites (the
+ *            operands' E8M0 bytes re-laid out for the kernel); calls that
+ *            run concurrently need separate workspaces.
+ *
+ * M, N >= 1; K >= 128 and K % 128 == 0, else MX_ERR_UNSUPPORTED (the
  * matrix instruction consumes 128 K-elements, four blocks, at a time).
  * M, N < 2^31.  All pointers are device memory owned by the caller; codes
- * and y must be 16-byte aligned and scales 4-byte aligned (MX_ERR_ALIGN);
- * a NULL pointer or bad out_dtype gives MX_ERR_ARG.  Asynchronous on
- * stream; allocates nothing; y must not overlap the operands.
+ * and y must be 16-byte aligned (MX_ERR_ALIGN); a NULL pointer or bad
+ * out_dtype gives MX_ERR_ARG; a missing or short workspace
+ * MX_ERR_WORKSPACE.  Asynchronous on stream; allocates nothing; y must not
+ * overlap the operands.  mxgemm_workspace_bytes returns 0 for bad sizes.
  */
+size_t mxgemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int mxgemm(const uint8_t *a_codes, const uint8_t *a_scales,
            const uint8_t *b_codes, const uint8_t *b_scales, int64_t M,
-           int64_t N, int64_t K, int out_dtype, void *y, void *stream);
+           int64_t N, int64_t K, int out_dtype, void *y, void *workspace,
+           size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

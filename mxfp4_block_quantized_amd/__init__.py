@@ -29,6 +29,7 @@ EXPORTS = (
     "mx_strerror", "mxq_quantize", "mxq_quantize_t", "mxq_dequantize",
     "mxattn_workspace_bytes", "mxattn_workspace_layout", "mxattn_kv_tile",
     "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare", "mxattn_fwd_prepared", "mxgemm",
+    "mxgemm_workspace_bytes",
 )
 
 _lib = None
@@ -64,7 +65,9 @@ def lib():
     L.mxattn_fwd_dump.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P, P, P, P]
     L.mxattn_prepare.argtypes = [P, P, P] + [ci] * 8 + [P, sz, P]
     L.mxattn_fwd_prepared.argtypes = [P, P] + [ci] * 9 + [P, P, sz, P]
-    L.mxgemm.argtypes = [P, P, P, P, i64, i64, i64, ci, P, P]
+    L.mxgemm.argtypes = [P, P, P, P, i64, i64, i64, ci, P, P, sz, P]
+    L.mxgemm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.mxgemm_workspace_bytes.restype = sz
     for f in ("mxq_quantize", "mxq_quantize_t", "mxq_dequantize", "mxattn_workspace_layout",
               "mxattn_kv_tile", "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare",
               "mxattn_fwd_prepared", "mxgemm"):
@@ -253,26 +256,38 @@ def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None
 
 # ------------------------------------------------------------ W4A4 GEMM ----
 
+def gemm_workspace(M: int, N: int, K: int, device="cuda"):
+    """Workspace for ``gemm`` at this shape (uint8 device tensor)."""
+    n = lib().mxgemm_workspace_bytes(M, N, K)
+    if n == 0:
+        raise MxError("mxgemm_workspace_bytes", -1)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
-         out_dtype=torch.float32, out=None, stream=None):
+         out_dtype=torch.float32, out=None, workspace=None, stream=None):
     """y [M, N] = deq(a) deq(b)^T for MXFP4 operands stored as ``quantize``
     writes row-major a [M, K] and b [N, K] (K % 128 == 0)."""
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if workspace is None:
+        workspace = gemm_workspace(M, N, K, a_codes.device)
     assert out.is_contiguous() and out.numel() == M * N
     for t in (a_codes, a_scales, b_codes, b_scales):
         assert t.is_cuda and t.is_contiguous() and t.dtype == torch.uint8
     assert a_codes.numel() == M * K // 2 and b_codes.numel() == N * K // 2
     assert a_scales.numel() == M * K // 32 and b_scales.numel() == N * K // 32
     _check("mxgemm", lib().mxgemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
-                                  M, N, K, _dtype_code(out), _ptr(out), _stream(stream)))
+                                  M, N, K, _dtype_code(out), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
     return out
 
 
 def linear_w4a4(x: torch.Tensor, w_codes, w_scales, N: int, mode="uos",
-                out_dtype=torch.bfloat16, out=None, stream=None):
+                out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
     """x [M, K] (fp32 or bf16) quantized along K with ``mode``, times the
     MXFP4 weight (w_codes [N, K/2], w_scales [N, K/32]): y [M, N]."""
     M, K = x.shape
     xc, xs = quantize(x.contiguous(), mode, stream=stream)
-    return gemm(xc, xs, w_codes, w_scales, M, N, K, out_dtype=out_dtype, out=out, stream=stream)
+    return gemm(xc, xs, w_codes, w_scales, M, N, K, out_dtype=out_dtype, out=out,
+                workspace=workspace, stream=stream)

@@ -292,19 +292,33 @@ int mxattn_fwd_dump(const void* q, const void* k, const void* v, int dtype, int 
 
 }  // extern "C"
 
-int mxgemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int out_dtype, void* y,
-           void* stream) {
-  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+namespace {
+int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return MX_ERR_ARG;
-  if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return MX_ERR_ARG;
   if (K % 128 != 0) return MX_ERR_UNSUPPORTED;
   if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
   // workgroup count (256 x 256 output tiles) must fit a 1-D grid
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
-  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(y, 16) ||
-      !aligned(a_scales, 4) || !aligned(b_scales, 4))
-    return MX_ERR_ALIGN;
+  return MX_OK;
+}
+}  // namespace
+
+size_t mxgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm_shape(M, N, K) != MX_OK) return 0;
+  return mxk::gemm_workspace_bytes(M, N, K);
+}
+
+int mxgemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int out_dtype, void* y,
+           void* workspace, size_t ws_bytes, void* stream) {
+  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+  const int st = check_gemm_shape(M, N, K);
+  if (st != MX_OK) return st;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return MX_ERR_ARG;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
+  if (!workspace || ws_bytes < mxk::gemm_workspace_bytes(M, N, K)) return MX_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MX_ERR_ALIGN;
   return to_status(mxk::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K,
-                                       out_dtype == MX_BF16, y, as_stream(stream)));
+                                       out_dtype == MX_BF16, y, static_cast<uint8_t*>(workspace),
+                                       as_stream(stream)));
 }

@@ -8,24 +8,28 @@
 //
 // Mapping onto v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4): an operand lane
 // l holds row (l % 16) and the 32 K-elements of K-block (l / 16) of one
-// 128-wide K-step -- 16 bytes, one contiguous quarter of that row's 64-byte
-// segment -- plus that block's E8M0 byte.  The product is formed transposed,
-// y^T tile = b-rows x a-rows^T, so that accumulator lane l, register r holds
-// y[m = a-row (l % 16)][n = b-row 4 (l / 16) + r]: four consecutive outputs
-// of one row, written with one 16-byte (fp32) or 8-byte (bf16) store.
+// 128-wide K-step -- 16 bytes -- plus that block's E8M0 byte, one byte of a
+// register picked by the instruction's op_sel.  The product is formed
+// transposed, y^T tile = b-rows x a-rows^T, so that accumulator lane l,
+// register r holds y[m = a-row (l % 16)][n = b-row 4 (l / 16) + r]: four
+// consecutive outputs of one row, one 16-byte (fp32) or 8-byte (bf16) store.
 //
-// Workgroup = 8 waves (two per SIMD: one wave alone cannot issue the matrix
-// instructions back to back) = a 256 (m) x 256 (n) output tile; wave (wm, wn)
-// owns 128 (m) x 64 (n) of it as 8 x 4 accumulator tiles held in VGPRs.  Per
-// K-step the workgroup needs
-// 256 rows x 64 bytes of each operand's codes plus 256 x 4 E8M0 bytes of each;
-// they move global -> LDS with direct loads (global_load_lds) in operand
-// order: code subtile i (16 rows) occupies 1 KiB with lane l's 16 bytes at
-// l * 16, so every operand read is one contiguous ds_read_b128 per lane.
-// K-steps stream through a 4-stage LDS ring (one LDS object per stage, loop
-// unrolled by 4, loads issued 3 steps ahead); each wave reads its step
-// operands from LDS and issues 32 MFMAs, the other wave on its SIMD covering
-// the read latency.
+// Workgroup = 8 waves, two per SIMD (one wave alone cannot issue the matrix
+// instructions back to back), = a 256 (m) x 256 (n) output tile; wave
+// (wm, wn) owns 128 (m) x 64 (n) as 8 x 4 accumulator tiles in VGPRs.
+//
+// Codes move global -> LDS with direct loads (global_load_lds_dwordx4) in
+// stages of 256 K: each row contributes one whole 128-byte line per stage
+// (8 lanes per row), and a stage holds 256 rows of each operand, 64 KiB in
+// all; two stages form the LDS ring.  Within a row the eight 16-byte chunks
+// are stored XOR-swizzled (chunk c of row r in slot c ^ swz(r)) so that the
+// matrix-operand reads -- 16 rows x one chunk per group of 16 lanes -- touch
+// every bank once; the swizzle is applied through the global addresses the
+// direct loads fetch, the LDS side of a direct load being fixed.
+// E8M0 bytes reach the registers without LDS: a pre-pass lays each
+// operand's bytes out as a "scale image", one 4-byte word per lane holding
+// the bytes of four consecutive K-steps, read with one coalesced load per
+// 16-row subtile every 512 K.
 //
 // Rows past M or N read the last valid row (their outputs are not stored).
 // K must be a positive multiple of 128.
@@ -39,25 +43,30 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
-constexpr int kGTile = 256;            // rows of a and of b per workgroup
-constexpr int kGSubA = 8;              // 16-row a subtiles per wave (128 m)
-constexpr int kGSubB = 4;              // 16-row b subtiles per wave (64 n)
-constexpr int kGStages = 4;
-// One K-step in LDS: [a codes 16 KiB][b codes 16 KiB][a E8M0 1 KiB][b E8M0 1 KiB]
+constexpr int kGTile = 256;  // rows of a and of b per workgroup
+constexpr int kGSubA = 8;    // 16-row a subtiles per wave (128 m)
+constexpr int kGSubB = 4;    // 16-row b subtiles per wave (64 n)
+// One stage: 256 K of the tile's 256 rows of a, then of b; 128 bytes a row.
+constexpr int kStRow = 128;
 constexpr int kStA = 0;
-constexpr int kStB = kGTile * 64;
-constexpr int kStSa = 2 * kGTile * 64;
-constexpr int kStSb = kStSa + kGTile * 4;
-constexpr int kStBytes = kStSb + kGTile * 4;
-// direct loads per wave and K-step: 2 + 2 code subtiles, one E8M0 row group of 64
-constexpr int kGLoads = 5;
+constexpr int kStB = kGTile * kStRow;
+constexpr int kStBytes = 2 * kGTile * kStRow;  // 64 KiB
 
+__host__ __device__ constexpr int64_t scale_groups(int64_t K) { return (K / 128 + 3) / 4; }
+
+// slot of the chunks of row r: chunk c sits in slot c ^ swz(r).  Over any 8
+// consecutive rows swz takes 8 distinct values, and over 16 rows the pairs
+// (r % 2, slot) are distinct, so a ds_read_b128 of 16 rows x one chunk is
+// conflict-free whether the LDS serves 8 or 16 lanes per pass.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int SEL>
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, int sa, int sb) {
   v8i av = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
             static_cast<int>(a.w), 0, 0, 0, 0};
   v8i bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
             static_cast<int>(b.w), 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL, sa, SEL, sb);
 }
 
 // s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
@@ -67,57 +76,96 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 struct GemmArgs {
-  const uint8_t* ac;  // [M][K/2]
-  const uint8_t* as;  // [M][K/32]
-  const uint8_t* bc;  // [N][K/2]
-  const uint8_t* bs;  // [N][K/32]
-  void* y;            // [M][N] fp32 or bf16
+  const uint8_t* ac;   // [M][K/2]
+  const uint8_t* bc;   // [N][K/2]
+  const uint8_t* asi;  // scale image of a: [ceil(M/16)][groups][64] words
+  const uint8_t* bsi;  // scale image of b
+  void* y;             // [M][N] fp32 or bf16
   int64_t M, N, K;
   int out_bf16;
   int tiles_m, tiles_n;
 };
 
-// Per-lane source pointers of this wave's direct loads for K-step 0; step s
-// adds s * 64 bytes (codes) or s * 4 bytes (E8M0).
-struct LoadPtrs {
-  const uint8_t* code[4];  // a subtiles wave, wave + 8; b subtiles wave, wave + 8
-  const uint8_t* sc;       // E8M0 bytes of 64 rows (a for waves 0-3, b for 4-7)
-};
-
-__device__ __forceinline__ void issue_step(uint8_t* st, const LoadPtrs& p, int s, int wave) {
-  const int64_t oc = static_cast<int64_t>(s) * 64;
-  const int64_t os = static_cast<int64_t>(s) * 4;
-  __builtin_amdgcn_global_load_lds(p.code[0] + oc, st + kStA + wave * 1024, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(p.code[1] + oc, st + kStA + (wave + 8) * 1024, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(p.code[2] + oc, st + kStB + wave * 1024, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(p.code[3] + oc, st + kStB + (wave + 8) * 1024, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(p.sc + os, st + kStSa + wave * 256, 4, 0, 0);
+// Scale image: the E8M0 byte of (row 16 t + l % 16, block 4 s + l / 16),
+// K-step s = 4 g + j, goes to byte j of word [t][g][l].  Rows and blocks
+// past the end read as 0.
+__global__ void scale_image_kernel(const uint8_t* __restrict__ sc, int64_t rows, int64_t K,
+                                   uint32_t* __restrict__ img) {
+  const int64_t ng = scale_groups(K);
+  const int64_t nb = K / 32;
+  const int64_t total = (rows + 15) / 16 * ng * 64;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int l = static_cast<int>(i & 63);
+    const int64_t g = (i >> 6) % ng;
+    const int64_t t = (i >> 6) / ng;
+    const int64_t r = 16 * t + (l & 15);
+    uint32_t w = 0;
+    if (r < rows) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t b = 4 * (4 * g + j) + (l >> 4);
+        if (b < nb) w |= static_cast<uint32_t>(sc[r * nb + b]) << (8 * j);
+      }
+    }
+    img[i] = w;
+  }
 }
 
-// The 32 MFMAs of one K-step on operands read from LDS stage `st`.
-__device__ __forceinline__ void step_mfma(v4f (&acc)[kGSubB][kGSubA], const uint8_t* st, int wm,
-                                          int wn, int lane) {
-  const int row = lane & 15, grp = lane >> 4;
+// Direct-load sources of this wave: load q (0..3) of a (and of b) covers
+// the tile rows 8 (wave + 8 q) .. + 7; lane L fetches row 8 (wave + 8 q) +
+// L / 8, chunk (L % 8) ^ swz(row), so that the chunk lands in LDS slot L % 8
+// of its row.  The chunk index is the same for all q.
+struct LoadPtrs {
+  const uint8_t* p[8];  // a rows, then b rows; stage 0
+  int chunk;
+};
+
+// Direct loads of one stage (256 K; `off` = its byte offset along a row).
+// In a last stage with one K-step (`half`) the second 64 bytes of a row do
+// not exist: the lanes that would fetch them re-fetch the first half (data
+// that the one K-step does not read from their slots).
+__device__ __forceinline__ void issue_stage(uint8_t* st, const LoadPtrs& lp, int64_t off, bool half,
+                                            int wave) {
+  const int64_t o = off - (half && lp.chunk >= 4 ? 64 : 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_global_load_lds(lp.p[q] + o, st + kStA + (wave + 8 * q) * 1024, 16, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_global_load_lds(lp.p[4 + q] + o, st + kStB + (wave + 8 * q) * 1024, 16, 0, 0);
+}
+
+// The 32 MFMAs of K-step h (0/1) of stage `st`, with E8M0 byte SEL of the
+// scale words.
+template <int SEL>
+__device__ __forceinline__ void step_mfma(v4f (&acc)[kGSubB][kGSubA], const uint8_t* st, int h,
+                                          const uint32_t (&sa)[kGSubA],
+                                          const uint32_t (&sb)[kGSubB], int wm, int wn, int lane) {
+  const int row = lane & 15;
+  const int c = 4 * h + (lane >> 4);
+  // swz(16 t + row) == swz(row)
+  const int off = row * kStRow + ((c ^ swz(row)) << 4);
   uint4 a[kGSubA], b[kGSubB];
-  int sa[kGSubA], sb[kGSubB];
 #pragma unroll
-  for (int i = 0; i < kGSubB; ++i) {
-    const int sub = kGSubB * wn + i;
-    b[i] = *reinterpret_cast<const uint4*>(st + kStB + sub * 1024 + lane * 16);
-    sb[i] = st[kStSb + (16 * sub + row) * 4 + grp];
-  }
+  for (int i = 0; i < kGSubB; ++i)
+    b[i] = *reinterpret_cast<const uint4*>(st + kStB + (kGSubB * wn + i) * 16 * kStRow + off);
 #pragma unroll
-  for (int j = 0; j < kGSubA; ++j) {
-    const int sub = kGSubA * wm + j;
-    a[j] = *reinterpret_cast<const uint4*>(st + kStA + sub * 1024 + lane * 16);
-    sa[j] = st[kStSa + (16 * sub + row) * 4 + grp];
-  }
+  for (int j = 0; j < kGSubA; ++j)
+    a[j] = *reinterpret_cast<const uint4*>(st + kStA + (kGSubA * wm + j) * 16 * kStRow + off);
 #pragma unroll
   for (int j = 0; j < kGSubA; ++j) {
 #pragma unroll
     for (int i = 0; i < kGSubB; ++i)
-      acc[i][j] = mfma_fp4(b[i], a[j], acc[i][j], sb[i], sa[j]);
+      acc[i][j] = mfma_fp4<SEL>(b[i], a[j], acc[i][j], static_cast<int>(sb[i]),
+                                static_cast<int>(sa[j]));
   }
 }
 
@@ -129,9 +177,6 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStBytes];
-  static_assert(kGStages == 4, "one LDS object per stage");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -155,20 +200,36 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
   const int64_t m0 = static_cast<int64_t>(tm) * kGTile;
   const int64_t n0 = static_cast<int64_t>(tn) * kGTile;
 
-  const int64_t ldc = a.K / 2, lds_ = a.K / 32;
-  LoadPtrs p;
+  const int64_t ldc = a.K / 2;
+  LoadPtrs lp;
+  {
+    const int rl = lane >> 3;
+    // swz(8 (wave + 8 q) + rl) does not depend on q
+    lp.chunk = (lane & 7) ^ swz(8 * wave + rl);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int sub = wave + 8 * i;
-    const int64_t ra = min(m0 + 16 * sub + (lane & 15), a.M - 1);
-    const int64_t rb = min(n0 + 16 * sub + (lane & 15), a.N - 1);
-    p.code[i] = a.ac + ra * ldc + (lane >> 4) * 16;
-    p.code[2 + i] = a.bc + rb * ldc + (lane >> 4) * 16;
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (wave + 8 * q) + rl;
+      lp.p[q] = a.ac + min(m0 + r, a.M - 1) * ldc + lp.chunk * 16;
+      lp.p[4 + q] = a.bc + min(n0 + r, a.N - 1) * ldc + lp.chunk * 16;
+    }
   }
-  if (wave < 4)
-    p.sc = a.as + min(m0 + 64 * wave + lane, a.M - 1) * lds_;
-  else
-    p.sc = a.bs + min(n0 + 64 * (wave - 4) + lane, a.N - 1) * lds_;
+
+  // scale-image words of this wave's subtiles (row tiles past the end read
+  // the last one: their outputs are not stored)
+  const int64_t ngrp = scale_groups(a.K);
+  const int64_t last_ta = (a.M + 15) / 16 - 1, last_tb = (a.N + 15) / 16 - 1;
+  const uint32_t* sia[kGSubA];
+  const uint32_t* sib[kGSubB];
+#pragma unroll
+  for (int j = 0; j < kGSubA; ++j) {
+    const int64_t t = min(m0 / 16 + kGSubA * wm + j, last_ta);
+    sia[j] = reinterpret_cast<const uint32_t*>(a.asi) + t * ngrp * 64 + lane;
+  }
+#pragma unroll
+  for (int i = 0; i < kGSubB; ++i) {
+    const int64_t t = min(n0 / 16 + kGSubB * wn + i, last_tb);
+    sib[i] = reinterpret_cast<const uint32_t*>(a.bsi) + t * ngrp * 64 + lane;
+  }
 
   v4f acc[kGSubB][kGSubA];
 #pragma unroll
@@ -177,30 +238,53 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
     for (int j = 0; j < kGSubA; ++j) acc[i][j] = v4f{0, 0, 0, 0};
   }
 
-  const int nk = static_cast<int>(a.K / 128);
-  // Ring: K-step s lives in stage s % 4, loaded three steps ahead.  Iteration
-  // s waits for the wave's own loads of step s (those of s + 1 and s + 2 may
-  // stay in flight); the barrier then makes every wave's loads of step s
-  // visible and tells that every wave is done reading step s - 1, whose
-  // stage the loads of step s + 3 refill.
-  issue_step(lds0, p, 0, wave);
-  if (nk > 1) issue_step(lds1, p, 1, wave);
-  if (nk > 2) issue_step(lds2, p, 2, wave);
-  for (int sb = 0; sb < nk; sb += kGStages) {
+  const int nk = static_cast<int>(a.K / 128);  // K-steps
+  const int nst = (nk + 1) / 2;                 // stages of two K-steps
+  uint32_t sa[kGSubA], sb[kGSubB], na[kGSubA], nb[kGSubB];
+
+  // Stage t lives in LDS slot t % 2; its direct loads are issued at the top
+  // of stage t - 1.  Each stage begins with vmcnt(0) (the wave's loads of
+  // this stage, and of the next scale group, have landed) and a barrier
+  // (every wave's loads have landed, and every wave is done reading stage
+  // t - 1, whose slot the loads of stage t + 1 then refill).  Scale group g
+  // (K-steps 4 g .. 4 g + 3 = stages 2 g, 2 g + 1) is fetched at the top of
+  // stage 2 g - 2.
 #pragma unroll
-    for (int k = 0; k < kGStages; ++k) {
-      const int s = sb + k;
-      if (s < nk) {
-        if (s + 2 < nk) wait_vmcnt<2 * kGLoads>();
-        else if (s + 1 < nk) wait_vmcnt<kGLoads>();
-        else wait_vmcnt<0>();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        uint8_t* fill = k == 0 ? lds3 : k == 1 ? lds0 : k == 2 ? lds1 : lds2;  // stage of s + 3
-        if (s + 3 < nk) issue_step(fill, p, s + 3, wave);
-        const uint8_t* st = k == 0 ? lds0 : k == 1 ? lds1 : k == 2 ? lds2 : lds3;
-        step_mfma(acc, st, wm, wn, lane);
+  for (int j = 0; j < kGSubA; ++j) na[j] = sia[j][0];
+#pragma unroll
+  for (int i = 0; i < kGSubB; ++i) nb[i] = sib[i][0];
+  issue_stage(lds0, lp, 0, nk == 1, wave);
+  for (int tb = 0; tb < nst; tb += 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = tb + k;
+      if (t < nst) {
+        wait_vmcnt<0>();
+        barrier();
+        if (k == 0) {
+          const int g = t / 2;
+#pragma unroll
+          for (int j = 0; j < kGSubA; ++j) sa[j] = na[j];
+#pragma unroll
+          for (int i = 0; i < kGSubB; ++i) sb[i] = nb[i];
+          if (g + 1 < ngrp) {
+#pragma unroll
+            for (int j = 0; j < kGSubA; ++j) na[j] = sia[j][64 * (g + 1)];
+#pragma unroll
+            for (int i = 0; i < kGSubB; ++i) nb[i] = sib[i][64 * (g + 1)];
+          }
+        }
+        if (t + 1 < nst)
+          issue_stage(k == 0 ? lds1 : lds0, lp, static_cast<int64_t>(t + 1) * 128,
+                      2 * (t + 1) + 1 >= nk, wave);
+        const uint8_t* st = k == 0 ? lds0 : lds1;
+        if (k == 0) {
+          step_mfma<0>(acc, st, 0, sa, sb, wm, wn, lane);
+          if (2 * t + 1 < nk) step_mfma<1>(acc, st, 1, sa, sb, wm, wn, lane);
+        } else {
+          step_mfma<2>(acc, st, 0, sa, sb, wm, wn, lane);
+          if (2 * t + 1 < nk) step_mfma<3>(acc, st, 1, sa, sb, wm, wn, lane);
+        }
       }
     }
   }
@@ -246,12 +330,35 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
   }
 }
 
+size_t scale_image_bytes(int64_t rows, int64_t K) {
+  return static_cast<size_t>((rows + 15) / 16 * scale_groups(K) * 256);
+}
+
+hipError_t launch_scale_image(const uint8_t* sc, int64_t rows, int64_t K, uint8_t* img,
+                              hipStream_t stream) {
+  const int64_t total = (rows + 15) / 16 * scale_groups(K) * 64;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(scale_image_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     sc, rows, K, reinterpret_cast<uint32_t*>(img));
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return (scale_image_bytes(M, K) + 255) / 256 * 256 + scale_image_bytes(N, K);
+}
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, int out_bf16,
-                          void* y, hipStream_t stream) {
-  GemmArgs g{ac, as, bc, bs, y, M, N, K, out_bf16, 0, 0};
+                          void* y, uint8_t* ws, hipStream_t stream) {
+  uint8_t* asi = ws;
+  uint8_t* bsi = ws + (scale_image_bytes(M, K) + 255) / 256 * 256;
+  hipError_t e = launch_scale_image(as, M, K, asi, stream);
+  if (e != hipSuccess) return e;
+  e = launch_scale_image(bs, N, K, bsi, stream);
+  if (e != hipSuccess) return e;
+  GemmArgs g{ac, bc, asi, bsi, y, M, N, K, out_bf16, 0, 0};
   g.tiles_m = static_cast<int>((M + kGTile - 1) / kGTile);
   g.tiles_n = static_cast<int>((N + kGTile - 1) / kGTile);
   const int64_t nwg = static_cast<int64_t>(g.tiles_m) * g.tiles_n;

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <cstddef>
 #include <cstdint>
+#include <algorithm>
 
 namespace mxk {
 
@@ -80,10 +81,12 @@ hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
 // W4A4 product y[M][N] = a[M][K] b[N][K]^T of MXFP4 operands (codes
 // [rows][K/2], E8M0 [rows][K/32]); K % 128 == 0; fp32 (out_bf16 == 0) or
-// bf16 output.
+// bf16 output.  ws: gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned
+// (the operands' E8M0 bytes re-laid out for the kernel).
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, int out_bf16,
-                          void* y, hipStream_t stream);
+                          void* y, uint8_t* ws, hipStream_t stream);
 
 // Operands of the 16-bit attention kernel.
 struct F16AttnArgs {

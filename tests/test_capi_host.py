@@ -96,8 +96,9 @@ def test_workspace_and_tile_queries():
 def test_gemm_rejects_bad_args():
     L = mx.lib()
     P = FAKE
-    def g(M=64, N=64, K=256, dt=0, a=P, sa=P, y=P):
-        return L.mxgemm(a, sa, P, P, M, N, K, dt, y, None)
+    big = 1 << 40
+    def g(M=64, N=64, K=256, dt=0, a=P, sa=P, y=P, ws=P, wsb=big):
+        return L.mxgemm(a, sa, P, P, M, N, K, dt, y, ws, wsb, None)
     assert g(K=96) == -2           # K % 128
     assert g(K=0) == -1
     assert g(M=0) == -1
@@ -107,4 +108,9 @@ def test_gemm_rejects_bad_args():
     assert g(y=None) == -1
     assert g(M=1 << 31) == -2
     assert g(y=ctypes.c_void_p((1 << 20) + 8)) == -5   # y not 16-byte aligned
-    assert g(sa=ctypes.c_void_p((1 << 20) + 2)) == -5  # scales not 4-byte aligned
+    assert g(ws=None) == -3
+    assert g(wsb=16) == -3
+    assert g(ws=ctypes.c_void_p((1 << 20) + 128)) == -5
+    assert L.mxgemm_workspace_bytes(64, 64, 96) == 0
+    # two scale images: ceil(rows/16) row tiles x ceil(K/512) groups x 256 B
+    assert L.mxgemm_workspace_bytes(300, 20, 1024) == 19 * 2 * 256 + 2 * 2 * 256
