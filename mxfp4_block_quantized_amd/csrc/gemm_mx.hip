@@ -54,11 +54,12 @@ constexpr int kStBytes = 2 * kGTile * kStRow;  // 64 KiB
 
 __host__ __device__ constexpr int64_t scale_groups(int64_t K) { return (K / 128 + 3) / 4; }
 
-// slot of the chunks of row r: chunk c sits in slot c ^ swz(r).  Over any 8
-// consecutive rows swz takes 8 distinct values, and over 16 rows the pairs
-// (r % 2, slot) are distinct, so a ds_read_b128 of 16 rows x one chunk is
-// conflict-free whether the LDS serves 8 or 16 lanes per pass.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// slot of the chunks of row r: chunk c sits in slot c ^ swz(r).  Over 16
+// consecutive rows (16 t .. 16 t + 15) the pairs (r % 2, slot) are all
+// distinct, so the 16 lanes of a ds_read_b128 that read one chunk of 16 rows
+// fall into distinct 16-byte bank groups; measured free of bank conflicts
+// on gfx950 (and so is (r & 7), unlike mixes of both).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 template <int SEL>
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, int sa, int sb) {
@@ -122,9 +123,13 @@ __global__ void scale_image_kernel(const uint8_t* __restrict__ sc, int64_t rows,
 // Direct-load sources of this wave: load q (0..3) of a (and of b) covers
 // the tile rows 8 (wave + 8 q) .. + 7; lane L fetches row 8 (wave + 8 q) +
 // L / 8, chunk (L % 8) ^ swz(row), so that the chunk lands in LDS slot L % 8
-// of its row.  The chunk index is the same for all q.
+// of its row.  The chunk index is the same for all q.  Bases are uniform
+// (the tile's first row); the per-lane byte offsets fit 32 bits (the row
+// within the tile times K/2 < 2^31).
 struct LoadPtrs {
-  const uint8_t* p[8];  // a rows, then b rows; stage 0
+  const uint8_t* abase;
+  const uint8_t* bbase;
+  uint32_t aoff[4], boff[4];
   int chunk;
 };
 
@@ -134,17 +139,24 @@ struct LoadPtrs {
 // that the one K-step does not read from their slots).
 __device__ __forceinline__ void issue_stage(uint8_t* st, const LoadPtrs& lp, int64_t off, bool half,
                                             int wave) {
-  const int64_t o = off - (half && lp.chunk >= 4 ? 64 : 0);
+  const uint8_t* ab = lp.abase + off;
+  const uint8_t* bb = lp.bbase + off;
+  const uint32_t fix = half && lp.chunk >= 4 ? 64u : 0u;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_global_load_lds(lp.p[q] + o, st + kStA + (wave + 8 * q) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ab + (lp.aoff[q] - fix), st + kStA + (wave + 8 * q) * 1024, 16, 0, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_global_load_lds(lp.p[4 + q] + o, st + kStB + (wave + 8 * q) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(bb + (lp.boff[q] - fix), st + kStB + (wave + 8 * q) * 1024, 16, 0, 0);
 }
 
 // The 32 MFMAs of K-step h (0/1) of stage `st`, with E8M0 byte SEL of the
-// scale words.
+// scale words.  Operand reads: the four b subtiles and a-subtiles 0..3
+// first; a-subtile j + 4 is read right after the MFMAs of a-subtile j have
+// issued, into the registers they release, and is used three MFMA groups
+// later, so its LDS latency stays hidden.  (Left to itself the scheduler
+// reads each operand just before its first use and waits for it, exposing
+// the LDS latency eight times per step.)
 template <int SEL>
 __device__ __forceinline__ void step_mfma(v4f (&acc)[kGSubB][kGSubA], const uint8_t* st, int h,
                                           const uint32_t (&sa)[kGSubA],
@@ -153,20 +165,28 @@ __device__ __forceinline__ void step_mfma(v4f (&acc)[kGSubB][kGSubA], const uint
   const int c = 4 * h + (lane >> 4);
   // swz(16 t + row) == swz(row)
   const int off = row * kStRow + ((c ^ swz(row)) << 4);
+  const uint8_t* pa = st + kStA + kGSubA * wm * 16 * kStRow + off;
+  const uint8_t* pb = st + kStB + kGSubB * wn * 16 * kStRow + off;
   uint4 a[kGSubA], b[kGSubB];
 #pragma unroll
-  for (int i = 0; i < kGSubB; ++i)
-    b[i] = *reinterpret_cast<const uint4*>(st + kStB + (kGSubB * wn + i) * 16 * kStRow + off);
+  for (int i = 0; i < kGSubB; ++i) b[i] = *reinterpret_cast<const uint4*>(pb + i * 16 * kStRow);
 #pragma unroll
-  for (int j = 0; j < kGSubA; ++j)
-    a[j] = *reinterpret_cast<const uint4*>(st + kStA + (kGSubA * wm + j) * 16 * kStRow + off);
+  for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const uint4*>(pa + j * 16 * kStRow);
 #pragma unroll
   for (int j = 0; j < kGSubA; ++j) {
 #pragma unroll
     for (int i = 0; i < kGSubB; ++i)
       acc[i][j] = mfma_fp4<SEL>(b[i], a[j], acc[i][j], static_cast<int>(sb[i]),
                                 static_cast<int>(sa[j]));
+    if (j + 4 < kGSubA) a[j + 4] = *reinterpret_cast<const uint4*>(pa + (j + 4) * 16 * kStRow);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kGSubB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4 * kGSubB, 0);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
@@ -174,130 +194,68 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs
 }
 
-__global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStBytes];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves
-
-  // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
-  // 8 XCDs (workgroup i to XCD i % 8); each XCD takes a contiguous run of the
-  // tile list, which walks column groups of 8 n-tiles with m-tiles inside, so
-  // the ~32 workgroups an XCD holds at once share 4 a-panels and 8 b-panels
-  // in its L2.
-  const int nwg = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int gi = (nwg >> 3) * xcd + min(xcd, nwg & 7) + (static_cast<int>(blockIdx.x) >> 3);
+// Output tile of entry gi of the tile list: column groups of 8 n-tiles,
+// m-tiles inside, so that workgroups working on neighbouring entries share
+// a-panels and b-panels in their XCD's L2.
+__device__ __forceinline__ void tile_origin(const GemmArgs& a, int gi, int64_t& m0, int64_t& n0) {
   constexpr int kGroupN = 8;
   const int per_group = kGroupN * a.tiles_m;
   const int ng = gi / per_group;
   const int rem = gi - ng * per_group;
   const int gn = min(kGroupN, a.tiles_n - ng * kGroupN);  // n-tiles in this group
-  const int tm = rem / gn;
-  const int tn = ng * kGroupN + rem % gn;
-  const int64_t m0 = static_cast<int64_t>(tm) * kGTile;
-  const int64_t n0 = static_cast<int64_t>(tn) * kGTile;
+  m0 = static_cast<int64_t>(rem / gn) * kGTile;
+  n0 = static_cast<int64_t>(ng * kGroupN + rem % gn) * kGTile;
+}
 
-  const int64_t ldc = a.K / 2;
+// Per-lane sources of a tile: direct loads (load q of a and of b covers tile
+// rows 8 (wave + 8 q) .. + 7; lane L fetches row 8 (wave + 8 q) + L / 8,
+// chunk (L % 8) ^ swz(row), which lands in LDS slot L % 8 of its row) and
+// the scale-image words of the wave's subtiles.  Rows and row tiles past
+// the end read the last valid one (their outputs are not stored).
+struct TileSrc {
   LoadPtrs lp;
-  {
-    const int rl = lane >> 3;
-    // swz(8 (wave + 8 q) + rl) does not depend on q
-    lp.chunk = (lane & 7) ^ swz(8 * wave + rl);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 8 * (wave + 8 * q) + rl;
-      lp.p[q] = a.ac + min(m0 + r, a.M - 1) * ldc + lp.chunk * 16;
-      lp.p[4 + q] = a.bc + min(n0 + r, a.N - 1) * ldc + lp.chunk * 16;
-    }
-  }
+  const uint32_t* sia[kGSubA];  // uniform: scale-image row tiles of the wave
+  const uint32_t* sib[kGSubB];
+};
 
-  // scale-image words of this wave's subtiles (row tiles past the end read
-  // the last one: their outputs are not stored)
+__device__ __forceinline__ void tile_sources(const GemmArgs& a, int64_t m0, int64_t n0, int wave,
+                                             int wm, int wn, int lane, TileSrc& ts) {
+  const int64_t ldc = a.K / 2;
+  const int rl = lane >> 3;
+  // swz(8 (wave + 8 q) + rl) = (4 wave + rl / 2) & 7 does not depend on q
+  ts.lp.chunk = (lane & 7) ^ swz(8 * wave + rl);
+  ts.lp.abase = a.ac + m0 * ldc;
+  ts.lp.bbase = a.bc + n0 * ldc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * (wave + 8 * q) + rl;
+    ts.lp.aoff[q] = static_cast<uint32_t>((min(m0 + r, a.M - 1) - m0) * ldc) + ts.lp.chunk * 16;
+    ts.lp.boff[q] = static_cast<uint32_t>((min(n0 + r, a.N - 1) - n0) * ldc) + ts.lp.chunk * 16;
+  }
   const int64_t ngrp = scale_groups(a.K);
   const int64_t last_ta = (a.M + 15) / 16 - 1, last_tb = (a.N + 15) / 16 - 1;
-  const uint32_t* sia[kGSubA];
-  const uint32_t* sib[kGSubB];
 #pragma unroll
   for (int j = 0; j < kGSubA; ++j) {
     const int64_t t = min(m0 / 16 + kGSubA * wm + j, last_ta);
-    sia[j] = reinterpret_cast<const uint32_t*>(a.asi) + t * ngrp * 64 + lane;
+    ts.sia[j] = reinterpret_cast<const uint32_t*>(a.asi) + t * ngrp * 64;
   }
 #pragma unroll
   for (int i = 0; i < kGSubB; ++i) {
     const int64_t t = min(n0 / 16 + kGSubB * wn + i, last_tb);
-    sib[i] = reinterpret_cast<const uint32_t*>(a.bsi) + t * ngrp * 64 + lane;
+    ts.sib[i] = reinterpret_cast<const uint32_t*>(a.bsi) + t * ngrp * 64;
   }
+}
 
-  v4f acc[kGSubB][kGSubA];
+__device__ __forceinline__ void load_scale_group(const TileSrc& ts, int64_t g, int lane,
+                                                 uint32_t (&na)[kGSubA], uint32_t (&nb)[kGSubB]) {
 #pragma unroll
-  for (int i = 0; i < kGSubB; ++i) {
+  for (int j = 0; j < kGSubA; ++j) na[j] = ts.sia[j][64 * g + lane];
 #pragma unroll
-    for (int j = 0; j < kGSubA; ++j) acc[i][j] = v4f{0, 0, 0, 0};
-  }
+  for (int i = 0; i < kGSubB; ++i) nb[i] = ts.sib[i][64 * g + lane];
+}
 
-  const int nk = static_cast<int>(a.K / 128);  // K-steps
-  const int nst = (nk + 1) / 2;                 // stages of two K-steps
-  uint32_t sa[kGSubA], sb[kGSubB], na[kGSubA], nb[kGSubB];
-
-  // Stage t lives in LDS slot t % 2; its direct loads are issued at the top
-  // of stage t - 1.  Each stage begins with vmcnt(0) (the wave's loads of
-  // this stage, and of the next scale group, have landed) and a barrier
-  // (every wave's loads have landed, and every wave is done reading stage
-  // t - 1, whose slot the loads of stage t + 1 then refill).  Scale group g
-  // (K-steps 4 g .. 4 g + 3 = stages 2 g, 2 g + 1) is fetched at the top of
-  // stage 2 g - 2.
-#pragma unroll
-  for (int j = 0; j < kGSubA; ++j) na[j] = sia[j][0];
-#pragma unroll
-  for (int i = 0; i < kGSubB; ++i) nb[i] = sib[i][0];
-  issue_stage(lds0, lp, 0, nk == 1, wave);
-  for (int tb = 0; tb < nst; tb += 2) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int t = tb + k;
-      if (t < nst) {
-        wait_vmcnt<0>();
-        barrier();
-        if (k == 0) {
-          const int g = t / 2;
-#pragma unroll
-          for (int j = 0; j < kGSubA; ++j) sa[j] = na[j];
-#pragma unroll
-          for (int i = 0; i < kGSubB; ++i) sb[i] = nb[i];
-          if (g + 1 < ngrp) {
-#pragma unroll
-            for (int j = 0; j < kGSubA; ++j) na[j] = sia[j][64 * (g + 1)];
-#pragma unroll
-            for (int i = 0; i < kGSubB; ++i) nb[i] = sib[i][64 * (g + 1)];
-          }
-        }
-        if (t + 1 < nst)
-          issue_stage(k == 0 ? lds1 : lds0, lp, static_cast<int64_t>(t + 1) * 128,
-                      2 * (t + 1) + 1 >= nk, wave);
-        const uint8_t* st = k == 0 ? lds0 : lds1;
-        if (k == 0) {
-          step_mfma<0>(acc, st, 0, sa, sb, wm, wn, lane);
-          if (2 * t + 1 < nk) step_mfma<1>(acc, st, 1, sa, sb, wm, wn, lane);
-        } else {
-          step_mfma<2>(acc, st, 0, sa, sb, wm, wn, lane);
-          if (2 * t + 1 < nk) step_mfma<3>(acc, st, 1, sa, sb, wm, wn, lane);
-        }
-      }
-    }
-  }
-
-  // The epilogue stores under per-lane conditions: keep every MFMA ahead of
-  // that divergent region (a matrix instruction issued with part of EXEC off
-  // would drop the disabled lanes' operands, which other lanes' results use).
-#pragma unroll
-  for (int i = 0; i < kGSubB; ++i) {
-#pragma unroll
-    for (int j = 0; j < kGSubA; ++j) asm volatile("" : "+v"(acc[i][j]));
-  }
-
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const v4f (&acc)[kGSubB][kGSubA],
+                                           int64_t m0, int64_t n0, int wm, int wn, int lane) {
   const int row = lane & 15, grp = lane >> 4;
   const bool vec = (a.N & 3) == 0;
 #pragma unroll
@@ -328,6 +286,147 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// Persistent: one workgroup per CU walks a run of output tiles.  Workgroups
+// are dispatched round-robin over the 8 XCDs (workgroup b to XCD b % 8);
+// each XCD owns a contiguous run of the tile list and its workgroups take
+// consecutive entries of it, so that the tiles in flight on an XCD are
+// neighbours in the list.
+__global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves
+
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int wg_x = (nwg >> 3) + (xcd < (nwg & 7) ? 1 : 0);             // workgroups on this XCD
+  const int tiles_x = (ntiles >> 3) + (xcd < (ntiles & 7) ? 1 : 0);    // tiles of this XCD
+  const int first_x = (ntiles >> 3) * xcd + min(xcd, ntiles & 7);
+  int local = static_cast<int>(blockIdx.x) >> 3;
+  if (local >= tiles_x) return;  // uniform over the workgroup
+
+  const int nk = static_cast<int>(a.K / 128);  // K-steps
+  const int nst = (nk + 1) / 2;                 // stages of two K-steps
+  const int64_t ngrp = scale_groups(a.K);
+  // The next tile's first stage (slot 0) is fetched right after the current
+  // tile's last stage, before its stores, when that last stage sits in slot
+  // 1 (an even number of stages).
+  const bool chain = (nst & 1) == 0;
+
+  int64_t m0, n0;
+  tile_origin(a, first_x + local, m0, n0);
+  TileSrc ts;
+  tile_sources(a, m0, n0, wave, wm, wn, lane, ts);
+  uint32_t sa[kGSubA], sb[kGSubB], na[kGSubA], nb[kGSubB];
+  load_scale_group(ts, 0, lane, na, nb);
+  issue_stage(lds0, ts.lp, 0, nk == 1, wave);
+  bool stores_ahead = false;  // the previous tile's stores were issued after this tile's first loads
+
+  for (;;) {
+    const int64_t cm0 = m0, cn0 = n0;  // this tile
+    const int next = local + wg_x;
+    const bool has_next = next < tiles_x;
+    v4f acc[kGSubB][kGSubA];
+#pragma unroll
+    for (int i = 0; i < kGSubB; ++i) {
+#pragma unroll
+      for (int j = 0; j < kGSubA; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+    }
+
+    // Stage t lives in LDS slot t % 2; its direct loads are issued at the top
+    // of stage t - 1.  Each stage begins with a wait for the wave's loads of
+    // this stage (and of the next scale group) and a barrier (every wave's
+    // loads have landed, and every wave is done reading stage t - 1, whose
+    // slot the loads of stage t + 1 then refill).  Scale group g (K-steps
+    // 4 g .. 4 g + 3 = stages 2 g, 2 g + 1) is fetched at the top of stage
+    // 2 g - 2.  Vector memory operations complete in issue order, so with
+    // the previous tile's 32 stores issued after this tile's first loads,
+    // vmcnt(32) waits for those loads alone.
+    for (int tb = 0; tb < nst; tb += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int t = tb + k;
+        if (t < nst) {
+          if (t == 0 && stores_ahead)
+            wait_vmcnt<kGSubA * kGSubB>();
+          else
+            wait_vmcnt<0>();
+          barrier();
+          if (k == 0) {
+#pragma unroll
+            for (int j = 0; j < kGSubA; ++j) sa[j] = na[j];
+#pragma unroll
+            for (int i = 0; i < kGSubB; ++i) sb[i] = nb[i];
+            if (t / 2 + 1 < ngrp) load_scale_group(ts, t / 2 + 1, lane, na, nb);
+          }
+          if (t + 1 < nst)
+            issue_stage(k == 0 ? lds1 : lds0, ts.lp, static_cast<int64_t>(t + 1) * 128,
+                        2 * (t + 1) + 1 >= nk, wave);
+          const uint8_t* st = k == 0 ? lds0 : lds1;
+          if (k == 0) {
+            step_mfma<0>(acc, st, 0, sa, sb, wm, wn, lane);
+            if (2 * t + 1 < nk) step_mfma<1>(acc, st, 1, sa, sb, wm, wn, lane);
+          } else {
+            step_mfma<2>(acc, st, 0, sa, sb, wm, wn, lane);
+            if (2 * t + 1 < nk) step_mfma<3>(acc, st, 1, sa, sb, wm, wn, lane);
+          }
+        }
+      }
+    }
+
+    // The epilogue stores under per-lane conditions: keep every MFMA ahead of
+    // that divergent region (a matrix instruction issued with part of EXEC
+    // off would drop the disabled lanes' operands, which other lanes' results
+    // use).
+#pragma unroll
+    for (int i = 0; i < kGSubB; ++i) {
+#pragma unroll
+      for (int j = 0; j < kGSubA; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
+    if (chain && has_next) {
+      // slot 0 (stage nst - 2) was released by the last stage's barrier
+      tile_origin(a, first_x + next, m0, n0);
+      tile_sources(a, m0, n0, wave, wm, wn, lane, ts);
+      load_scale_group(ts, 0, lane, na, nb);
+      issue_stage(lds0, ts.lp, 0, nk == 1, wave);
+    }
+    store_tile(a, acc, cm0, cn0, wm, wn, lane);
+    if (!has_next) break;
+    // a full tile issues exactly kGSubA * kGSubB stores per wave
+    const bool full = cm0 + kGTile <= a.M && cn0 + kGTile <= a.N && (a.N & 3) == 0;
+    stores_ahead = chain && full;
+    if (!chain) {
+      wait_vmcnt<0>();
+      barrier();  // every wave is done with both slots
+      tile_origin(a, first_x + next, m0, n0);
+      tile_sources(a, m0, n0, wave, wm, wn, lane, ts);
+      load_scale_group(ts, 0, lane, na, nb);
+      issue_stage(lds0, ts.lp, 0, nk == 1, wave);
+    }
+    local = next;
+  }
+}
+
+// Compute units of the current device (cached per device).
+hipError_t cu_count(int* out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cache[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[dev] = n;
+  }
+  *out = cache[dev];
+  return hipSuccess;
 }
 
 size_t scale_image_bytes(int64_t rows, int64_t K) {
@@ -361,7 +460,12 @@ hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* b
   GemmArgs g{ac, bc, asi, bsi, y, M, N, K, out_bf16, 0, 0};
   g.tiles_m = static_cast<int>((M + kGTile - 1) / kGTile);
   g.tiles_n = static_cast<int>((N + kGTile - 1) / kGTile);
-  const int64_t nwg = static_cast<int64_t>(g.tiles_m) * g.tiles_n;
+  const int64_t ntiles = static_cast<int64_t>(g.tiles_m) * g.tiles_n;
+  int cus = 0;
+  e = cu_count(&cus);
+  if (e != hipSuccess) return e;
+  // one resident workgroup per CU (128 KiB of LDS and 512 threads each)
+  const int64_t nwg = std::min<int64_t>(ntiles, cus);
   hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(nwg)), dim3(kGThreads), 0, stream,
                      g);
   return hipGetLastError();

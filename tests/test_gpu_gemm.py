@@ -99,6 +99,30 @@ def test_deterministic_and_linear_w4a4():
     check(torch_out(torch, y1), y, yabs, K, False, "linear_w4a4 700x600x1024")
 
 
+@pytest.mark.parametrize("shape", [(4352, 4352, 640), (4352, 4400, 512), (4500, 4352, 1536)])
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_many_tiles_per_workgroup(shape, out_bf16):
+    """More output tiles than compute units: each workgroup walks several
+    tiles (odd and even numbers of 256-K stages, full and ragged tiles)."""
+    torch, mx = gpu()
+    M, N, K = shape
+    print(f"[case] gemm many tiles M={M} N={N} K={K} bf16={out_bf16}", flush=True)
+    rng = np.random.default_rng(M + N + K)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = (rng.standard_normal((N, K)) * 0.1).astype(np.float32)
+    ac, as_ = oracle.quantize(a, oracle.RULE_UOS)
+    bc, bs = oracle.quantize(b, oracle.RULE_UOS)
+    dev = lambda t: torch.from_numpy(t).cuda()
+    out = mx.gemm(dev(ac), dev(as_), dev(bc), dev(bs), M, N, K,
+                  out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    rows = np.sort(rng.choice(M, 96, replace=False))
+    rows[-1] = M - 1
+    y, yabs = oracle.gemm_q(ac.reshape(M, K // 2)[rows], as_.reshape(M, K // 32)[rows], bc, bs,
+                            rows.size, N, K)
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    check(got, y, yabs, K, out_bf16, f"many tiles {shape}")
+
+
 # ----------------------------------------------------------- full sizes ----
 
 @functools.lru_cache(maxsize=1)
