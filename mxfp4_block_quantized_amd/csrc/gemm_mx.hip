@@ -288,6 +288,46 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const v4f (&acc)[k
   }
 }
 
+// bf16 epilogue through LDS: each wave owns an 8 KiB area of the free stage
+// slot and, in two rounds of 64 rows, writes its 64-row x 64-column bf16
+// block there (one 128-byte line per row; the eight 16-byte chunks of row r
+// XOR-swizzled by r & 7 against bank conflicts), then reads it back as
+// whole lines and stores each row with 8 lanes x 16 bytes.  Needs a full
+// tile and N % 8 == 0; issues exactly 16 stores per wave.
+__device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& a,
+                                                    const v4f (&acc)[kGSubB][kGSubA], int64_t m0,
+                                                    int64_t n0, int wm, int wn, int lane,
+                                                    uint8_t* area) {
+  const int row16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int lrow = 16 * jj + row16;
+#pragma unroll
+      for (int i = 0; i < kGSubB; ++i) {
+        const v4f v = acc[i][4 * r + jj];
+        const int chunk = 2 * i + (g >> 1);
+        const int addr = lrow * 128 + ((chunk ^ (lrow & 7)) << 4) + (g & 1) * 8;
+        *reinterpret_cast<uint2*>(area + addr) =
+            make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+      }
+    }
+    // the area is this wave's alone: its own writes are in order before
+    // its reads (LDS operations of one wave execute in order)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int lrow = 8 * q + (lane >> 3);
+      const int p = lane & 7;
+      const uint4 w = *reinterpret_cast<const uint4*>(area + lrow * 128 + (p << 4));
+      const int chunk = p ^ (lrow & 7);
+      const int64_t m = m0 + 128 * wm + 64 * r + lrow;
+      const int64_t n = n0 + 64 * wn + 8 * chunk;
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + m * a.N + n) = w;
+    }
+  }
+}
+
 // Persistent: one workgroup per CU walks a run of output tiles.  Workgroups
 // are dispatched round-robin over the 8 XCDs (workgroup b to XCD b % 8);
 // each XCD owns a contiguous run of the tile list and its workgroups take
@@ -326,6 +366,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
   load_scale_group(ts, 0, lane, na, nb);
   issue_stage(lds0, ts.lp, 0, nk == 1, wave);
   bool stores_ahead = false;  // the previous tile's stores were issued after this tile's first loads
+  bool staged_prev = false;   // ... and went through LDS (16 per wave)
 
   for (;;) {
     const int64_t cm0 = m0, cn0 = n0;  // this tile
@@ -352,7 +393,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
       for (int k = 0; k < 2; ++k) {
         const int t = tb + k;
         if (t < nst) {
-          if (t == 0 && stores_ahead)
+          if (t == 0 && stores_ahead && staged_prev)
+            wait_vmcnt<16>();
+          else if (t == 0 && stores_ahead)
             wait_vmcnt<kGSubA * kGSubB>();
           else
             wait_vmcnt<0>();
@@ -395,11 +438,20 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
       load_scale_group(ts, 0, lane, na, nb);
       issue_stage(lds0, ts.lp, 0, nk == 1, wave);
     }
-    store_tile(a, acc, cm0, cn0, wm, wn, lane);
+    const bool full = cm0 + kGTile <= a.M && cn0 + kGTile <= a.N;
+    const bool staged = full && a.out_bf16 && (a.N & 7) == 0;
+    if (staged) {
+      // slot 1 is free once every wave is done reading the last stage (the
+      // next tile's first loads, if any, go to slot 0)
+      barrier();
+      store_tile_bf16_lds(a, acc, cm0, cn0, wm, wn, lane, lds1 + wave * 8192);
+    } else {
+      store_tile(a, acc, cm0, cn0, wm, wn, lane);
+    }
     if (!has_next) break;
-    // a full tile issues exactly kGSubA * kGSubB stores per wave
-    const bool full = cm0 + kGTile <= a.M && cn0 + kGTile <= a.N && (a.N & 3) == 0;
-    stores_ahead = chain && full;
+    // stores per wave of a full tile: 16 staged (bf16) or kGSubA * kGSubB direct
+    stores_ahead = chain && full && (staged || (a.N & 3) == 0);
+    staged_prev = staged;
     if (!chain) {
       wait_vmcnt<0>();
       barrier();  // every wave is done with both slots
