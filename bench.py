@@ -39,15 +39,17 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "mxfp4_block_quantized_amd", "csrc", f)
                 for f in ("attn_mx.hip", "internal.h")]
+GEMM_SOURCES = [os.path.join(ROOT, "mxfp4_block_quantized_amd", "csrc", f)
+                for f in ("gemm_mx.hip", "internal.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=ATTN_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in ATTN_SOURCES:
+    for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -81,12 +83,12 @@ def time_attention(torch, mx, qt, kt, vt, c, mode, steps, warmup):
     return wall / steps * 1e3, prep, attn
 
 
-def read_traffic(sha: str, workload: str):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary, if it was taken on this kernel source."""
+def read_traffic(sha: str, workload: str, kernel="attn_mx_kernel"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary, if it was taken on this kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)["attn_mx_kernel"]
+            t = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
         return None
     if t.get("src_sha256") != sha or t.get("workload") != workload:
@@ -189,9 +191,11 @@ def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
     gemm_ms = timed(lambda: mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=work))
     lin_ms = timed(lambda: (mx.quantize(xt, "uos", xc, xs),
                             mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=work)))
+    alg_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
     return {"workload": f"{name}: x [{M}, {K}] bf16 (N(0,1), 1% channels x20) times UOS-MXFP4 "
                         f"weight [{N}, {K}] (Student-t(3)*0.02, 0.1% x50), bf16 output",
-            "flops": flops,
+            "flops": flops, "algorithmic_bytes": alg_bytes,
+            "traffic": read_traffic(kernel_source_sha(GEMM_SOURCES), name, "gemm_mx_kernel"),
             "gemm_ms": gemm_ms, "gemm_tflops": flops / gemm_ms / 1e9,
             "gemm_frac_fp4_peak": flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS,
             "linear_w4a4_ms": lin_ms, "linear_w4a4_tflops": flops / lin_ms / 1e9}
@@ -225,7 +229,7 @@ def main():
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
-                    help="only the standalone quantizer (for profiling it alone)")
+                    help="only the standalone quantizer and the GEMM (for profiling them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size "
@@ -253,7 +257,12 @@ def main():
             torch.empty_like(src).copy_(src)
             torch.cuda.synchronize()
             del src
-        print(json.dumps({"quantizer": bench_quantizer(torch, mx, reps=3)}), flush=True)
+        res = {}
+        if not args.no_quantizer:
+            res["quantizer"] = bench_quantizer(torch, mx, reps=3)
+        if not args.no_gemm:
+            res["gemm"] = bench_gemm(torch, mx, reps=3)
+        print(json.dumps(res), flush=True)
         return
     c = dict(mxsynth.CONFIGS[args.workload])
     log(f"[bench] generating {args.workload} inputs")
