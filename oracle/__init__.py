@@ -76,6 +76,8 @@ def _load():
     lib.oracle_dequantize.restype = ci
     lib.oracle_attn_rows.argtypes = [P, P, P, ci] + [ci] * 9 + [P, i64, P, P, P, P, P, P]
     lib.oracle_attn_rows.restype = ci
+    lib.oracle_attn_rows_split.argtypes = [P, P, P, ci] + [ci] * 9 + [i64, P, i64, P, P, P, P, P, P]
+    lib.oracle_attn_rows_split.restype = ci
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ci
     lib.oracle_efq_beta.argtypes = []
@@ -181,14 +183,17 @@ def dequantize(codes, scales):
 
 
 def attn_rows(q, k, v, *, causal: bool, mode: int, bc: int, rows,
-              want_p: bool = False, want_tiles: bool = False):
+              want_p: bool = False, want_tiles: bool = False, split: int = 0):
     """Attention output rows, binary64.
 
     q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (float32 or bf16 bits as uint16).
     ``rows``: flattened (b*Hq + h)*Sq + i indices.  ``bc``: keys per KV
-    tile (the running-max schedule).  Returns a dict with ``o`` [n, D],
-    ``l`` [n], ``m`` [n] and, on request, ``p_codes``/``p_scales`` and
-    ``m_tiles``."""
+    tile (the running-max schedule).  ``split``: keys per split (a multiple
+    of ``bc``; 0 = none): each split runs its own running max and the
+    splits are merged in order.  Causal queries are aligned to the end of
+    the keys (query i sees keys j <= i + Skv - Sq).  Returns a dict with
+    ``o`` [n, D], ``l`` [n], ``m`` [n] and, on request,
+    ``p_codes``/``p_scales`` and ``m_tiles``."""
     q, dt = _as_input(q)
     k, dt2 = _as_input(k)
     v, dt3 = _as_input(v)
@@ -208,9 +213,9 @@ def attn_rows(q, k, v, *, causal: bool, mode: int, bc: int, rows,
     pc = np.empty((n, skv_pad // 2), np.uint8) if want_p else None
     ps = np.empty((n, skv_pad // BLOCK), np.uint8) if want_p else None
     mt = np.empty((n, ntiles), np.float64) if want_tiles else None
-    rc = _load().oracle_attn_rows(
+    rc = _load().oracle_attn_rows_split(
         _ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
-        int(mode), int(bc), _ptr(rows), n, _ptr(o), _ptr(l_out), _ptr(m_out),
+        int(mode), int(bc), int(split), _ptr(rows), n, _ptr(o), _ptr(l_out), _ptr(m_out),
         _ptr(mt), _ptr(pc), _ptr(ps))
     if rc != 0:
         raise ValueError(f"oracle_attn_rows failed ({rc})")

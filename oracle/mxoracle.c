@@ -272,6 +272,26 @@ static void fake_quant(double *x, int64_t len, int rule)
     }
 }
 
+/* At the last tile of a split, fold the split's state (m, l, acc) into the
+ * merged state (M, Lm, accm); a split that saw no key (m = -inf) adds
+ * nothing. */
+static void merge_if_split_end(int64_t t, int64_t tiles_per_split, int64_t ntiles, int D,
+                               const double *m, const double *l, const double *acc,
+                               double *M, double *Lm, double *accm)
+{
+    if ((t + 1) % tiles_per_split != 0 && t + 1 != ntiles)
+        return;
+    if (*m == -INFINITY)
+        return;
+    const double Mn = *M > *m ? *M : *m;
+    const double wa = (*M == -INFINITY) ? 0.0 : exp(*M - Mn);
+    const double wb = exp(*m - Mn);
+    for (int d = 0; d < D; ++d)
+        accm[d] = accm[d] * wa + acc[d] * wb;
+    *Lm = *Lm * wa + *l * wb;
+    *M = Mn;
+}
+
 /*
  * Attention on a list of query rows.
  *
@@ -289,20 +309,34 @@ static void fake_quant(double *x, int64_t len, int rule)
  *   p_codes  [nrows][skv_pad/2], p_scales [nrows][skv_pad/32] -- the P~
  *                          codes and E8M0 bytes (quantized modes only),
  *                          skv_pad = ceil(Skv/32)*32, unvisited blocks zero.
+ *
+ * Causal: query i sees keys j <= i + (Skv - Sq) (queries aligned to the end
+ * of the key sequence; Sq == Skv gives j <= i).  Sq <= Skv is required.
+ *
+ * split (oracle_attn_rows_split): keys per split, a multiple of bc, or 0 for
+ * none.  The keys are cut into splits [s*split, (s+1)*split) from key 0; each
+ * split runs the tile loop above on its own from m = -inf, so its P~ blocks
+ * are scaled by the split's own running max, and the splits are then merged
+ * in ascending order by the usual rescaling: with M the larger of the two
+ * maxima, acc = acc*exp(m - M) + acc_s*exp(m_s - M), and likewise l.  A
+ * split with no visible key contributes nothing.  With one split (or none)
+ * this is the unsplit result exactly.
  */
-int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
-                     int B, int Hq, int Hkv, int Sq, int Skv, int D,
-                     int causal, int mode, int bc,
-                     const int64_t *rows, int64_t nrows, double *out,
-                     double *l_out, double *m_out, double *m_tiles,
-                     uint8_t *p_codes, uint8_t *p_scales)
+int oracle_attn_rows_split(const void *q, const void *k, const void *v, int dtype,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                           int causal, int mode, int bc, int64_t split,
+                           const int64_t *rows, int64_t nrows, double *out,
+                           double *l_out, double *m_out, double *m_tiles,
+                           uint8_t *p_codes, uint8_t *p_scales)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1)
         return -1;
     if (Hq % Hkv != 0 || D % ORC_BLOCK != 0 || bc < ORC_BLOCK ||
         bc % ORC_BLOCK != 0 || mode < 0 || mode > 4)
         return -1;
-    if (causal && Sq != Skv)
+    if (causal && Sq > Skv)
+        return -1;
+    if (split < 0 || split % bc != 0)
         return -1;
     const int quantized = (mode != ORC_MODE_FP16);
     const int rule = (mode == ORC_MODE_OCP) ? ORC_RULE_OCP : ORC_RULE_UOS;
@@ -311,6 +345,7 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
     const int group = Hq / Hkv;
     const int64_t skv_pad = ((int64_t)Skv + ORC_BLOCK - 1) / ORC_BLOCK * ORC_BLOCK;
     const int64_t ntiles = ((int64_t)Skv + bc - 1) / bc;
+    const int64_t tiles_per_split = (split > 0) ? split / bc : ntiles;
     const double inv_sqrt_d = 1.0 / sqrt((double)D);
 
     for (int64_t r = 0; r < nrows; ++r)
@@ -377,6 +412,11 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
                 if (quantized)
                     fake_quant(qr, D, rule);
 
+                /* last visible key of this query */
+                const int64_t klim = causal ? (int64_t)i + (Skv - Sq) : (int64_t)Skv - 1;
+                /* merged state of the finished splits */
+                double M = -INFINITY, Lm = 0.0;
+                double *accm = (double *)calloc((size_t)D, sizeof(double));
                 double m = -INFINITY, l = 0.0;
                 uint8_t *pc = p_codes ? p_codes + r * (skv_pad / 2) : NULL;
                 uint8_t *ps = p_scales ? p_scales + r * (skv_pad / ORC_BLOCK) : NULL;
@@ -386,13 +426,21 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
                     memset(ps, 0, (size_t)(skv_pad / ORC_BLOCK));
 
                 for (int64_t t = 0; t < ntiles; ++t) {
+                    if (t % tiles_per_split == 0) {
+                        /* a new split starts from scratch */
+                        m = -INFINITY;
+                        l = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            acc[d] = 0.0;
+                    }
                     int64_t t0 = t * bc;
                     int64_t nvalid = Skv - t0 < bc ? Skv - t0 : bc;
-                    if (causal && i + 1 - t0 < nvalid)
-                        nvalid = i + 1 - t0; /* keys j <= i only */
+                    if (klim + 1 - t0 < nvalid)
+                        nvalid = klim + 1 - t0; /* keys j <= klim only */
                     if (nvalid <= 0) {       /* nothing visible: state unchanged */
                         if (m_tiles)
                             m_tiles[r * ntiles + t] = m;
+                        merge_if_split_end(t, tiles_per_split, ntiles, D, &m, &l, acc, &M, &Lm, accm);
                         continue;
                     }
                     /* scores */
@@ -465,16 +513,19 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
                     m = mnew;
                     if (m_tiles)
                         m_tiles[r * ntiles + t] = m;
+                    /* (merge below) */
+                    merge_if_split_end(t, tiles_per_split, ntiles, D, &m, &l, acc, &M, &Lm, accm);
                 }
                 /* final normalization [EFQ] */
                 for (int d = 0; d < D; ++d)
-                    out[r * D + d] = acc[d] / l;
+                    out[r * D + d] = accm[d] / Lm;
                 if (l_out)
-                    l_out[r] = l;
+                    l_out[r] = Lm;
                 if (m_out)
-                    m_out[r] = m;
+                    m_out[r] = M;
                 free(qr);
                 free(acc);
+                free(accm);
                 free(s);
                 free(p);
                 free(pt);
@@ -497,4 +548,15 @@ int oracle_threads(void)
 #else
     return 1;
 #endif
+}
+
+int oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                     int causal, int mode, int bc,
+                     const int64_t *rows, int64_t nrows, double *out,
+                     double *l_out, double *m_out, double *m_tiles,
+                     uint8_t *p_codes, uint8_t *p_scales)
+{
+    return oracle_attn_rows_split(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, bc, 0,
+                                  rows, nrows, out, l_out, m_out, m_tiles, p_codes, p_scales);
 }
