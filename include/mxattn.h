@@ -215,6 +215,47 @@ int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
                     uint8_t *p_scales, void *stream);
 
 /*
+ * Short-query attention over key splits (decode): the same attention as
+ * mxattn_fwd for few queries against many keys, with the keys cut into
+ * splits of mxattn_decode_split(B, Hkv, Skv) keys (a multiple of the
+ * 128-key tile, counted from key 0).  Each split runs the tiled online
+ * softmax on its own, from m = -inf ("EFQ-Softmax", abstract: running-max
+ * update, history rescaling, final normalization), so the P~ blocks of a
+ * split are scaled by that split's running max; the splits are then merged
+ * in ascending order by rescaling to the largest max.  One wave handles the
+ * (Hq/Hkv) x Sq queries of one GQA group on one split, reading the group's
+ * K~/V~ once.
+ *
+ * Arguments as for mxattn_fwd, except: causal queries are aligned to the
+ * end of the keys (query i sees keys j <= i + Skv - Sq; Sq <= Skv);
+ * (Hq/Hkv) * Sq <= 16 and an MX mode (MXATTN_OCP .. MXATTN_UOS_EFQ), else
+ * MX_ERR_UNSUPPORTED (FP16 mode and longer query blocks: mxattn_fwd); the
+ * workspace holds mxattn_decode_workspace_bytes(...) bytes (the
+ * mxattn_prepare layout followed by the per-split partial states).
+ * mxattn_decode_prepared runs the split and merge kernels on a workspace
+ * that mxattn_prepare filled (q, k, v are not read: a quantized KV cache is
+ * reused across calls).  mxattn_decode_dump also writes the P~ codes and
+ * E8M0 bytes of selected rows (as mxattn_fwd_dump).
+ * mxattn_decode_split returns MX_ERR_ARG, and the workspace size 0, for bad
+ * arguments.
+ */
+int mxattn_decode_split(int B, int Hkv, int Skv);
+size_t mxattn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv,
+                                     int D, int dtype, int mode);
+int mxattn_decode(const void *q, const void *k, const void *v, int dtype,
+                  int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                  int mode, float *o, void *workspace, size_t ws_bytes,
+                  void *stream);
+int mxattn_decode_prepared(int dtype, int B, int Hq, int Hkv, int Sq, int Skv,
+                           int D, int causal, int mode, float *o,
+                           void *workspace, size_t ws_bytes, void *stream);
+int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                       int causal, int mode, float *o, void *workspace,
+                       size_t ws_bytes, const int32_t *row_slot,
+                       uint8_t *p_codes, uint8_t *p_scales, void *stream);
+
+/*
  * W4A4 product of two MXFP4 operands ("MXCode: Vector Quantization for
  * MX-Native Inference at Scale", abstract: MX-native W4A4 operands; the
  * 32-element blocks and E8M0 scales of the OCP MX format):

@@ -29,7 +29,8 @@ EXPORTS = (
     "mx_strerror", "mxq_quantize", "mxq_quantize_t", "mxq_dequantize",
     "mxattn_workspace_bytes", "mxattn_workspace_layout", "mxattn_kv_tile",
     "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare", "mxattn_fwd_prepared", "mxgemm",
-    "mxgemm_workspace_bytes",
+    "mxgemm_workspace_bytes", "mxattn_decode_split", "mxattn_decode_workspace_bytes",
+    "mxattn_decode", "mxattn_decode_prepared", "mxattn_decode_dump",
 )
 
 _lib = None
@@ -66,11 +67,18 @@ def lib():
     L.mxattn_prepare.argtypes = [P, P, P] + [ci] * 8 + [P, sz, P]
     L.mxattn_fwd_prepared.argtypes = [P, P] + [ci] * 9 + [P, P, sz, P]
     L.mxgemm.argtypes = [P, P, P, P, i64, i64, i64, ci, P, P, sz, P]
+    L.mxattn_decode_split.argtypes = [ci, ci, ci]
+    L.mxattn_decode_workspace_bytes.argtypes = [ci] * 8
+    L.mxattn_decode_workspace_bytes.restype = sz
+    L.mxattn_decode.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P]
+    L.mxattn_decode_prepared.argtypes = [ci] * 9 + [P, P, sz, P]
+    L.mxattn_decode_dump.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P, P, P, P]
     L.mxgemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxgemm_workspace_bytes.restype = sz
     for f in ("mxq_quantize", "mxq_quantize_t", "mxq_dequantize", "mxattn_workspace_layout",
               "mxattn_kv_tile", "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare",
-              "mxattn_fwd_prepared", "mxgemm"):
+              "mxattn_fwd_prepared", "mxgemm", "mxattn_decode_split", "mxattn_decode",
+              "mxattn_decode_prepared", "mxattn_decode_dump"):
         getattr(L, f).restype = ci
     _lib = L
     return L
@@ -248,6 +256,84 @@ def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None
     if workspace is None:
         workspace = alloc_workspace(q, k, mode)
     _check("mxattn_fwd_dump", lib().mxattn_fwd_dump(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+        _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _ptr(slot),
+        _ptr(pc), _ptr(ps), _stream(stream)))
+    return out, pc[:n], ps[:n], workspace
+
+
+# ------------------------------------------------- short-query (decode) ----
+
+def decode_split(B: int, Hkv: int, Skv: int) -> int:
+    """Keys per split of attn_decode for this shape: the schedule the
+    oracle must mirror (attn_rows(..., split=...))."""
+    r = lib().mxattn_decode_split(B, Hkv, Skv)
+    if r < 0:
+        raise MxError("mxattn_decode_split", r)
+    return r
+
+
+def alloc_decode_workspace(q, k, mode):
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    nb = lib().mxattn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dt, _mode(mode, MODES))
+    if nb == 0:
+        raise ValueError("invalid or unsupported decode shape")
+    return torch.empty(nb, dtype=torch.uint8, device=q.device)
+
+
+def attn_decode(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
+                stream=None):
+    """Short-query attention over key splits (fp32 output); causal queries
+    are aligned to the end of the keys.  q [B,Hq,Sq,D] with (Hq/Hkv)*Sq <=
+    16, k/v [B,Hkv,Skv,D]."""
+    for t in (q, k, v):
+        assert t.is_cuda and t.is_contiguous()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_decode_workspace(q, k, mode)
+    _check("mxattn_decode", lib().mxattn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+        _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def attn_decode_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None,
+                         stream=None):
+    """attn_decode on a workspace filled by attn_prepare (shapes from q, k;
+    their data is not read)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    _check("mxattn_decode_prepared", lib().mxattn_decode_prepared(
+        _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), _mode(mode, MODES),
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def attn_decode_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None,
+                     stream=None):
+    """attn_decode plus the P~ codes / E8M0 bytes of the flattened query
+    rows ``rows``; returns (o, p_codes, p_scales, workspace)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    rows = torch.as_tensor(rows, dtype=torch.int64)
+    n = rows.numel()
+    skv_ld = (Skv + 127) // 128 * 128
+    slot = torch.full((B * Hq * Sq,), -1, dtype=torch.int32)
+    slot[rows] = torch.arange(n, dtype=torch.int32)
+    slot = slot.to(q.device)
+    pc = torch.zeros((max(n, 1), skv_ld // 2), dtype=torch.uint8, device=q.device)
+    ps = torch.zeros((max(n, 1), skv_ld // 32), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_decode_workspace(q, k, mode)
+    _check("mxattn_decode_dump", lib().mxattn_decode_dump(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _ptr(slot),
         _ptr(pc), _ptr(ps), _stream(stream)))

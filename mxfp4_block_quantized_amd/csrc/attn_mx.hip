@@ -532,10 +532,198 @@ hipError_t pick_mode(const MxAttnArgs& a, hipStream_t s) {
   }
 }
 
+// ---- short-query attention over key splits ----------------------------
+//
+// One wave per (b, KV head g, split): its 16 query columns are the G x Sq
+// queries of the GQA group (column c = h_local * Sq + i, G * Sq <= 16),
+// so the group's K~/V~ are read once per split.  The wave runs the same
+// tile step as above (S^T on the matrix core with -m as accumulator input,
+// block scales, P~, O^T += V~^T P~^T) over the split's KV tiles, with its
+// own running max from -inf, reading the tile images straight from global
+// memory into the operand registers (nothing is shared between waves), the
+// next tile's loads in flight during the current tile.  It leaves (m, l,
+// unnormalized O) per query column; the merge kernel combines the splits
+// in ascending order.  Columns with no visible key in the split leave
+// m = -inf, l = 0, O = 0.
+template <int D>
+struct TileOps {
+  uint4 kop[kSub];
+  uint2 ksc;
+  uint4 vop[D / 16];
+  uint32_t vsc[(D / 16 + 3) / 4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile_ops(TileOps<D>& t, const uint8_t* st, int lane) {
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int i = 0; i < kSub; ++i) t.kop[i] = *reinterpret_cast<const uint4*>(st + kImgKc + i * 1024 + lane * 16);
+  t.ksc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) t.vop[n] = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
+  if (NT == 8) {
+    const uint2 v2 = *reinterpret_cast<const uint2*>(st + img_vs(D) + lane * 8);
+    t.vsc[0] = v2.x;
+    t.vsc[(NT + 3) / 4 - 1] = v2.y;
+  } else {
+    t.vsc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
+  }
+}
+
+template <int D, int UOS, int PNQ, int DUMP>
+__global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d, float sl2) {
+  const MxAttnArgs& a = d.at;
+  constexpr int IMG = img_bytes(D);
+  constexpr int NT = D / 16;
+  constexpr int DC = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t nunits = static_cast<int64_t>(a.B) * a.Hkv * d.nsplit;
+  if (unit >= nunits) return;  // whole wave; no barriers in this kernel
+  const int sp = static_cast<int>(unit % d.nsplit);
+  const int64_t bg = unit / d.nsplit;
+  const int b = static_cast<int>(bg / a.Hkv), g = static_cast<int>(bg % a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // query of this column; unused columns multiply zero codes and see every key
+  const bool cvalid = col < G * a.Sq;
+  const int hl = cvalid ? col / a.Sq : 0, qi = cvalid ? col % a.Sq : 0;
+  const int64_t bh = static_cast<int64_t>(b) * a.Hq + g * G + hl;
+  uint4 qop = make_uint4(0, 0, 0, 0);
+  int qsc = 127;
+  if (cvalid && grp < DC) {
+    const int64_t row = bh * a.Sq + qi;
+    qop = *reinterpret_cast<const uint4*>(a.qc + row * (D / 2) + grp * 16);
+    qsc = a.qs[row * DC + grp];
+  }
+  const int klim = (cvalid && a.causal) ? qi + (a.Skv - a.Sq) : a.Skv - 1;
+  const int qrow = cvalid ? qi : a.Sq;  // rows >= Sq are never dumped
+
+  const int nt = static_cast<int>(a.skv_ld / kKvTile);
+  const int t_begin = sp * d.split_tiles;
+  const int t_end = min(t_begin + d.split_tiles, nt);
+  // tiles needing the per-key mask: past the key end, or past the first
+  // causal limit (Skv - Sq)
+  const int first_masked = a.causal ? (a.Skv - a.Sq) / kKvTile : (a.Skv % kKvTile ? nt - 1 : nt);
+
+  WaveState<D> w;
+  w.m[0] = -INFINITY;
+  w.mref[0] = 0.0f;
+  w.lsum[0] = 0.0f;
+  w.lacc[0] = v4f{0, 0, 0, 0};
+#pragma unroll
+  for (int n = 0; n < NT; ++n) w.oacc[0][n] = v4f{0, 0, 0, 0};
+
+  const uint8_t* img = a.img + bg * nt * static_cast<int64_t>(IMG);
+  TileOps<D> cur, nxt;
+  if (t_begin < t_end) load_tile_ops<D>(cur, img + static_cast<int64_t>(t_begin) * IMG, lane);
+  for (int t = t_begin; t < t_end; ++t) {
+    if (t + 1 < t_end) load_tile_ops<D>(nxt, img + static_cast<int64_t>(t + 1) * IMG, lane);
+    const int j0 = t * kKvTile;
+    v4f s[kSub];
+    s_tile(s, cur.kop, cur.ksc, qop, qsc, w.mref[0]);
+    if (t >= first_masked) mask_tile(s, klim - (j0 + grp * 32));
+    const TileStats ts = tile_stats<D, UOS, PNQ>(w, 0, s, sl2);
+    float vsum;
+    const uint4 pop = p_tile<PNQ>(s, sl2, ts.kofs, vsum);
+    dump_tile<DUMP>(a, bh, qrow, j0 <= klim, j0, grp, pop, ts.X);
+    pv_tile<D, PNQ>(w, 0, pop, ts, vsum, cur.vop, cur.vsc);
+    if (t + 1 < t_end) cur = nxt;
+  }
+
+  // pin the accumulators ahead of the per-lane stores (see attn_mx_kernel)
+#pragma unroll
+  for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[0][n]));
+  asm volatile("" : "+v"(w.lacc[0]));
+  const float l = PNQ ? w.lacc[0][0] : xlane_sum4(w.lsum[0]);
+  const bool empty = klim < t_begin * kKvTile;  // no visible key in this split
+  if (cvalid) {  // unused columns are never merged
+    float* pr = d.part + (unit * 16 + col) * (D + 2);
+    if (grp == 0) {
+      pr[0] = empty ? -INFINITY : w.m[0];
+      pr[1] = empty ? 0.0f : l;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const v4f v = empty ? v4f{0, 0, 0, 0} : w.oacc[0][n];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[2 + 16 * n + 4 * grp + r] = v[r];
+    }
+  }
+}
+
+// One wave per query row: O = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s,
+// M the largest m_s, splits in ascending order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, float sl2) {
+  const MxAttnArgs& a = d.at;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (b*Hq + h)*Sq + i
+  if (row >= static_cast<int64_t>(a.B) * a.Hq * a.Sq) return;
+  const int i = static_cast<int>(row % a.Sq);
+  const int64_t bh = row / a.Sq;
+  const int h = static_cast<int>(bh % a.Hq), b = static_cast<int>(bh / a.Hq);
+  const int G = a.Hq / a.Hkv;
+  const int64_t bg = static_cast<int64_t>(b) * a.Hkv + h / G;
+  const int col = (h % G) * a.Sq + i;
+  const float* base = d.part + (bg * d.nsplit * 16 + col) * (D + 2);
+  const int64_t stride = 16 * static_cast<int64_t>(D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < d.nsplit; ++s) M = fmaxf(M, base[s * stride]);
+  constexpr int PER = D / 64;
+  float acc[PER], L = 0.0f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+  for (int s = 0; s < d.nsplit; ++s) {
+    const float* ps = base + s * stride;
+    const float wgt = __builtin_amdgcn_exp2f((ps[0] - M) * sl2);  // 0 for an empty split
+    L = fmaf(wgt, ps[1], L);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wgt, ps[2 + lane + 64 * k], acc[k]);
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) a.o[row * D + lane + 64 * k] = acc[k] * inv;
+}
+
+template <int D, int UOS, int PNQ, int DUMP>
+hipError_t launch_decode_t(const MxDecodeArgs& d, hipStream_t s) {
+  const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
+  const int64_t nunits = static_cast<int64_t>(d.at.B) * d.at.Hkv * d.nsplit;
+  hipLaunchKernelGGL((attn_decode_kernel<D, UOS, PNQ, DUMP>), dim3(static_cast<unsigned>((nunits + kWaves - 1) / kWaves)),
+                     dim3(kThreads), 0, s, d, sl2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = static_cast<int64_t>(d.at.B) * d.at.Hq * d.at.Sq;
+  hipLaunchKernelGGL((attn_decode_merge_kernel<D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s,
+                     d, sl2);
+  return hipGetLastError();
+}
+
+template <int D, int UOS, int PNQ>
+hipError_t decode_pick_dump(const MxDecodeArgs& d, hipStream_t s) {
+  return d.at.row_slot ? launch_decode_t<D, UOS, PNQ, 1>(d, s) : launch_decode_t<D, UOS, PNQ, 0>(d, s);
+}
+template <int D>
+hipError_t decode_pick_mode(const MxDecodeArgs& d, hipStream_t s) {
+  switch (d.at.mode) {
+    case 1: return decode_pick_dump<D, 0, 0>(d, s);
+    case 2: return decode_pick_dump<D, 1, 0>(d, s);
+    case 3: return decode_pick_dump<D, 1, 1>(d, s);
+    default: return decode_pick_dump<D, 1, 2>(d, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream) {
   return a.D == 64 ? pick_mode<64>(a, stream) : pick_mode<128>(a, stream);
+}
+
+hipError_t launch_attn_decode(const MxDecodeArgs& d, hipStream_t stream) {
+  return d.at.D == 64 ? decode_pick_mode<64>(d, stream) : decode_pick_mode<128>(d, stream);
 }
 
 }  // namespace mxk

@@ -168,6 +168,95 @@ int attn_common(const void* q, const void* k, const void* v, int dtype, int B, i
                        dump ? p_scales : nullptr, s);
 }
 
+// ---- short-query attention over key splits ----
+
+// KV tiles per split: at least 4 (the per-split partial state is small next
+// to the keys it covers), more when the (b, KV head) groups alone give
+// about 2048 waves (8 per CU).
+int decode_split_tiles(int B, int Hkv, int Skv) {
+  const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kKvTile - 1) / mxk::kKvTile;
+  const int64_t groups = static_cast<int64_t>(B) * Hkv;
+  int64_t st = (nt * groups + 2047) / 2048;
+  if (st < 4) st = 4;
+  if (st > nt) st = nt;
+  return static_cast<int>(st);
+}
+
+int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                       int mode) {
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
+  if (mode < MXATTN_FP16 || mode > MXATTN_UOS_EFQ) return MX_ERR_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1) return MX_ERR_ARG;
+  if (causal != 0 && causal != 1) return MX_ERR_ARG;
+  if (Hq % Hkv != 0) return MX_ERR_ARG;
+  if (mode == MXATTN_FP16) return MX_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return MX_ERR_UNSUPPORTED;
+  if ((Hq / Hkv) * static_cast<int64_t>(Sq) > 16) return MX_ERR_UNSUPPORTED;
+  if (causal && Sq > Skv) return MX_ERR_UNSUPPORTED;
+  if (B > 65535 || Hq > 65535) return MX_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * Hkv * Skv * D > (int64_t(1) << 40)) return MX_ERR_UNSUPPORTED;
+  return MX_OK;
+}
+
+struct DecodeLayout {
+  Layout L;        // Q~ and KV images as for mxattn_prepare
+  size_t part;     // partial states
+  size_t total;
+  int split_tiles, nsplit;
+};
+
+DecodeLayout make_decode_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                                int mode) {
+  DecodeLayout dl;
+  dl.L = make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode);
+  dl.split_tiles = decode_split_tiles(B, Hkv, Skv);
+  const int64_t nt = dl.L.skv_ld / mxk::kKvTile;
+  dl.nsplit = static_cast<int>((nt + dl.split_tiles - 1) / dl.split_tiles);
+  dl.part = round_up(dl.L.total, 256);
+  dl.total = dl.part + static_cast<size_t>(B) * Hkv * dl.nsplit * 16 * (D + 2) * sizeof(float);
+  return dl;
+}
+
+int decode_common(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                  int Hkv, int Sq, int Skv, int D, int causal, int mode, float* o, void* ws,
+                  size_t ws_bytes, const int32_t* row_slot, uint8_t* p_codes,
+                  uint8_t* p_scales, bool prepare, bool dump, void* stream) {
+  int st = check_decode_shape(dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode);
+  if (st != MX_OK) return st;
+  if (prepare && (!q || !k || !v)) return MX_ERR_ARG;
+  if (!o) return MX_ERR_ARG;
+  if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)) ||
+      !aligned(o, 16))
+    return MX_ERR_ALIGN;
+  if (dump && (!row_slot || !p_codes || !p_scales)) return MX_ERR_ARG;
+  if (dump && (!aligned(p_codes, 16) || !aligned(row_slot, 4))) return MX_ERR_ALIGN;
+  const DecodeLayout dl = make_decode_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode);
+  if (!ws || ws_bytes < dl.total) return MX_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MX_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  if (prepare) {
+    st = run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, dl.L, ws, s);
+    if (st != MX_OK) return st;
+  }
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  mxk::MxDecodeArgs d{};
+  d.at.qc = w + dl.L.off[0];
+  d.at.qs = w + dl.L.off[1];
+  d.at.img = w + dl.L.off[2];
+  d.at.o = o;
+  d.at.row_slot = dump ? row_slot : nullptr;
+  d.at.p_codes = dump ? p_codes : nullptr;
+  d.at.p_scales = dump ? p_scales : nullptr;
+  d.at.B = B; d.at.Hq = Hq; d.at.Hkv = Hkv; d.at.Sq = Sq; d.at.Skv = Skv; d.at.D = D;
+  d.at.skv_ld = dl.L.skv_ld;
+  d.at.causal = causal;
+  d.at.mode = mode;
+  d.part = reinterpret_cast<float*>(w + dl.part);
+  d.split_tiles = dl.split_tiles;
+  d.nsplit = dl.nsplit;
+  return to_status(mxk::launch_attn_decode(d, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,4 +410,36 @@ int mxgemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_cod
   return to_status(mxk::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K,
                                        out_dtype == MX_BF16, y, static_cast<uint8_t*>(workspace),
                                        as_stream(stream)));
+}
+
+int mxattn_decode_split(int B, int Hkv, int Skv) {
+  if (B < 1 || Hkv < 1 || Skv < 1) return MX_ERR_ARG;
+  return decode_split_tiles(B, Hkv, Skv) * mxk::kKvTile;
+}
+
+size_t mxattn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                                     int mode) {
+  if (check_decode_shape(dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode) != MX_OK) return 0;
+  return make_decode_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode).total;
+}
+
+int mxattn_decode(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                  int Sq, int Skv, int D, int causal, int mode, float* o, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  return decode_common(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, workspace,
+                       ws_bytes, nullptr, nullptr, nullptr, true, false, stream);
+}
+
+int mxattn_decode_prepared(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                           int mode, float* o, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_common(nullptr, nullptr, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o,
+                       workspace, ws_bytes, nullptr, nullptr, nullptr, false, false, stream);
+}
+
+int mxattn_decode_dump(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                       int Hkv, int Sq, int Skv, int D, int causal, int mode, float* o,
+                       void* workspace, size_t ws_bytes, const int32_t* row_slot,
+                       uint8_t* p_codes, uint8_t* p_scales, void* stream) {
+  return decode_common(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, workspace,
+                       ws_bytes, row_slot, p_codes, p_scales, true, true, stream);
 }

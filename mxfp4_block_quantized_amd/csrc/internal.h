@@ -79,6 +79,18 @@ struct MxAttnArgs {
 };
 hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
+// Short-query attention over key splits: one wave per (b, KV head, split)
+// computes the partial softmax state of the (Hq/Hkv) x Sq queries of a GQA
+// group (at most 16) over its keys; a second kernel merges the splits in
+// order into o.  Causal queries are aligned to the end of the keys.
+struct MxDecodeArgs {
+  MxAttnArgs at;      // Q~, KV images, o, dump, shapes, mode (at.causal: end-aligned)
+  float* part;        // [B*Hkv*nsplit][16][D + 2]: m, l, unnormalized O per query slot
+  int split_tiles;    // KV tiles (128 keys) per split
+  int nsplit;
+};
+hipError_t launch_attn_decode(const MxDecodeArgs& a, hipStream_t stream);
+
 // W4A4 product y[M][N] = a[M][K] b[N][K]^T of MXFP4 operands (codes
 // [rows][K/2], E8M0 [rows][K/32]); K % 128 == 0; fp32 (out_bf16 == 0) or
 // bf16 output.  ws: gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned

@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "tiny_attn", "tiny_quant",
     "roundtrip_tensor", "llm_prefill", "video_dit", "sample_rows", "CONFIGS",
-    "w4a4_operands", "GEMM_CONFIGS", "make_gemm_inputs",
+    "w4a4_operands", "GEMM_CONFIGS", "make_gemm_inputs", "llm_decode", "DECODE_CONFIGS",
 ]
 
 
@@ -98,6 +98,34 @@ def llm_prefill(seed: int = 3, B: int = 4, Hq: int = 32, Hkv: int = 8,
         for h in range(g * group, (g + 1) * group):
             q[:, h, :, ch] *= np.float32(gain)
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def llm_decode(seed: int = 8, B: int = 8, Hq: int = 32, Hkv: int = 8, Sq: int = 1,
+               Skv: int = 32768, D: int = 128, frac: float = 0.02, gain: float = 15.0):
+    """Short-query GQA shapes (a decode step against a long key/value cache):
+    q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D], bf16 bits.  The recipe of
+    ``llm_prefill`` with separate query and key lengths: q, k, v ~ N(0,1) in
+    that order (k and v in chunks of KV heads), then per KV head round(frac*D)
+    channels (``rng.choice``) x gain in K head g and its query heads."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (B, Hq, Sq, D))
+    k = np.empty((B, Hkv, Skv, D), np.uint16)
+    v = np.empty((B, Hkv, Skv, D), np.uint16)
+    nch = int(round(frac * D))
+    group = Hq // Hkv
+    chans = []
+    kf = [_normal(rng, (B, 1, Skv, D)) for _ in range(Hkv)]
+    for g in range(Hkv):
+        v[:, g:g + 1] = f32_to_bf16_bits(_normal(rng, (B, 1, Skv, D)))
+    for g in range(Hkv):
+        ch = rng.choice(D, nch, replace=False)
+        chans.append(ch)
+        kf[g][:, :, :, ch] *= np.float32(gain)
+        k[:, g:g + 1] = f32_to_bf16_bits(kf[g])
+        kf[g] = None
+        for h in range(g * group, (g + 1) * group):
+            q[:, h, :, ch] *= np.float32(gain)
+    return f32_to_bf16_bits(q), k, v
 
 
 def _smooth_bias(rng, grid, std):
@@ -214,3 +242,10 @@ def make_gemm_inputs(name: str):
     """(x, w) for a named workload of ``GEMM_CONFIGS``."""
     c = GEMM_CONFIGS[name]
     return w4a4_operands(c["seed"], c["M"], c["N"], c["K"])
+
+
+# Short-query workloads: one decode step of the LLM shape (32 query heads,
+# 8 KV heads, D = 128) against a 32K-token cache.
+DECODE_CONFIGS = {
+    "llm_decode": dict(B=8, Hq=32, Hkv=8, Sq=1, Skv=32768, D=128, causal=True, seed=8),
+}

@@ -114,3 +114,24 @@ def test_gemm_rejects_bad_args():
     assert L.mxgemm_workspace_bytes(64, 64, 96) == 0
     # two scale images: ceil(rows/16) row tiles x ceil(K/512) groups x 256 B
     assert L.mxgemm_workspace_bytes(300, 20, 1024) == 19 * 2 * 256 + 2 * 2 * 256
+
+
+def test_decode_rejects_bad_args():
+    L = mx.lib()
+    P = FAKE
+    big = 1 << 40
+    def d(dtype=1, B=1, Hq=8, Hkv=2, Sq=1, Skv=1000, D=128, causal=0, mode=3, ws=P, wsb=big, q=P):
+        return L.mxattn_decode(q, P, P, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, P, ws, wsb, None)
+    assert d(mode=0) == -2                 # FP16 mode: use mxattn_fwd
+    assert d(Sq=5) == -2                   # (Hq/Hkv) * Sq > 16
+    assert d(D=96) == -2
+    assert d(causal=1, Sq=4, Skv=3) == -2  # causal needs Sq <= Skv
+    assert d(Hq=6, Hkv=4) == -1
+    assert d(mode=5) == -1
+    assert d(q=None) == -1
+    assert d(ws=None) == -3
+    assert d(wsb=10) == -3
+    assert L.mxattn_decode_split(1, 8, 32768) % 128 == 0
+    assert L.mxattn_decode_split(0, 8, 32768) == -1
+    assert L.mxattn_decode_workspace_bytes(1, 8, 2, 1, 1000, 128, 1, 0) == 0
+    assert L.mxattn_decode_workspace_bytes(1, 8, 2, 1, 1000, 128, 1, 3) > 0

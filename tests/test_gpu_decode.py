@@ -1,0 +1,108 @@
+"""GPU parity of short-query attention over key splits (``mxattn_decode``)
+against the binary64 oracle run with the same split schedule.
+
+Bars as for mxattn_fwd: O max-abs <= 2e-3 and mean-abs <= 2e-4; the P~
+codes and E8M0 bytes read back through the dump entry point differ from the
+oracle's in at most 1e-4 of the elements; the dump variant and the prepared
+variant give the same O bits as the plain call.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+from common import (FLIP_MAX, MAX_ABS, MEAN_ABS, MODE_IDS, flips, gpu, mxsynth, np_u8,
+                    to_torch)
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+MX_MODES = ["ocp", "uos", "uos_pnq", "uos_efq"]
+
+
+def run_decode(q, k, v, causal, mode, rows=None, label=""):
+    torch, mx = gpu()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    split = mx.decode_split(B, Hkv, Skv)
+    print(f"[case] decode {label} mode={mode} causal={causal} q={q.shape} k={k.shape} "
+          f"split={split}", flush=True)
+    if rows is None:
+        rows = np.arange(B * Hq * Sq, dtype=np.int64)
+    qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
+    o = mx.attn_decode(qt, kt, vt, causal=causal, mode=mode)
+    o2, pc, ps, ws = mx.attn_decode_dump(qt, kt, vt, rows, causal=causal, mode=mode)
+    assert torch.equal(o, o2), "dump variant changed O"
+    mx.attn_prepare(qt, kt, vt, mode=mode, workspace=ws)
+    o3 = mx.attn_decode_prepared(qt, kt, ws, causal=causal, mode=mode)
+    assert torch.equal(o, o3), "prepared variant changed O"
+    ref = oracle.attn_rows(q, k, v, causal=causal, mode=MODE_IDS[mode], bc=128, rows=rows,
+                           want_p=True, split=split)
+    got = o.reshape(-1, D)[torch.from_numpy(rows).to(o.device)].double().cpu().numpy()
+    err = np.abs(got - ref["o"])
+    fr, sfr, nflip = flips(np_u8(pc), np_u8(ps), ref["p_codes"], ref["p_scales"], Skv)
+    stats = {"max_abs": float(err.max()), "mean_abs": float(err.mean()), "flip_frac": fr,
+             "scale_flip_frac": sfr, "nflip": nflip}
+    print(f"[case] decode {label} {mode}: {stats}", flush=True)
+    assert fr <= FLIP_MAX, stats
+    assert stats["max_abs"] <= MAX_ABS, stats
+    assert stats["mean_abs"] <= MEAN_ABS, stats
+    return o
+
+
+SMALL = [
+    # (B, Hq, Hkv, Sq, Skv, D, causal)
+    (1, 8, 2, 1, 1000, 128, True),      # 4 heads x 1 query per group
+    (2, 4, 4, 4, 700, 64, False),       # MHA, 4 queries
+    (1, 16, 2, 2, 2049, 128, True),     # 16 query columns, ragged keys
+    (1, 8, 8, 16, 4097, 128, True),     # last split (key 4096) empty for rows 0..14
+    (3, 6, 2, 5, 1300, 64, True),       # 15 columns
+]
+
+
+@pytest.mark.parametrize("mode", MX_MODES)
+@pytest.mark.parametrize("shape", SMALL)
+def test_small_decode(shape, mode):
+    B, Hq, Hkv, Sq, Skv, D, causal = shape
+    q, k, v = mxsynth.llm_decode(40 + Skv, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, D=D)
+    run_decode(q, k, v, causal, mode, label=f"{shape}")
+
+
+def test_decode_single_key_and_v_ones():
+    torch, mx = gpu()
+    # one key: O is that key's quantized value row
+    q, k, v = mxsynth.llm_decode(50, B=1, Hq=4, Hkv=1, Sq=1, Skv=1, D=128)
+    run_decode(q, k, v, True, "uos_pnq", label="one key")
+    # V = 1 under PNQ (and EFQ): O = 1 up to fp32 rounding, through the merge
+    q, k, v = mxsynth.llm_decode(51, B=1, Hq=8, Hkv=2, Sq=2, Skv=3000, D=128)
+    v[:] = mxsynth.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    for mode in ("uos_pnq", "uos_efq"):
+        o = mx.attn_decode(to_torch(q), to_torch(k), to_torch(v), causal=True, mode=mode)
+        assert (o - 1.0).abs().max().item() <= 1e-5
+
+
+def test_decode_deterministic():
+    torch, mx = gpu()
+    q, k, v = mxsynth.llm_decode(52, B=2, Hq=8, Hkv=2, Sq=1, Skv=5000, D=128)
+    qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
+    a = mx.attn_decode(qt, kt, vt, causal=True, mode="uos_pnq")
+    b = mx.attn_decode(qt, kt, vt, causal=True, mode="uos_pnq")
+    assert torch.equal(a, b)
+
+
+@functools.lru_cache(maxsize=1)
+def full_inputs(name):
+    c = mxsynth.DECODE_CONFIGS[name]
+    return mxsynth.llm_decode(c["seed"], B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], Sq=c["Sq"],
+                              Skv=c["Skv"], D=c["D"])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", ["uos_pnq", "uos_efq", "ocp"])
+def test_full_llm_decode(mode):
+    c = mxsynth.DECODE_CONFIGS["llm_decode"]
+    q, k, v = full_inputs("llm_decode")
+    # every query of batch items 0 and B-1
+    per_b = c["Hq"] * c["Sq"]
+    rows = np.r_[np.arange(per_b), np.arange((c["B"] - 1) * per_b, c["B"] * per_b)].astype(np.int64)
+    run_decode(q, k, v, c["causal"], mode, rows=rows, label="llm_decode")
