@@ -655,13 +655,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
 }
 
 // One wave per query row: O = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s,
-// M the largest m_s, splits in ascending order.
+// M the largest m_s, splits in ascending order.  The lanes first take the
+// splits' (m, l) in parallel (wave max and sum), leaving each split's
+// weight in LDS; then each lane accumulates its channels over the splits,
+// eight splits' loads in flight at a time.
+constexpr int kMaxSplits = 1024;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, float sl2) {
+  __shared__ float wts[4][kMaxSplits];
   const MxAttnArgs& a = d.at;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (b*Hq + h)*Sq + i
-  if (row >= static_cast<int64_t>(a.B) * a.Hq * a.Sq) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wv;  // (b*Hq + h)*Sq + i
+  if (row >= static_cast<int64_t>(a.B) * a.Hq * a.Sq) return;  // whole wave; no block barrier
   const int i = static_cast<int>(row % a.Sq);
   const int64_t bh = row / a.Sq;
   const int h = static_cast<int>(bh % a.Hq), b = static_cast<int>(bh / a.Hq);
@@ -671,18 +688,37 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   const float* base = d.part + (bg * d.nsplit * 16 + col) * (D + 2);
   const int64_t stride = 16 * static_cast<int64_t>(D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < d.nsplit; ++s) M = fmaxf(M, base[s * stride]);
+  for (int s = lane; s < d.nsplit; s += 64) M = fmaxf(M, base[s * stride]);
+  M = wave_max(M);
+  float L = 0.0f;
+  for (int s = lane; s < d.nsplit; s += 64) {
+    const float wgt = __builtin_amdgcn_exp2f((base[s * stride] - M) * sl2);  // 0 when empty
+    wts[wv][s] = wgt;
+    L = fmaf(wgt, base[s * stride + 1], L);
+  }
+  L = wave_sum(L);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   constexpr int PER = D / 64;
-  float acc[PER], L = 0.0f;
+  float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-  for (int s = 0; s < d.nsplit; ++s) {
-    const float* ps = base + s * stride;
-    const float wgt = __builtin_amdgcn_exp2f((ps[0] - M) * sl2);  // 0 for an empty split
-    L = fmaf(wgt, ps[1], L);
+  int s = 0;
+  for (; s + 8 <= d.nsplit; s += 8) {
+    float o[8][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wgt, ps[2 + lane + 64 * k], acc[k]);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[u][k] = base[(s + u) * stride + 2 + lane + 64 * k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][s + u], o[u][k], acc[k]);
   }
+  for (; s < d.nsplit; ++s)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][s], base[s * stride + 2 + lane + 64 * k], acc[k]);
   const float inv = 1.0f / L;
 #pragma unroll
   for (int k = 0; k < PER; ++k) a.o[row * D + lane + 64 * k] = acc[k] * inv;

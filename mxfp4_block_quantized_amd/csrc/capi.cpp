@@ -178,6 +178,7 @@ int decode_split_tiles(int B, int Hkv, int Skv) {
   const int64_t groups = static_cast<int64_t>(B) * Hkv;
   int64_t st = (nt * groups + 2047) / 2048;
   if (st < 4) st = 4;
+  if (st < (nt + 1023) / 1024) st = (nt + 1023) / 1024;  // at most 1024 splits (merge kernel)
   if (st > nt) st = nt;
   return static_cast<int>(st);
 }
