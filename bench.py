@@ -15,6 +15,10 @@ alongside  = the UOS+EFQ (exp-free P~), FP16, OCP and UOS modes on the same
              inputs;
 quantizer  = the standalone quantize / dequantize of the 8192 x 28672 bf16
              roundtrip tensor, GB/s against 8 TB/s HBM;
+decode     = short-query attention over key splits (mxattn_decode_prepared,
+             KV cache already quantized) on one LLM decode step (B=8, 32 query
+             / 8 KV heads, 32768 cached keys), GB/s of the quantized KV cache
+             read against 8 TB/s;
 gemm       = the W4A4 product (mxgemm) on the DiT feed-forward up-projection
              (32760 tokens x 5120 -> 13824, UOS operands, bf16 output), alone
              and with the activation quantization, against 10.1 PFLOP/s;
@@ -159,6 +163,45 @@ def bench_quantizer(torch, mx, reps=20):
     return res
 
 
+def bench_decode(torch, mx, reps=20, name="llm_decode"):
+    import mxsynth
+    c = mxsynth.DECODE_CONFIGS[name]
+    B, Hq, Hkv, Sq, Skv, D = c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Skv"], c["D"]
+    log(f"[bench] decode: generating {name} inputs")
+    q, k, v = mxsynth.llm_decode(c["seed"], B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, D=D)
+    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
+    qt, kt, vt = to(q), to(k), to(v)
+    del q, k, v
+    res = {"workload": f"{name}: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} causal "
+                       f"(end-aligned), bf16 inputs, KV cache quantized once",
+           "split_keys": mx.decode_split(B, Hkv, Skv)}
+    nt = (Skv + 127) // 128
+    # one KV tile image: K codes (8 KiB), V codes (64 D), K and V scales (512 + 4 D),
+    # rounded up to 1 KiB -- the quantized KV cache the kernel streams
+    img_bytes = B * Hkv * nt * ((8192 + 64 * D + 512 + 4 * D + 1023) // 1024 * 1024)
+    alg = img_bytes + B * Hq * Sq * D * 17 // 32 + B * Hq * Sq * D * 4  # KV cache, Q~, fp32 O
+    flops = 4.0 * B * Hq * Sq * Skv * D
+    for mode in ("uos_pnq", "uos_efq"):
+        ws = mx.alloc_decode_workspace(qt, kt, mode)
+        mx.attn_prepare(qt, kt, vt, mode=mode, workspace=ws)
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            mx.attn_decode_prepared(qt, kt, ws, causal=True, mode=mode, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            mx.attn_decode_prepared(qt, kt, ws, causal=True, mode=mode, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[mode] = {"ms": ms, "gbps": alg / ms / 1e6, "frac_hbm": alg / ms / 1e6 / HBM_PEAK_GBPS,
+                     "tflops": flops / ms / 1e9}
+        del ws
+    res["algorithmic_bytes"] = alg
+    return res
+
+
 def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
     import mxsynth
     g = mxsynth.GEMM_CONFIGS[name]
@@ -228,6 +271,7 @@ def main():
                     help="first mode is the headline; the rest run alongside")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
                     help="only the standalone quantizer and the GEMM (for profiling them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -262,6 +306,8 @@ def main():
             res["quantizer"] = bench_quantizer(torch, mx, reps=3)
         if not args.no_gemm:
             res["gemm"] = bench_gemm(torch, mx, reps=3)
+        if not args.no_decode:
+            res["decode"] = bench_decode(torch, mx, reps=3)
         print(json.dumps(res), flush=True)
         return
     c = dict(mxsynth.CONFIGS[args.workload])
@@ -325,6 +371,9 @@ def main():
     if not args.no_gemm:
         out["gemm"] = bench_gemm(torch, mx)
         log(f"[bench] gemm: {out['gemm']}")
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, mx)
+        log(f"[bench] decode: {out['decode']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, c, args.workload)
