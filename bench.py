@@ -179,7 +179,7 @@ def bench_decode(torch, mx, reps=20, name="llm_decode"):
     # one KV tile image: K codes (8 KiB), V codes (64 D), K and V scales (512 + 4 D),
     # rounded up to 1 KiB -- the quantized KV cache the kernel streams
     img_bytes = B * Hkv * nt * ((8192 + 64 * D + 512 + 4 * D + 1023) // 1024 * 1024)
-    alg = img_bytes + B * Hq * Sq * D * 17 // 32 + B * Hq * Sq * D * 4  # KV cache, Q~, fp32 O
+    alg = img_bytes + B * Hq * Sq * D * 2 + B * Hq * Sq * D * 4  # KV cache, bf16 Q, fp32 O
     flops = 4.0 * B * Hq * Sq * Skv * D
     for mode in ("uos_pnq", "uos_efq"):
         ws = mx.alloc_decode_workspace(qt, kt, mode)

@@ -120,6 +120,8 @@ size_t mxattn_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D,
  * Where the quantized operands of an MX mode lie inside the workspace (host
  * array `off` of 6 entries):
  *   off[0] Q~ codes [B][Hq][Sq][D/2]      off[1] Q~ scales [B][Hq][Sq][D/32]
+ *          (written only by the dump entry points: the attention kernels
+ *          quantize Q themselves, and the dump variants store that Q~ here)
  *   off[2] KV tile images [B][Hkv][skv_ld/128][off[3]]
  *   off[3] bytes per image (17408 for D = 128, 13312 for D = 64)
  *   off[4] = off[5] = 0
@@ -168,10 +170,13 @@ int mxattn_kv_tile(int D, int mode);
  *  clamp(round-half-even(2 (z - e) + beta), 0, 7), beta = 1.8678023 (the
  *  least-squares fit of this rule to the E2M1 rounding boundaries of
  *  codes 2..7).
- * In the MX modes the call first quantizes Q and K (blocks along D) and V
- * (blocks along keys) into the workspace, K~ and V~ as KV tile images in
- * matrix-core operand order, then runs the fused attention kernel.  In FP16 mode, V (and, for fp32 inputs, Q and K) is
- * first converted to fp16 in the workspace.
+ * In the MX modes the call first quantizes K (blocks along D) and V (blocks
+ * along keys) into the workspace as KV tile images in matrix-core operand
+ * order, then runs the fused attention kernel, which reads Q itself and
+ * quantizes each 32-element block of it (blocks along D, the mode's scale
+ * rule) as it loads it; the codes equal mxq_quantize's.  In FP16 mode, V
+ * (and, for fp32 inputs, Q and K) is first converted to fp16 in the
+ * workspace.
  */
 int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
                int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
@@ -181,16 +186,17 @@ int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
 /*
  * The two halves of mxattn_fwd, for callers that reuse prepared operands or
  * time the attention kernel alone.
- * mxattn_prepare: fills the workspace -- MX modes: Q~ (blocks along D) and
- * K~ / V~ (blocks along D / along keys) as KV tile images (see
- * mxattn_workspace_layout);
+ * mxattn_prepare: fills the workspace -- MX modes: K~ / V~ (blocks along D /
+ * along keys) as KV tile images (see mxattn_workspace_layout; q is checked
+ * but not read);
  * FP16 mode: K and V^T as 16-bit tile images of 64 keys (K bf16 for bf16
  * inputs, else fp16; V fp16), and fp16 Q for fp32 inputs.
  * mxattn_fwd_prepared: the fused attention kernel alone, reading the
  * operands a previous mxattn_prepare with the same sizes, dtype and mode
- * left in the workspace (q is read directly only in FP16 mode with bf16
- * inputs; k is not read; both may be NULL otherwise).  Arguments as for
- * mxattn_fwd.  mxattn_fwd == mxattn_prepare followed by mxattn_fwd_prepared.
+ * left in the workspace, and q (quantized in the kernel in the MX modes,
+ * read directly in FP16 mode with bf16 inputs; only FP16 mode with fp32
+ * inputs does not read it, and then it may be NULL).  k is not read and may
+ * be NULL.  Arguments as for mxattn_fwd.  mxattn_fwd == mxattn_prepare followed by mxattn_fwd_prepared.
  */
 int mxattn_prepare(const void *q, const void *k, const void *v, int dtype,
                    int B, int Hq, int Hkv, int Sq, int Skv, int D, int mode,
@@ -207,6 +213,7 @@ int mxattn_fwd_prepared(const void *q, const void *k, int dtype, int B,
  * [nslots][skv_ld/2] and p_scales [nslots][skv_ld/32] receive, for every
  * key block a slot's row visits, its packed codes and E8M0 byte; blocks the
  * row never visits (beyond the causal diagonal tile) are left untouched.
+ * The kernel's Q~ (every row) is stored at off[0] / off[1] of the workspace.
  */
 int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
                     int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
@@ -232,10 +239,12 @@ int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
  * MX_ERR_UNSUPPORTED (FP16 mode and longer query blocks: mxattn_fwd); the
  * workspace holds mxattn_decode_workspace_bytes(...) bytes (the
  * mxattn_prepare layout followed by the per-split partial states).
+ * Q is quantized inside the split kernel (as in mxattn_fwd).
  * mxattn_decode_prepared runs the split and merge kernels on a workspace
- * that mxattn_prepare filled (q, k, v are not read: a quantized KV cache is
- * reused across calls).  mxattn_decode_dump also writes the P~ codes and
- * E8M0 bytes of selected rows (as mxattn_fwd_dump).
+ * that mxattn_prepare filled, for the queries q (k, v are not taken: a
+ * quantized KV cache is reused across calls; q must not be NULL).
+ * mxattn_decode_dump also writes the P~ codes and E8M0 bytes of selected
+ * rows, and the kernel's Q~, as mxattn_fwd_dump.
  * mxattn_decode_split returns MX_ERR_ARG, and the workspace size 0, for bad
  * arguments.
  */
@@ -246,9 +255,10 @@ int mxattn_decode(const void *q, const void *k, const void *v, int dtype,
                   int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                   int mode, float *o, void *workspace, size_t ws_bytes,
                   void *stream);
-int mxattn_decode_prepared(int dtype, int B, int Hq, int Hkv, int Sq, int Skv,
-                           int D, int causal, int mode, float *o,
-                           void *workspace, size_t ws_bytes, void *stream);
+int mxattn_decode_prepared(const void *q, int dtype, int B, int Hq, int Hkv,
+                           int Sq, int Skv, int D, int causal, int mode,
+                           float *o, void *workspace, size_t ws_bytes,
+                           void *stream);
 int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D,
                        int causal, int mode, float *o, void *workspace,

@@ -71,7 +71,7 @@ def lib():
     L.mxattn_decode_workspace_bytes.argtypes = [ci] * 8
     L.mxattn_decode_workspace_bytes.restype = sz
     L.mxattn_decode.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P]
-    L.mxattn_decode_prepared.argtypes = [ci] * 9 + [P, P, sz, P]
+    L.mxattn_decode_prepared.argtypes = [P] + [ci] * 9 + [P, P, sz, P]
     L.mxattn_decode_dump.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P, P, P, P]
     L.mxgemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxgemm_workspace_bytes.restype = sz
@@ -211,8 +211,9 @@ def attn_fwd(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
 
 
 def attn_prepare(q, k, v, *, mode="uos_pnq", workspace=None, stream=None):
-    """First half of attn_fwd: quantize (or convert) the operands into the
-    workspace.  Returns the workspace."""
+    """First half of attn_fwd: quantize (or convert) the key/value operands
+    into the workspace (Q is quantized inside the attention kernels).
+    Returns the workspace."""
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     if workspace is None:
@@ -225,8 +226,10 @@ def attn_prepare(q, k, v, *, mode="uos_pnq", workspace=None, stream=None):
 
 def attn_fwd_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None,
                       stream=None):
-    """Second half of attn_fwd: the fused attention kernel on a workspace
-    filled by attn_prepare with the same shapes, dtype and mode."""
+    """Second half of attn_fwd: the fused attention kernel for the queries q
+    on a workspace filled by attn_prepare with the same shapes, dtype and
+    mode."""
+    assert q.is_cuda and q.is_contiguous()
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     if out is None:
@@ -241,7 +244,8 @@ def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None
                   stream=None):
     """attn_fwd plus the P~ codes / E8M0 bytes of the flattened query rows
     ``rows`` ((b*Hq + h)*Sq + i).  Returns (o, p_codes [n, skv_ld/2],
-    p_scales [n, skv_ld/32], workspace); unvisited key blocks stay zero."""
+    p_scales [n, skv_ld/32], workspace); unvisited key blocks stay zero.
+    The workspace also holds the kernel's Q~ (workspace_layout off[0:2])."""
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     rows = torch.as_tensor(rows, dtype=torch.int64)
@@ -304,14 +308,15 @@ def attn_decode(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=No
 
 def attn_decode_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None,
                          stream=None):
-    """attn_decode on a workspace filled by attn_prepare (shapes from q, k;
-    their data is not read)."""
+    """attn_decode of the queries q on a workspace filled by attn_prepare
+    (the key shape from k, whose data is not read)."""
+    assert q.is_cuda and q.is_contiguous()
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     if out is None:
         out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
     _check("mxattn_decode_prepared", lib().mxattn_decode_prepared(
-        _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), _mode(mode, MODES),
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), _mode(mode, MODES),
         _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
@@ -319,7 +324,8 @@ def attn_decode_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=N
 def attn_decode_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None,
                      stream=None):
     """attn_decode plus the P~ codes / E8M0 bytes of the flattened query
-    rows ``rows``; returns (o, p_codes, p_scales, workspace)."""
+    rows ``rows``; returns (o, p_codes, p_scales, workspace), the workspace
+    holding the kernel's Q~ as for attn_fwd_dump."""
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     rows = torch.as_tensor(rows, dtype=torch.int64)

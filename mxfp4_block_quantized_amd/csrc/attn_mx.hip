@@ -26,6 +26,10 @@
 //    queries) straight from the registers above, with one E8M0 byte per
 //    lane.  The accumulator keeps query l % 16 in every lane of a column,
 //    matching the softmax state.
+// Q is quantized in the kernel's prologue: each lane holds exactly one
+// 32-element block of its query row (the B operand layout), so it applies
+// the block rule of the mode to the raw bf16/fp32 elements it loads
+// (mx_block.h, the same code as the standalone quantizer).
 // The quantizer writes K~ and V~ as KV tile images already in these operand
 // orders, so a tile moves to LDS with contiguous 16-byte-per-lane direct
 // loads (global_load_lds) and every operand read is one ds_read per lane.
@@ -39,6 +43,7 @@
 // function of its log2 residual to the block's exponent, rounded and
 // clamped by v_cvt_pk_u8_f32 (efq_block_exp, tile_stats, p_tile).
 #include "internal.h"
+#include "mx_block.h"
 
 namespace mxk {
 namespace {
@@ -298,6 +303,23 @@ __device__ __forceinline__ void dump_tile(const MxAttnArgs& a, int64_t bh, int q
   }
 }
 
+// Q~ operand of one lane: query row `row` (global row index), d-block grp
+// (< D/32), quantized from the raw row; the dump variants also store it.
+template <int D, int UOS, int DUMP>
+__device__ __forceinline__ void quant_q_block(const MxAttnArgs& a, int64_t row, int grp, uint4& qop,
+                                              int& qsc) {
+  const int64_t e0 = row * D + grp * 32;
+  const void* src = a.q_bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.q) + e0)
+                             : static_cast<const void*>(static_cast<const float*>(a.q) + e0);
+  uint32_t X;
+  qop = quant_block32<UOS>(src, a.q_bf16 != 0, X);
+  qsc = static_cast<int>(X);
+  if (DUMP) {
+    *reinterpret_cast<uint4*>(a.qc + row * (D / 2) + grp * 16) = qop;
+    a.qs[row * (D / 32) + grp] = static_cast<uint8_t>(X);
+  }
+}
+
 // Interleave n matrix-core instructions with the vector work around them
 // (k VALU instructions after each), so that the transcendental unit runs
 // while the matrix core is busy.
@@ -403,21 +425,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   const int64_t bh = static_cast<int64_t>(b) * a.Hq + h;
   const int64_t bg = static_cast<int64_t>(b) * a.Hkv + g;
 
-  // Q~ operands (B of S^T): query column `col`, d-block `grp`.
+  // Q~ operands (B of S^T): query column `col`, d-block `grp`, quantized
+  // here; rows past Sq (and d-blocks past D) are zero codes.
   uint4 qop[kQT];
   int qsc[kQT];
   int qrow[kQT];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     qrow[t] = qw0 + t * 16 + col;
-    const int64_t row = bh * a.Sq + qrow[t];  // rows past Sq land in zeroed padding
-    if (grp < DC) {
-      qop[t] = *reinterpret_cast<const uint4*>(a.qc + row * (D / 2) + grp * 16);
-      qsc[t] = a.qs[row * DC + grp];
-    } else {
-      qop[t] = make_uint4(0, 0, 0, 0);
-      qsc[t] = 127;
-    }
+    qop[t] = make_uint4(0, 0, 0, 0);
+    qsc[t] = 127;
+    if (grp < DC && qrow[t] < a.Sq)
+      quant_q_block<D, UOS, DUMP>(a, bh * a.Sq + qrow[t], grp, qop[t], qsc[t]);
   }
 
   WaveState<D> w;
@@ -594,9 +613,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   uint4 qop = make_uint4(0, 0, 0, 0);
   int qsc = 127;
   if (cvalid && grp < DC) {
-    const int64_t row = bh * a.Sq + qi;
-    qop = *reinterpret_cast<const uint4*>(a.qc + row * (D / 2) + grp * 16);
-    qsc = a.qs[row * DC + grp];
+    // every split of a group quantizes the same rows; split 0 dumps them
+    if (DUMP && sp == 0)
+      quant_q_block<D, UOS, 1>(a, bh * a.Sq + qi, grp, qop, qsc);
+    else
+      quant_q_block<D, UOS, 0>(a, bh * a.Sq + qi, grp, qop, qsc);
   }
   const int klim = (cvalid && a.causal) ? qi + (a.Skv - a.Sq) : a.Skv - 1;
   const int qrow = cvalid ? qi : a.Sq;  // rows >= Sq are never dumped

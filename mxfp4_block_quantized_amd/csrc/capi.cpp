@@ -103,10 +103,8 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
     }
     return MX_OK;
   }
+  // MX modes: Q is quantized inside the attention kernels
   const int uos = (mode == MXATTN_OCP) ? 0 : 1;
-  e = mxk::launch_quant_rows(q, nq, nq + static_cast<int64_t>(mxk::kMxQTile) * D, dt, uos,
-                             w + L.off[0], w + L.off[1], s);
-  if (e != hipSuccess) return MX_ERR_HIP;
   e = mxk::launch_quant_kv_images(k, v, static_cast<int64_t>(B) * Hkv, Skv, D, dt, uos,
                                   w + L.off[2], s);
   return to_status(e);
@@ -135,7 +133,11 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
     return to_status(mxk::launch_attn_f16(a, s));
   }
   mxk::MxAttnArgs a{};
-  a.qc = w + L.off[0]; a.qs = w + L.off[1];
+  a.q = q;
+  a.q_bf16 = dtype == MX_BF16;
+  // written only by the dump variant, whose workspace is writable
+  a.qc = const_cast<uint8_t*>(w + L.off[0]);
+  a.qs = const_cast<uint8_t*>(w + L.off[1]);
   a.img = w + L.off[2];
   a.o = o;
   a.row_slot = row_slot;
@@ -224,7 +226,7 @@ int decode_common(const void* q, const void* k, const void* v, int dtype, int B,
                   uint8_t* p_scales, bool prepare, bool dump, void* stream) {
   int st = check_decode_shape(dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode);
   if (st != MX_OK) return st;
-  if (prepare && (!q || !k || !v)) return MX_ERR_ARG;
+  if (!q || (prepare && (!k || !v))) return MX_ERR_ARG;
   if (!o) return MX_ERR_ARG;
   if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)) ||
       !aligned(o, 16))
@@ -241,6 +243,8 @@ int decode_common(const void* q, const void* k, const void* v, int dtype, int B,
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
   mxk::MxDecodeArgs d{};
+  d.at.q = q;
+  d.at.q_bf16 = dtype == MX_BF16;
   d.at.qc = w + dl.L.off[0];
   d.at.qs = w + dl.L.off[1];
   d.at.img = w + dl.L.off[2];
@@ -365,7 +369,8 @@ int mxattn_fwd_prepared(const void* q, const void* k, int dtype, int B, int Hq, 
   int st = check_attn_call(q, k, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode,
                            workspace, ws_bytes, false, false, &L);
   if (st != MX_OK) return st;
-  if (mode == MXATTN_FP16 && dtype == MX_BF16 && !q) return MX_ERR_ARG;  // read directly
+  // q is read directly (FP16 mode with bf16 input) or quantized in the kernel (MX modes)
+  if (!q && (mode != MXATTN_FP16 || dtype == MX_BF16)) return MX_ERR_ARG;
   if (!o) return MX_ERR_ARG;
   if (!aligned(o, 16)) return MX_ERR_ALIGN;
   return run_attention(q, k, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, L, workspace,
@@ -431,9 +436,10 @@ int mxattn_decode(const void* q, const void* k, const void* v, int dtype, int B,
                        ws_bytes, nullptr, nullptr, nullptr, true, false, stream);
 }
 
-int mxattn_decode_prepared(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                           int mode, float* o, void* workspace, size_t ws_bytes, void* stream) {
-  return decode_common(nullptr, nullptr, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o,
+int mxattn_decode_prepared(const void* q, int dtype, int B, int Hq, int Hkv, int Sq, int Skv,
+                           int D, int causal, int mode, float* o, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  return decode_common(q, nullptr, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o,
                        workspace, ws_bytes, nullptr, nullptr, nullptr, false, false, stream);
 }
 

@@ -65,8 +65,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n
 
 // Operands of the MXFP4 attention kernel (all device pointers).
 struct MxAttnArgs {
-  const uint8_t* qc;   // [B*Hq*Sq (+pad)][D/2]
-  const uint8_t* qs;   // [B*Hq*Sq (+pad)][D/32]
+  const void* q;       // [B][Hq][Sq][D] bf16 (q_bf16) or fp32, quantized in the kernel
+  int q_bf16;
+  uint8_t* qc;         // dump only: the kernel's Q~ codes [B*Hq*Sq][D/2]
+  uint8_t* qs;         // dump only: the kernel's Q~ E8M0 bytes [B*Hq*Sq][D/32]
   const uint8_t* img;  // KV tile images [B*Hkv][skv_ld/128][img_bytes(D)]
   float* o;            // [B][Hq][Sq][D]
   const int32_t* row_slot;  // dump only: [B*Hq*Sq]

@@ -1,21 +1,7 @@
-// MXFP4 block quantizer and dequantizer kernels for gfx950.
-//
-// Format ("Quantization Error", section "Where the error comes from"; OCP
-// Microscaling Formats v1.0): 32 elements share an E8M0 scale 2^(X-127);
-// elements are E2M1 codes, rounded to nearest with ties to the even code and
-// saturating at 6.  Scale rules ("MXAttention ...", abstract): OCP puts the
-// block maximum into [4, 8) of the scaled domain, UOS into (3.625, 7.25]
-// (boundary Qmax = 7.25, inclusive).
-//
-// Both rules reduce to the exponent field Ef and mantissa field of the
-// block maximum |x|max:  X = max(0, Ef - 2 + up), with up = 1 only for UOS
-// and a mantissa above 1.8125 (fp32 field > 0x680000), i.e. exactly when
-// amax / 2^(Ef-129) > 7.25.  Zero and subnormal maxima give X = 0.
-//
-// Element rounding uses v_cvt_scalef32_pk_fp4_f32 (round to nearest even,
-// saturating, sign kept) on v = x * 2^-e, which is exact in fp32 for every
-// value that can round away from zero (fp32 denormals are kept).
+// MXFP4 block quantizer and dequantizer kernels for gfx950 (block rule and
+// rounding: mx_block.h).
 #include "internal.h"
+#include "mx_block.h"
 
 namespace mxk {
 namespace {
@@ -25,20 +11,6 @@ constexpr int kThreads = 256;
 // Streamed data (read or written once) goes through nontemporal vector
 // accesses, so that it does not displace reused lines in the caches.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Largest |x| of a block, as the fp32 bit pattern, to the E8M0 byte.
-template <int UOS>
-__device__ __forceinline__ uint32_t e8m0_of_amax(uint32_t abits) {
-  int ef = static_cast<int>(abits >> 23);
-  int up = UOS ? ((abits & 0x7FFFFFu) > 0x680000u ? 1 : 0) : 0;
-  int x = ef - 2 + up;
-  return x < 0 ? 0u : static_cast<uint32_t>(x);
-}
-
-// 2^-e for the E8M0 byte X (e = X - 127): always a normal fp32.
-__device__ __forceinline__ float inv_scale_of(uint32_t X) {
-  return __uint_as_float((254u - X) << 23);
-}
 
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   // quad_perm [1,0,3,2] then [2,3,0,1]
@@ -67,21 +39,6 @@ __device__ __forceinline__ void load8(const float* __restrict__ x, int64_t o,
   const uint4 a = make_uint4(av[0], av[1], av[2], av[3]), b = make_uint4(bv[0], bv[1], bv[2], bv[3]);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
-// Pack 8 fp32 elements (bit patterns) under inverse scale `inv` into one
-// dword of codes: element 2j -> low nibble of byte j.
-__device__ __forceinline__ uint32_t pack8(const uint32_t f[8], float inv) {
-  uint32_t r = 0;
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[0]) * inv,
-                                               __uint_as_float(f[1]) * inv, 1.0f, 0);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[2]) * inv,
-                                               __uint_as_float(f[3]) * inv, 1.0f, 1);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[4]) * inv,
-                                               __uint_as_float(f[5]) * inv, 1.0f, 2);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(f[6]) * inv,
-                                               __uint_as_float(f[7]) * inv, 1.0f, 3);
-  return r;
 }
 
 // Blocks along the contiguous axis.  Each lane owns 8 consecutive elements

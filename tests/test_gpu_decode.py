@@ -4,15 +4,16 @@ against the binary64 oracle run with the same split schedule.
 Bars as for mxattn_fwd: O max-abs <= 2e-3 and mean-abs <= 2e-4; the P~
 codes and E8M0 bytes read back through the dump entry point differ from the
 oracle's in at most 1e-4 of the elements; the dump variant and the prepared
-variant give the same O bits as the plain call.
+variant give the same O bits as the plain call; the Q~ the split kernel forms
+(stored by the dump variant) is bit-exact against the oracle's quantizer.
 """
 import functools
 
 import numpy as np
 import pytest
 
-from common import (FLIP_MAX, MAX_ABS, MEAN_ABS, MODE_IDS, flips, gpu, mxsynth, np_u8,
-                    to_torch)
+from common import (FLIP_MAX, MAX_ABS, MEAN_ABS, MODE_IDS, RULE_IDS, RULE_OF_MODE, flips, gpu,
+                    mxsynth, np_u8, to_torch)
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +34,13 @@ def run_decode(q, k, v, causal, mode, rows=None, label=""):
     o = mx.attn_decode(qt, kt, vt, causal=causal, mode=mode)
     o2, pc, ps, ws = mx.attn_decode_dump(qt, kt, vt, rows, causal=causal, mode=mode)
     assert torch.equal(o, o2), "dump variant changed O"
+    # the split kernel's own Q~ (stored by the dump variant) is the quantizer's
+    off, _ = mx.workspace_layout(B, Hq, Hkv, Sq, Skv, D,
+                                 "bf16" if q.dtype == np.uint16 else "f32", mode)
+    w = np_u8(ws)
+    rc, rs = oracle.quantize(q, RULE_IDS[RULE_OF_MODE[mode]])
+    assert np.array_equal(w[off[0]:off[0] + rc.size], rc)
+    assert np.array_equal(w[off[1]:off[1] + rs.size], rs)
     mx.attn_prepare(qt, kt, vt, mode=mode, workspace=ws)
     o3 = mx.attn_decode_prepared(qt, kt, ws, causal=causal, mode=mode)
     assert torch.equal(o, o3), "prepared variant changed O"
