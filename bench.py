@@ -42,7 +42,7 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "mxfp4_block_quantized_amd", "csrc", f)
-                for f in ("attn_mx.hip", "internal.h")]
+                for f in ("attn_mx.hip", "internal.h", "mx_block.h")]
 GEMM_SOURCES = [os.path.join(ROOT, "mxfp4_block_quantized_amd", "csrc", f)
                 for f in ("gemm_mx.hip", "internal.h")]
 
@@ -199,6 +199,7 @@ def bench_decode(torch, mx, reps=20, name="llm_decode"):
                      "tflops": flops / ms / 1e9}
         del ws
     res["algorithmic_bytes"] = alg
+    res["traffic"] = read_traffic(kernel_source_sha(ATTN_SOURCES), name, "attn_decode_kernel")
     return res
 
 
