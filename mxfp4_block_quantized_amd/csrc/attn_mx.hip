@@ -676,11 +676,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
 }
 
 // One wave per query row: O = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s,
-// M the largest m_s, splits in ascending order.  The lanes first take the
-// splits' (m, l) in parallel (wave max and sum), leaving each split's
-// weight in LDS; then each lane accumulates its channels over the splits,
-// eight splits' loads in flight at a time.
+// M the largest m_s, splits in ascending order.  The partial outputs of the
+// first kMergeChunk splits are loaded together with the splits' (m, l), so a
+// row costs one memory round trip when nsplit <= kMergeChunk; the lanes take
+// (m, l) in parallel (wave max and sum) and leave each split's weight in
+// LDS; each lane then accumulates its channels over the splits in order.
 constexpr int kMaxSplits = 1024;
+constexpr int kMergeChunk = 32;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -708,12 +710,29 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   const int col = (h % G) * a.Sq + i;
   const float* base = d.part + (bg * d.nsplit * 16 + col) * (D + 2);
   const int64_t stride = 16 * static_cast<int64_t>(D + 2);
-  float M = -INFINITY;
-  for (int s = lane; s < d.nsplit; s += 64) M = fmaxf(M, base[s * stride]);
+  constexpr int PER = D / 64;
+  const int n0 = min(d.nsplit, kMergeChunk);
+  float o0[kMergeChunk][PER];
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o0[u][k] = u < n0 ? base[u * stride + 2 + lane + 64 * k] : 0.0f;
+  float ms = -INFINITY, ls = 0.0f;
+  if (lane < d.nsplit) {
+    ms = base[lane * stride];
+    ls = base[lane * stride + 1];
+  }
+  float M = ms;
+  for (int s = lane + 64; s < d.nsplit; s += 64) M = fmaxf(M, base[s * stride]);
   M = wave_max(M);
   float L = 0.0f;
-  for (int s = lane; s < d.nsplit; s += 64) {
-    const float wgt = __builtin_amdgcn_exp2f((base[s * stride] - M) * sl2);  // 0 when empty
+  if (lane < d.nsplit) {
+    const float wgt = __builtin_amdgcn_exp2f((ms - M) * sl2);  // 0 when the split is empty
+    wts[wv][lane] = wgt;
+    L = fmaf(wgt, ls, L);
+  }
+  for (int s = lane + 64; s < d.nsplit; s += 64) {
+    const float wgt = __builtin_amdgcn_exp2f((base[s * stride] - M) * sl2);
     wts[wv][s] = wgt;
     L = fmaf(wgt, base[s * stride + 1], L);
   }
@@ -721,11 +740,17 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-  int s = 0;
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u) {
+    if (u < n0) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][u], o0[u][k], acc[k]);
+    }
+  }
+  int s = kMergeChunk;
   for (; s + 8 <= d.nsplit; s += 8) {
     float o[8][PER];
 #pragma unroll

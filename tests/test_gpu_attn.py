@@ -116,6 +116,17 @@ def test_d64_bf16(mode):
     run_case(q, k, v, True, mode, label="d64")
 
 
+@pytest.mark.parametrize("mode", MX_MODES)
+def test_fp32_d128(mode):
+    """fp32 inputs at D = 128 (the kernel quantizes fp32 query rows; ragged
+    query and key ends)."""
+    rng = np.random.default_rng(15)
+    q = (rng.standard_normal((1, 2, 190, 128)) * 1.4).astype(np.float32)
+    k = (rng.standard_normal((1, 2, 261, 128)) * 1.4).astype(np.float32)
+    v = rng.standard_normal((1, 2, 261, 128)).astype(np.float32)
+    run_case(q, k, v, False, mode, label="fp32_d128")
+
+
 @pytest.mark.parametrize("shape", [(1, 1), (5, 1), (1, 1000), (33, 33), (129, 129)])
 @pytest.mark.parametrize("mode", ["fp16", "uos_pnq", "ocp", "uos_efq"])
 def test_edge_lengths(shape, mode):

@@ -76,6 +76,19 @@ def test_small_decode(shape, mode):
     run_decode(q, k, v, causal, mode, label=f"{shape}")
 
 
+@pytest.mark.parametrize("mode", ["ocp", "uos_pnq"])
+def test_decode_fp32_inputs(mode):
+    """fp32 q, k, v: the split kernel quantizes fp32 query rows (the other
+    cases are bf16); values off the bf16 grid, scaled so some blocks need
+    the UOS step-up."""
+    rng = np.random.default_rng(53)
+    B, Hq, Hkv, Sq, Skv, D = 2, 8, 2, 3, 1500, 128
+    q = (rng.standard_normal((B, Hq, Sq, D)) * 1.7).astype(np.float32)
+    k = (rng.standard_normal((B, Hkv, Skv, D)) * 1.3).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Skv, D)).astype(np.float32)
+    run_decode(q, k, v, True, mode, label="fp32")
+
+
 def test_decode_single_key_and_v_ones():
     torch, mx = gpu()
     # one key: O is that key's quantized value row
