@@ -33,6 +33,8 @@
 //
 // Rows past M or N read the last valid row (their outputs are not stored).
 // K must be a positive multiple of 128.
+#include <atomic>
+
 #include "internal.h"
 
 namespace mxk {
@@ -130,18 +132,27 @@ struct LoadPtrs {
   const uint8_t* abase;
   const uint8_t* bbase;
   uint32_t aoff[4], boff[4];
-  int chunk;
+  uint32_t half_fix;  // 64 for lanes fetching the second 64 bytes of a row, else 0
 };
 
 // Direct loads of one stage (256 K; `off` = its byte offset along a row).
 // In a last stage with one K-step (`half`) the second 64 bytes of a row do
 // not exist: the lanes that would fetch them re-fetch the first half (data
 // that the one K-step does not read from their slots).
+// The stage's base addresses are wave-uniform: keeping them in scalar
+// registers lets each load take the scalar-base + 32-bit lane-offset form.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ void issue_stage(uint8_t* st, const LoadPtrs& lp, int64_t off, bool half,
                                             int wave) {
-  const uint8_t* ab = lp.abase + off;
-  const uint8_t* bb = lp.bbase + off;
-  const uint32_t fix = half && lp.chunk >= 4 ? 64u : 0u;
+  const uint8_t* ab = uniform_ptr(lp.abase + off);
+  const uint8_t* bb = uniform_ptr(lp.bbase + off);
+  const uint32_t fix = half ? lp.half_fix : 0u;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     __builtin_amdgcn_global_load_lds(ab + (lp.aoff[q] - fix), st + kStA + (wave + 8 * q) * 1024, 16, 0, 0);
@@ -223,14 +234,15 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, int64_t m0, int6
   const int64_t ldc = a.K / 2;
   const int rl = lane >> 3;
   // swz(8 (wave + 8 q) + rl) = (4 wave + rl / 2) & 7 does not depend on q
-  ts.lp.chunk = (lane & 7) ^ swz(8 * wave + rl);
+  const int chunk = (lane & 7) ^ swz(8 * wave + rl);
+  ts.lp.half_fix = chunk >= 4 ? 64u : 0u;
   ts.lp.abase = a.ac + m0 * ldc;
   ts.lp.bbase = a.bc + n0 * ldc;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 8 * (wave + 8 * q) + rl;
-    ts.lp.aoff[q] = static_cast<uint32_t>((min(m0 + r, a.M - 1) - m0) * ldc) + ts.lp.chunk * 16;
-    ts.lp.boff[q] = static_cast<uint32_t>((min(n0 + r, a.N - 1) - n0) * ldc) + ts.lp.chunk * 16;
+    ts.lp.aoff[q] = static_cast<uint32_t>((min(m0 + r, a.M - 1) - m0) * ldc) + chunk * 16;
+    ts.lp.boff[q] = static_cast<uint32_t>((min(n0 + r, a.N - 1) - n0) * ldc) + chunk * 16;
   }
   const int64_t ngrp = scale_groups(a.K);
   const int64_t last_ta = (a.M + 15) / 16 - 1, last_tb = (a.N + 15) / 16 - 1;
@@ -466,18 +478,20 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mx_kernel(GemmArgs a) {
 
 // Compute units of the current device (cached per device).
 hipError_t cu_count(int* out) {
-  static int cache[64] = {0};
+  // filled on first use; host threads may race to fill an entry, all with
+  // the same value
+  static std::atomic<int> cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  *out = cache[dev];
+  *out = n;
   return hipSuccess;
 }
 
