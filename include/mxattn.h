@@ -266,6 +266,46 @@ int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
                        uint8_t *p_codes, uint8_t *p_scales, void *stream);
 
 /*
+ * Sequences of different lengths in one padded batch: per entry, exactly the
+ * attention of mxattn_fwd / mxattn_decode on that entry's own rows and keys
+ * (the pages time their kernels over sequence lengths of 16K to 128K,
+ * "EFQ-Softmax", abstract, and fix no batching).  q [B][Hq][Sq][D] and
+ * k, v [B][Hkv][Skv][D] as for mxattn_fwd / mxattn_decode, Sq and Skv being
+ * the padded extents; seqlens_q and seqlens_k are DEVICE int32 arrays of B
+ * entries: batch entry b holds seqlens_q[b] query rows and seqlens_k[b]
+ * keys (values are clamped to [0, Sq] and [0, Skv]; the host does not read
+ * them).  Keys at or past seqlens_k[b] take no part in entry b: K~ and V~
+ * are quantized as if they were zero (so V~'s 32-key blocks end as at Skv),
+ * and they are masked.  Query rows at or past seqlens_q[b] are not written
+ * (their o rows keep their contents).  Causal queries are aligned to the
+ * end of the entry's keys (row i sees keys j <= i + seqlens_k[b] -
+ * seqlens_q[b]); an entry with no key, or a causal entry with more query
+ * rows than keys, writes no row.
+ *
+ * mxattn_fwd_varlen: the prefill form (per-entry query and key lengths); MX
+ * modes only (MXATTN_FP16 gives MX_ERR_UNSUPPORTED); Sq and Skv may differ
+ * also when causal.  Workspace as for mxattn_fwd.
+ * mxattn_decode_varlen: the short-query form (every entry has Sq query
+ * rows, seqlens_k[b] keys: a padded KV cache), split as mxattn_decode with
+ * the split size of the padded Skv; workspace as for mxattn_decode.
+ * Both: row_slot, p_codes, p_scales are all NULL (no dump) or all set (the
+ * P~ and Q~ dump of mxattn_fwd_dump, rows past an entry's length never
+ * dumped); a mix gives MX_ERR_ARG, as does a NULL seqlens pointer.
+ */
+int mxattn_fwd_varlen(const void *q, const void *k, const void *v, int dtype,
+                      int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                      const int32_t *seqlens_q, const int32_t *seqlens_k,
+                      int causal, int mode, float *o, void *workspace,
+                      size_t ws_bytes, const int32_t *row_slot,
+                      uint8_t *p_codes, uint8_t *p_scales, void *stream);
+int mxattn_decode_varlen(const void *q, const void *k, const void *v,
+                         int dtype, int B, int Hq, int Hkv, int Sq, int Skv,
+                         int D, const int32_t *seqlens_k, int causal,
+                         int mode, float *o, void *workspace, size_t ws_bytes,
+                         const int32_t *row_slot, uint8_t *p_codes,
+                         uint8_t *p_scales, void *stream);
+
+/*
  * W4A4 product of two MXFP4 operands ("MXCode: Vector Quantization for
  * MX-Native Inference at Scale", abstract: MX-native W4A4 operands; the
  * 32-element blocks and E8M0 scales of the OCP MX format):

@@ -30,7 +30,8 @@ EXPORTS = (
     "mxattn_workspace_bytes", "mxattn_workspace_layout", "mxattn_kv_tile",
     "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare", "mxattn_fwd_prepared", "mxgemm",
     "mxgemm_workspace_bytes", "mxattn_decode_split", "mxattn_decode_workspace_bytes",
-    "mxattn_decode", "mxattn_decode_prepared", "mxattn_decode_dump",
+    "mxattn_decode", "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
+    "mxattn_decode_varlen",
 )
 
 _lib = None
@@ -73,12 +74,15 @@ def lib():
     L.mxattn_decode.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P]
     L.mxattn_decode_prepared.argtypes = [P] + [ci] * 9 + [P, P, sz, P]
     L.mxattn_decode_dump.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P, P, P, P]
+    L.mxattn_fwd_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, P, ci, ci, P, P, sz, P, P, P, P]
+    L.mxattn_decode_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, ci, ci, P, P, sz, P, P, P, P]
     L.mxgemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxgemm_workspace_bytes.restype = sz
     for f in ("mxq_quantize", "mxq_quantize_t", "mxq_dequantize", "mxattn_workspace_layout",
               "mxattn_kv_tile", "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare",
               "mxattn_fwd_prepared", "mxgemm", "mxattn_decode_split", "mxattn_decode",
-              "mxattn_decode_prepared", "mxattn_decode_dump"):
+              "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
+              "mxattn_decode_varlen"):
         getattr(L, f).restype = ci
     _lib = L
     return L
@@ -383,3 +387,77 @@ def linear_w4a4(x: torch.Tensor, w_codes, w_scales, N: int, mode="uos",
     xc, xs = quantize(x.contiguous(), mode, stream=stream)
     return gemm(xc, xs, w_codes, w_scales, M, N, K, out_dtype=out_dtype, out=out,
                 workspace=workspace, stream=stream)
+
+
+# ------------------------------------------------ per-sequence lengths ----
+
+def _dump_buffers(q, rows, B, Hq, Sq, skv_ld):
+    rows = torch.as_tensor(rows, dtype=torch.int64)
+    n = rows.numel()
+    slot = torch.full((B * Hq * Sq,), -1, dtype=torch.int32)
+    slot[rows] = torch.arange(n, dtype=torch.int32)
+    slot = slot.to(q.device)
+    pc = torch.zeros((max(n, 1), skv_ld // 2), dtype=torch.uint8, device=q.device)
+    ps = torch.zeros((max(n, 1), skv_ld // 32), dtype=torch.uint8, device=q.device)
+    return n, slot, pc, ps
+
+
+def _lens(x, B, device):
+    t = torch.as_tensor(x, dtype=torch.int32)
+    assert t.numel() == B
+    return t.to(device).contiguous()
+
+
+def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_k, *, causal=False, mode="uos_pnq", out=None,
+                    workspace=None, rows=None, stream=None):
+    """Padded batch of sequences with their own lengths: entry b has
+    seqlens_q[b] query rows and seqlens_k[b] keys (q [B,Hq,Sq,D], k/v
+    [B,Hkv,Skv,D] padded).  Rows past an entry's length are not written
+    (``out`` defaults to zeros).  With ``rows`` (flattened query rows), also
+    returns the P~ dump: (o, p_codes, p_scales, workspace)."""
+    for t in (q, k, v):
+        assert t.is_cuda and t.is_contiguous()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    lq, lk = _lens(seqlens_q, B, q.device), _lens(seqlens_k, B, q.device)
+    if out is None:
+        out = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(q, k, mode)
+    slot = pc = ps = None
+    if rows is not None:
+        n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
+    _check("mxattn_fwd_varlen", lib().mxattn_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _ptr(lq), _ptr(lk),
+        int(bool(causal)), _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(),
+        _ptr(slot), _ptr(pc), _ptr(ps), _stream(stream)))
+    if rows is None:
+        return out
+    return out, pc[:n], ps[:n], workspace
+
+
+def attn_decode_varlen(q, k, v, seqlens_k, *, causal=False, mode="uos_pnq", out=None,
+                       workspace=None, rows=None, stream=None):
+    """Short-query attention over key splits for a padded KV cache whose
+    entry b holds seqlens_k[b] keys (q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D]).
+    Rows that see no key are not written (``out`` defaults to zeros).  With
+    ``rows``, also returns the P~ dump: (o, p_codes, p_scales, workspace)."""
+    for t in (q, k, v):
+        assert t.is_cuda and t.is_contiguous()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    lk = _lens(seqlens_k, B, q.device)
+    if out is None:
+        out = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_decode_workspace(q, k, mode)
+    slot = pc = ps = None
+    if rows is not None:
+        n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
+    _check("mxattn_decode_varlen", lib().mxattn_decode_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _ptr(lk),
+        int(bool(causal)), _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(),
+        _ptr(slot), _ptr(pc), _ptr(ps), _stream(stream)))
+    if rows is None:
+        return out
+    return out, pc[:n], ps[:n], workspace

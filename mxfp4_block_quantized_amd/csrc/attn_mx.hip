@@ -425,8 +425,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   const int64_t bh = static_cast<int64_t>(b) * a.Hq + h;
   const int64_t bg = static_cast<int64_t>(b) * a.Hkv + g;
 
+  // This sequence's query rows and keys: the padded extents, or its own
+  // lengths.  A sequence in which no row sees a key writes nothing.
+  int sq = a.Sq, skv = a.Skv;
+  if (a.lens_k) {
+    skv = min(max(a.lens_k[b], 0), a.Skv);
+    sq = min(max(a.lens_q[b], 0), a.Sq);
+    if (skv == 0 || (CAUSAL && sq > skv)) sq = 0;
+  }
+  if (q0 >= sq) return;  // whole workgroup, before any barrier
+  const int koff = CAUSAL ? skv - sq : 0;  // causal: row i sees keys j <= i + koff
+
   // Q~ operands (B of S^T): query column `col`, d-block `grp`, quantized
-  // here; rows past Sq (and d-blocks past D) are zero codes.
+  // here; rows past the sequence (and d-blocks past D) are zero codes.
   uint4 qop[kQT];
   int qsc[kQT];
   int qrow[kQT];
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     qrow[t] = qw0 + t * 16 + col;
     qop[t] = make_uint4(0, 0, 0, 0);
     qsc[t] = 127;
-    if (grp < DC && qrow[t] < a.Sq)
+    if (grp < DC && qrow[t] < sq)
       quant_q_block<D, UOS, DUMP>(a, bh * a.Sq + qrow[t], grp, qop[t], qsc[t]);
   }
 
@@ -450,19 +461,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     for (int n = 0; n < NT; ++n) w.oacc[t][n] = v4f{0, 0, 0, 0};
   }
 
-  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles of the key sequence
+  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
+  const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
   // tiles this workgroup visits: all, or up to its last causal diagonal tile
-  const int ntiles = CAUSAL ? min(nt, (q0 + kMxQTile - 1) / kKvTile + 1) : nt;
-  // Tiles [0, nmain) are unmasked for every wave; the rest are computed
-  // masked.  A wave computes only the tiles up to its own last one: the
-  // sequence end, or its causal diagonal tile (its 32 rows lie in one KV
-  // tile); a wave whose rows all lie past Sq computes nothing.
-  const bool mask_last = a.Skv % kKvTile != 0;
-  const int nmain = CAUSAL ? min(q0 / kKvTile, nt) : (mask_last ? nt - 1 : nt);
-  const int last_w = qw0 >= a.Sq ? -1 : (CAUSAL ? min(qw0 / kKvTile, nt - 1) : nt - 1);
+  const int ntiles = CAUSAL ? min(ntk, (q0 + kMxQTile - 1 + koff) / kKvTile + 1) : ntk;
+  // Tiles [0, nmain) are unmasked for every wave (whole tiles at or below
+  // the first row's limit); the rest are computed masked.  A wave dumps P~
+  // only up to its own last tile (the sequence end, or the causal limit of
+  // its last row); a wave whose rows all lie past the sequence dumps none.
+  const int nmain = CAUSAL ? min((q0 + koff + 1) / kKvTile, skv / kKvTile) : skv / kKvTile;
+  const int last_w = qw0 >= sq ? -1 : (CAUSAL ? min((qw0 + kQT * 16 - 1 + koff) / kKvTile, ntk - 1) : ntk - 1);
   int klim[kQT];
 #pragma unroll
-  for (int t = 0; t < kQT; ++t) klim[t] = CAUSAL ? min(a.Skv - 1, qrow[t]) : a.Skv - 1;
+  for (int t = 0; t < kQT; ++t) {
+    klim[t] = CAUSAL ? min(skv - 1, qrow[t] + koff) : skv - 1;
+    if (qrow[t] >= sq) qrow[t] = a.Sq;  // past the sequence: never dumped or stored
+  }
 
   const uint8_t* img = a.img + bg * nt * static_cast<int64_t>(IMG);
   const int nl = loads_per_tile<D>(wave);
@@ -619,15 +633,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
     else
       quant_q_block<D, UOS, 0>(a, bh * a.Sq + qi, grp, qop, qsc);
   }
-  const int klim = (cvalid && a.causal) ? qi + (a.Skv - a.Sq) : a.Skv - 1;
+  // this sequence's keys: the padded extent, or its own length
+  const int skv = a.lens_k ? min(max(a.lens_k[b], 0), a.Skv) : a.Skv;
+  // causal: end-aligned; a row with no visible key (klim < 0) stays empty
+  const int klim = (cvalid && a.causal) ? qi + (skv - a.Sq) : skv - 1;
   const int qrow = cvalid ? qi : a.Sq;  // rows >= Sq are never dumped
 
-  const int nt = static_cast<int>(a.skv_ld / kKvTile);
+  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
+  const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
   const int t_begin = sp * d.split_tiles;
-  const int t_end = min(t_begin + d.split_tiles, nt);
+  const int t_end = min(t_begin + d.split_tiles, ntk);
   // tiles needing the per-key mask: past the key end, or past the first
-  // causal limit (Skv - Sq)
-  const int first_masked = a.causal ? (a.Skv - a.Sq) / kKvTile : (a.Skv % kKvTile ? nt - 1 : nt);
+  // causal limit (skv - Sq)
+  const int first_masked = a.causal ? max(skv - a.Sq, 0) / kKvTile : skv / kKvTile;
 
   WaveState<D> w;
   w.m[0] = -INFINITY;
@@ -725,6 +743,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   float M = ms;
   for (int s = lane + 64; s < d.nsplit; s += 64) M = fmaxf(M, base[s * stride]);
   M = wave_max(M);
+  if (M == -INFINITY) return;  // no split saw a key: the row is left unwritten
   float L = 0.0f;
   if (lane < d.nsplit) {
     const float wgt = __builtin_amdgcn_exp2f((ms - M) * sl2);  // 0 when the split is empty

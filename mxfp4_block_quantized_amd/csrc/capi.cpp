@@ -88,7 +88,7 @@ int check_attn_call(const void* q, const void* k, const void* v, int dtype, int 
 // Operand preparation into the workspace (arguments already validated).
 int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
                 int Hkv, int Sq, int Skv, int D, int mode, const Layout& L, void* ws,
-                hipStream_t s) {
+                hipStream_t s, const int32_t* lens_k = nullptr) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   const mxk::Dtype dt = dtype == MX_BF16 ? mxk::Dtype::BF16 : mxk::Dtype::F32;
   const int64_t nq = static_cast<int64_t>(B) * Hq * Sq * D;
@@ -106,7 +106,7 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
   // MX modes: Q is quantized inside the attention kernels
   const int uos = (mode == MXATTN_OCP) ? 0 : 1;
   e = mxk::launch_quant_kv_images(k, v, static_cast<int64_t>(B) * Hkv, Skv, D, dt, uos,
-                                  w + L.off[2], s);
+                                  w + L.off[2], lens_k, Hkv, s);
   return to_status(e);
 }
 
@@ -114,7 +114,8 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
 int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int Sq,
                   int Skv, int D, int causal, int mode, float* o, const Layout& L,
                   const void* ws, const int32_t* row_slot, uint8_t* p_codes,
-                  uint8_t* p_scales, hipStream_t s) {
+                  uint8_t* p_scales, hipStream_t s, const int32_t* lens_q = nullptr,
+                  const int32_t* lens_k = nullptr) {
   const uint8_t* w = static_cast<const uint8_t*>(ws);
   if (mode == MXATTN_FP16) {
     mxk::F16AttnArgs a{};
@@ -135,6 +136,8 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
   mxk::MxAttnArgs a{};
   a.q = q;
   a.q_bf16 = dtype == MX_BF16;
+  a.lens_q = lens_q;
+  a.lens_k = lens_k;
   // written only by the dump variant, whose workspace is writable
   a.qc = const_cast<uint8_t*>(w + L.off[0]);
   a.qs = const_cast<uint8_t*>(w + L.off[1]);
@@ -223,7 +226,8 @@ DecodeLayout make_decode_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, 
 int decode_common(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
                   int Hkv, int Sq, int Skv, int D, int causal, int mode, float* o, void* ws,
                   size_t ws_bytes, const int32_t* row_slot, uint8_t* p_codes,
-                  uint8_t* p_scales, bool prepare, bool dump, void* stream) {
+                  uint8_t* p_scales, bool prepare, bool dump, void* stream,
+                  const int32_t* lens_k = nullptr) {
   int st = check_decode_shape(dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode);
   if (st != MX_OK) return st;
   if (!q || (prepare && (!k || !v))) return MX_ERR_ARG;
@@ -238,13 +242,14 @@ int decode_common(const void* q, const void* k, const void* v, int dtype, int B,
   if (!aligned(ws, 256)) return MX_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
   if (prepare) {
-    st = run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, dl.L, ws, s);
+    st = run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, dl.L, ws, s, lens_k);
     if (st != MX_OK) return st;
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
   mxk::MxDecodeArgs d{};
   d.at.q = q;
   d.at.q_bf16 = dtype == MX_BF16;
+  d.at.lens_k = lens_k;
   d.at.qc = w + dl.L.off[0];
   d.at.qs = w + dl.L.off[1];
   d.at.img = w + dl.L.off[2];
@@ -449,4 +454,58 @@ int mxattn_decode_dump(const void* q, const void* k, const void* v, int dtype, i
                        uint8_t* p_codes, uint8_t* p_scales, void* stream) {
   return decode_common(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, workspace,
                        ws_bytes, row_slot, p_codes, p_scales, true, true, stream);
+}
+
+// ---- per-sequence lengths ----
+
+namespace {
+// Dump pointers of the varlen entry points: all null (no dump) or all set.
+int check_optional_dump(const int32_t* row_slot, const uint8_t* p_codes, const uint8_t* p_scales,
+                        bool* dump) {
+  const int n = (row_slot != nullptr) + (p_codes != nullptr) + (p_scales != nullptr);
+  if (n != 0 && n != 3) return MX_ERR_ARG;
+  *dump = n == 3;
+  return MX_OK;
+}
+}  // namespace
+
+int mxattn_fwd_varlen(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                      int Hkv, int Sq, int Skv, int D, const int32_t* seqlens_q,
+                      const int32_t* seqlens_k, int causal, int mode, float* o,
+                      void* workspace, size_t ws_bytes, const int32_t* row_slot,
+                      uint8_t* p_codes, uint8_t* p_scales, void* stream) {
+  bool dump = false;
+  int st = check_optional_dump(row_slot, p_codes, p_scales, &dump);
+  if (st != MX_OK) return st;
+  if (causal != 0 && causal != 1) return MX_ERR_ARG;
+  Layout L;
+  // shape checks as for mxattn_fwd, except that causal queries are aligned
+  // to the end of each sequence's keys, so Sq and Skv may differ
+  st = check_attn_call(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode, workspace, ws_bytes,
+                       true, true, &L);
+  if (st != MX_OK) return st;
+  if (mode == MXATTN_FP16) return MX_ERR_UNSUPPORTED;
+  if (!o || !seqlens_q || !seqlens_k) return MX_ERR_ARG;
+  if (!aligned(o, 16) || !aligned(seqlens_q, 4) || !aligned(seqlens_k, 4)) return MX_ERR_ALIGN;
+  if (dump && (!aligned(p_codes, 16) || !aligned(row_slot, 4))) return MX_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  st = run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, L, workspace, s, seqlens_k);
+  if (st != MX_OK) return st;
+  return run_attention(q, k, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, L, workspace,
+                       dump ? row_slot : nullptr, dump ? p_codes : nullptr,
+                       dump ? p_scales : nullptr, s, seqlens_q, seqlens_k);
+}
+
+int mxattn_decode_varlen(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                         int Hkv, int Sq, int Skv, int D, const int32_t* seqlens_k, int causal,
+                         int mode, float* o, void* workspace, size_t ws_bytes,
+                         const int32_t* row_slot, uint8_t* p_codes, uint8_t* p_scales,
+                         void* stream) {
+  bool dump = false;
+  int st = check_optional_dump(row_slot, p_codes, p_scales, &dump);
+  if (st != MX_OK) return st;
+  if (!seqlens_k) return MX_ERR_ARG;
+  if (!aligned(seqlens_k, 4)) return MX_ERR_ALIGN;
+  return decode_common(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o, workspace,
+                       ws_bytes, row_slot, p_codes, p_scales, true, dump, stream, seqlens_k);
 }

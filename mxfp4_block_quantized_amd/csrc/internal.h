@@ -55,9 +55,11 @@ hipError_t launch_quant_cols(const void* x, int64_t batch, int64_t rows,
 // Quantize K [batch][rows][D] (blocks along D) and V [batch][rows][D]
 // (blocks along rows) into KV tile images [batch][ntiles][img_bytes(D)],
 // ntiles = ceil(rows / kKvTile); rows past the end are quantized as zeros.
+// lens (device, may be null): entry e of the batch holds lens[e / per_len]
+// valid rows (clamped to [0, rows]); its rows past that are zeros too.
 hipError_t launch_quant_kv_images(const void* k, const void* v, int64_t batch, int rows,
                                   int D, Dtype dt, int uos, uint8_t* img,
-                                  hipStream_t stream);
+                                  const int32_t* lens, int per_len, hipStream_t stream);
 
 // Dequantize n elements to fp32 (out_bf16 == 0) or bf16.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
@@ -67,6 +69,11 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n
 struct MxAttnArgs {
   const void* q;       // [B][Hq][Sq][D] bf16 (q_bf16) or fp32, quantized in the kernel
   int q_bf16;
+  // per-sequence lengths (device, may be null): batch entry b has lens_q[b]
+  // query rows (<= Sq) and lens_k[b] keys (<= Skv); causal queries are
+  // aligned to the end of the keys
+  const int32_t* lens_q;
+  const int32_t* lens_k;
   uint8_t* qc;         // dump only: the kernel's Q~ codes [B*Hq*Sq][D/2]
   uint8_t* qs;         // dump only: the kernel's Q~ E8M0 bytes [B*Hq*Sq][D/32]
   const uint8_t* img;  // KV tile images [B*Hkv][skv_ld/128][img_bytes(D)]

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 template <typename In, int UOS, int D>
 __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
     const In* __restrict__ x, int rows, int ntiles, int blocks_per_batch,
-    uint8_t* __restrict__ img) {
+    uint8_t* __restrict__ img, const int32_t* __restrict__ lens, int per_len) {
   constexpr int OPR = D / 8;  // octets per row
   constexpr int IMG = img_bytes(D);
   const int bgi = blockIdx.x / blocks_per_batch;
@@ -152,8 +152,10 @@ __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
   const int kr = o / OPR;
   if (kr >= ntiles * kKvTile) return;  // whole quads: OPR is a multiple of 4
   const int w = o % OPR;
+  // rows of this sequence: all, or its own length (rows past it are zeros)
+  const int valid = lens ? min(max(lens[bgi / per_len], 0), rows) : rows;
   uint32_t f[8];
-  if (kr < rows) {
+  if (kr < valid) {
     load8(x + (static_cast<int64_t>(bgi) * rows + kr) * D, w, f);
   } else {
 #pragma unroll
@@ -201,7 +203,7 @@ __device__ __forceinline__ uint32_t lane_bits<float>(const uint4& r, int ch) {
 template <typename In, int UOS, int D>
 __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
     const In* __restrict__ x, int rows, int ntiles, int blocks_per_batch,
-    uint8_t* __restrict__ img) {
+    uint8_t* __restrict__ img, const int32_t* __restrict__ lens, int per_len) {
   constexpr int CPT = 16 / static_cast<int>(sizeof(In));  // channels per thread
   constexpr int NCG = D / CPT;
   constexpr int NT = D / 16;
@@ -210,11 +212,12 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
   const int i = (blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
   const int cg = i % NCG, kb = i / NCG;
   if (kb >= ntiles * (kKvTile / kBlock)) return;
+  const int valid = lens ? min(max(lens[bgi / per_len], 0), rows) : rows;
   const In* src = x + (static_cast<int64_t>(bgi) * rows + kb * kBlock) * D + cg * CPT;
   uint4 r[kBlock];
 #pragma unroll
   for (int k = 0; k < kBlock; ++k)
-    if (kb * kBlock + k < rows) {
+    if (kb * kBlock + k < valid) {
       const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(k) * D));
       r[k] = make_uint4(t[0], t[1], t[2], t[3]);
     } else {
@@ -282,36 +285,40 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 
 template <typename In, int UOS, int D>
 hipError_t launch_kv_images_t(const void* k, const void* v, int64_t batch, int rows,
-                              int ntiles, uint8_t* img, hipStream_t stream) {
+                              int ntiles, uint8_t* img, const int32_t* lens, int per_len,
+                              hipStream_t stream) {
   const int kper = (ntiles * kKvTile * (D / 8) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((quant_kimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * kper)),
-                     dim3(kThreads), 0, stream, static_cast<const In*>(k), rows, ntiles, kper, img);
+                     dim3(kThreads), 0, stream, static_cast<const In*>(k), rows, ntiles, kper, img,
+                     lens, per_len);
   constexpr int CPT = 16 / static_cast<int>(sizeof(In));
   const int vper = (ntiles * (kKvTile / kBlock) * (D / CPT) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((quant_vimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * vper)),
-                     dim3(kThreads), 0, stream, static_cast<const In*>(v), rows, ntiles, vper, img);
+                     dim3(kThreads), 0, stream, static_cast<const In*>(v), rows, ntiles, vper, img,
+                     lens, per_len);
   return hipGetLastError();
 }
 
 template <typename In, int UOS>
 hipError_t launch_kv_images_d(const void* k, const void* v, int64_t batch, int rows, int D,
-                              int ntiles, uint8_t* img, hipStream_t stream) {
-  return D == 64 ? launch_kv_images_t<In, UOS, 64>(k, v, batch, rows, ntiles, img, stream)
-                 : launch_kv_images_t<In, UOS, 128>(k, v, batch, rows, ntiles, img, stream);
+                              int ntiles, uint8_t* img, const int32_t* lens, int per_len,
+                              hipStream_t stream) {
+  return D == 64 ? launch_kv_images_t<In, UOS, 64>(k, v, batch, rows, ntiles, img, lens, per_len, stream)
+                 : launch_kv_images_t<In, UOS, 128>(k, v, batch, rows, ntiles, img, lens, per_len, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quant_kv_images(const void* k, const void* v, int64_t batch, int rows,
                                   int D, Dtype dt, int uos, uint8_t* img,
-                                  hipStream_t stream) {
+                                  const int32_t* lens, int per_len, hipStream_t stream) {
   if (batch <= 0 || rows <= 0) return hipSuccess;
   const int ntiles = (rows + kKvTile - 1) / kKvTile;
   if (dt == Dtype::BF16)
-    return uos ? launch_kv_images_d<uint16_t, 1>(k, v, batch, rows, D, ntiles, img, stream)
-               : launch_kv_images_d<uint16_t, 0>(k, v, batch, rows, D, ntiles, img, stream);
-  return uos ? launch_kv_images_d<float, 1>(k, v, batch, rows, D, ntiles, img, stream)
-             : launch_kv_images_d<float, 0>(k, v, batch, rows, D, ntiles, img, stream);
+    return uos ? launch_kv_images_d<uint16_t, 1>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream)
+               : launch_kv_images_d<uint16_t, 0>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream);
+  return uos ? launch_kv_images_d<float, 1>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream)
+             : launch_kv_images_d<float, 0>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream);
 }
 
 hipError_t launch_quant_rows(const void* x, int64_t n, int64_t n_write, Dtype dt,

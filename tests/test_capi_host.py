@@ -135,3 +135,31 @@ def test_decode_rejects_bad_args():
     assert L.mxattn_decode_split(0, 8, 32768) == -1
     assert L.mxattn_decode_workspace_bytes(1, 8, 2, 1, 1000, 128, 1, 0) == 0
     assert L.mxattn_decode_workspace_bytes(1, 8, 2, 1, 1000, 128, 1, 3) > 0
+
+
+def test_varlen_rejects_bad_args():
+    L = mx.lib()
+    P = FAKE
+    big = 1 << 40
+    odd = ctypes.c_void_p((1 << 20) + 2)
+
+    def f(mode=3, lq=P, lk=P, slot=None, pc=None, ps=None, causal=1, Sq=200, Skv=300, D=128):
+        return L.mxattn_fwd_varlen(P, P, P, 1, 2, 4, 2, Sq, Skv, D, lq, lk, causal, mode, P, P,
+                                   big, slot, pc, ps, None)
+
+    def d(lk=P, slot=None, pc=None, ps=None, Sq=1, mode=3):
+        return L.mxattn_decode_varlen(P, P, P, 1, 2, 8, 2, Sq, 4000, 128, lk, 1, mode, P, P, big,
+                                      slot, pc, ps, None)
+
+    assert f(mode=0) == -2          # FP16 mode has no varlen form
+    assert f(D=80) == -2
+    assert f(lq=None) == -1 and f(lk=None) == -1
+    assert f(lk=odd) == -5
+    assert f(slot=P) == -1          # dump pointers: all or none
+    assert f(slot=P, pc=P) == -1
+    assert f(causal=2) == -1
+    assert d(lk=None) == -1
+    assert d(lk=odd) == -5
+    assert d(pc=P) == -1
+    assert d(Sq=5) == -2            # (Hq/Hkv) * Sq > 16
+    assert d(mode=0) == -2
