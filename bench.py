@@ -3,8 +3,8 @@
 
 A step is one mxattn_fwd call in UOS+PNQ mode on the video-DiT 14B
 self-attention shape (B=1, H=40, S=32760, D=128, bf16 inputs, non-causal):
-quantize Q, K (blocks along D) and V (blocks along keys), then the fused
-FP4 attention kernel.  Inputs are seeded synthetic tensors (mxsynth) already
+quantize K (blocks along D) and V (blocks along keys), then the fused FP4
+attention kernel, which quantizes Q (blocks along D) as it loads it.  Inputs are seeded synthetic tensors (mxsynth) already
 resident in HBM.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 value      = attention TFLOP/s of the whole step, 4*B*H*Sq*Skv*D / time
@@ -18,7 +18,11 @@ quantizer  = the standalone quantize / dequantize of the 8192 x 28672 bf16
 decode     = short-query attention over key splits (mxattn_decode_prepared,
              KV cache already quantized) on one LLM decode step (B=8, 32 query
              / 8 KV heads, 32768 cached keys), GB/s of the quantized KV cache
-             read against 8 TB/s;
+             read against 8 TB/s; decode.varlen the same cache with per-entry
+             lengths (mxattn_decode_varlen_prepared);
+prefill_varlen = the LLM prefill batch (B=4, causal) with per-entry prompt
+             lengths, one mxattn_fwd_varlen call per step, TFLOP/s of each
+             entry's own causal pairs against 10.1 PFLOP/s;
 gemm       = the W4A4 product (mxgemm) on the DiT feed-forward up-projection
              (32760 tokens x 5120 -> 13824, UOS operands, bf16 output), alone
              and with the activation quantization, against 10.1 PFLOP/s;
@@ -200,7 +204,72 @@ def bench_decode(torch, mx, reps=20, name="llm_decode"):
         del ws
     res["algorithmic_bytes"] = alg
     res["traffic"] = read_traffic(kernel_source_sha(ATTN_SOURCES), name, "attn_decode_kernel")
+
+    # the same cache with per-entry lengths (mxattn_decode_varlen_prepared)
+    vc = mxsynth.VARLEN_CONFIGS["llm_decode_varlen"]
+    lens = mxsynth.seq_lengths(vc["lens_seed"], B, vc["lo"], vc["hi"])
+    lk = torch.from_numpy(lens).cuda()
+    vimg = int(sum(Hkv * ((int(n) + 127) // 128) * ((8192 + 64 * D + 512 + 4 * D + 1023) // 1024 * 1024)
+                   for n in lens))
+    valg = vimg + B * Hq * Sq * D * 2 + B * Hq * Sq * D * 4
+    vflops = 4.0 * Hq * Sq * D * float(lens.sum())
+    mode = "uos_pnq"
+    ws = mx.alloc_decode_workspace(qt, kt, mode)
+    mx.attn_prepare_varlen(qt, kt, vt, lk, mode=mode, workspace=ws)
+    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        mx.attn_decode_varlen_prepared(qt, kt, ws, lk, causal=True, mode=mode, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        mx.attn_decode_varlen_prepared(qt, kt, ws, lk, causal=True, mode=mode, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    res["varlen"] = {"workload": f"llm_decode_varlen: the llm_decode cache with per-entry lengths "
+                                 f"uniform on [{vc['lo']}, {vc['hi']}] (seed {vc['lens_seed']}): "
+                                 f"{lens.tolist()}, {mode}",
+                     "ms": ms, "algorithmic_bytes": valg, "gbps": valg / ms / 1e6,
+                     "frac_hbm": valg / ms / 1e6 / HBM_PEAK_GBPS, "tflops": vflops / ms / 1e9}
+    del ws
     return res
+
+
+def bench_prefill_varlen(torch, mx, reps=5, name="llm_prefill_varlen"):
+    """The LLM prefill batch (B=4, 32/8 heads, D=128, causal) with per-entry
+    prompt lengths, one mxattn_fwd_varlen call (K/V quantize + attention)
+    per step; flops count only each entry's own causal pairs."""
+    import mxsynth
+    vc = mxsynth.VARLEN_CONFIGS[name]
+    c = mxsynth.CONFIGS[vc["base"]]
+    B, Hq, S, D = c["B"], c["Hq"], c["S"], c["D"]
+    log(f"[bench] prefill varlen: generating {vc['base']} inputs")
+    q, k, v = mxsynth.make_attn_inputs(vc["base"])
+    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
+    qt, kt, vt = to(q), to(k), to(v)
+    del q, k, v
+    lens = mxsynth.seq_lengths(vc["lens_seed"], B, vc["lo"], vc["hi"])
+    lt = torch.from_numpy(lens).cuda()
+    flops = sum(4.0 * Hq * D * int(n) * (int(n) + 1) / 2 for n in lens)
+    mode = "uos_pnq"
+    ws = mx.alloc_workspace(qt, kt, mode)
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        mx.attn_fwd_varlen(qt, kt, vt, lt, lt, causal=True, mode=mode, out=out, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        mx.attn_fwd_varlen(qt, kt, vt, lt, lt, causal=True, mode=mode, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"workload": f"{name}: {vc['base']} (B={B} Hq={Hq} Hkv={c['Hkv']} S<={S} D={D} causal, "
+                        f"bf16) with per-entry lengths uniform on [{vc['lo']}, {vc['hi']}] "
+                        f"(seed {vc['lens_seed']}): {lens.tolist()}, {mode}",
+            "ms": ms, "flops": flops, "tflops": flops / ms / 1e9,
+            "frac_fp4_peak": flops / ms / 1e9 / FP4_PEAK_TFLOPS}
 
 
 def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
@@ -273,6 +342,8 @@ def main():
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the per-sequence-length prefill section")
     ap.add_argument("--no-attention", action="store_true",
                     help="only the standalone quantizer and the GEMM (for profiling them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -375,6 +446,9 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(torch, mx)
         log(f"[bench] decode: {out['decode']}")
+    if not args.no_varlen:
+        out["prefill_varlen"] = bench_prefill_varlen(torch, mx)
+        log(f"[bench] prefill varlen: {out['prefill_varlen']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, c, args.workload)

@@ -291,6 +291,12 @@ int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
  * Both: row_slot, p_codes, p_scales are all NULL (no dump) or all set (the
  * P~ and Q~ dump of mxattn_fwd_dump, rows past an entry's length never
  * dumped); a mix gives MX_ERR_ARG, as does a NULL seqlens pointer.
+ * mxattn_prepare_varlen / mxattn_decode_varlen_prepared: the two halves of
+ * mxattn_decode_varlen, for a KV cache quantized once and read by many
+ * calls (as mxattn_prepare / mxattn_decode_prepared): the first writes the
+ * KV tile images with keys past seqlens_k[b] quantized as zero (MX modes;
+ * q is checked, not read); the second runs the split and merge kernels for
+ * the queries q with the same seqlens_k (k and v are not taken).
  */
 int mxattn_fwd_varlen(const void *q, const void *k, const void *v, int dtype,
                       int B, int Hq, int Hkv, int Sq, int Skv, int D,
@@ -298,6 +304,15 @@ int mxattn_fwd_varlen(const void *q, const void *k, const void *v, int dtype,
                       int causal, int mode, float *o, void *workspace,
                       size_t ws_bytes, const int32_t *row_slot,
                       uint8_t *p_codes, uint8_t *p_scales, void *stream);
+int mxattn_prepare_varlen(const void *q, const void *k, const void *v,
+                          int dtype, int B, int Hq, int Hkv, int Sq, int Skv,
+                          int D, const int32_t *seqlens_k, int mode,
+                          void *workspace, size_t ws_bytes, void *stream);
+int mxattn_decode_varlen_prepared(const void *q, int dtype, int B, int Hq,
+                                  int Hkv, int Sq, int Skv, int D,
+                                  const int32_t *seqlens_k, int causal,
+                                  int mode, float *o, void *workspace,
+                                  size_t ws_bytes, void *stream);
 int mxattn_decode_varlen(const void *q, const void *k, const void *v,
                          int dtype, int B, int Hq, int Hkv, int Sq, int Skv,
                          int D, const int32_t *seqlens_k, int causal,

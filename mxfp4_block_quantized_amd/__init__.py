@@ -31,7 +31,7 @@ EXPORTS = (
     "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare", "mxattn_fwd_prepared", "mxgemm",
     "mxgemm_workspace_bytes", "mxattn_decode_split", "mxattn_decode_workspace_bytes",
     "mxattn_decode", "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
-    "mxattn_decode_varlen",
+    "mxattn_decode_varlen", "mxattn_prepare_varlen", "mxattn_decode_varlen_prepared",
 )
 
 _lib = None
@@ -76,13 +76,15 @@ def lib():
     L.mxattn_decode_dump.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P, P, P, P]
     L.mxattn_fwd_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, P, ci, ci, P, P, sz, P, P, P, P]
     L.mxattn_decode_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, ci, ci, P, P, sz, P, P, P, P]
+    L.mxattn_prepare_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, ci, P, sz, P]
+    L.mxattn_decode_varlen_prepared.argtypes = [P] + [ci] * 7 + [P, ci, ci, P, P, sz, P]
     L.mxgemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxgemm_workspace_bytes.restype = sz
     for f in ("mxq_quantize", "mxq_quantize_t", "mxq_dequantize", "mxattn_workspace_layout",
               "mxattn_kv_tile", "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare",
               "mxattn_fwd_prepared", "mxgemm", "mxattn_decode_split", "mxattn_decode",
               "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
-              "mxattn_decode_varlen"):
+              "mxattn_decode_varlen", "mxattn_prepare_varlen", "mxattn_decode_varlen_prepared"):
         getattr(L, f).restype = ci
     _lib = L
     return L
@@ -461,3 +463,34 @@ def attn_decode_varlen(q, k, v, seqlens_k, *, causal=False, mode="uos_pnq", out=
     if rows is None:
         return out
     return out, pc[:n], ps[:n], workspace
+
+
+def attn_prepare_varlen(q, k, v, seqlens_k, *, mode="uos_pnq", workspace=None, stream=None):
+    """KV tile images of a padded KV cache whose entry b holds seqlens_k[b]
+    keys (keys past it quantized as zero), for attn_decode_varlen_prepared.
+    Returns the workspace (decode-sized unless one is given)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    lk = _lens(seqlens_k, B, q.device)
+    if workspace is None:
+        workspace = alloc_decode_workspace(q, k, mode)
+    _check("mxattn_prepare_varlen", lib().mxattn_prepare_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _ptr(lk),
+        _mode(mode, MODES), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def attn_decode_varlen_prepared(q, k, workspace, seqlens_k, *, causal=False, mode="uos_pnq",
+                                out=None, stream=None):
+    """attn_decode_varlen on a workspace filled by attn_prepare_varlen with
+    the same lengths (the key shape from k, whose data is not read)."""
+    assert q.is_cuda and q.is_contiguous()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    lk = seqlens_k if (torch.is_tensor(seqlens_k) and seqlens_k.is_cuda) else _lens(seqlens_k, B, q.device)
+    if out is None:
+        out = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    _check("mxattn_decode_varlen_prepared", lib().mxattn_decode_varlen_prepared(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _ptr(lk), int(bool(causal)),
+        _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

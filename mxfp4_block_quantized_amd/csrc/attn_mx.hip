@@ -405,18 +405,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   const int nqb = (a.Sq + kMxQTile - 1) / kMxQTile;
   // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin
   // over the 8 XCDs (each with its own L2), workgroup i to XCD i % 8.  Each
-  // XCD is given a contiguous run of the head-major (head, query tile) list,
-  // so a head's K~/V~ tile images are fetched from HBM by one XCD (two at a
-  // run boundary) instead of all eight.
+  // XCD is given a contiguous run of a list of (KV group, query head of the
+  // group, query tile), so a KV head's K~/V~ tile images are fetched from
+  // HBM by one XCD (two at a run boundary) instead of all eight.  With
+  // per-sequence lengths the KV groups gg = b * Hkv + g are listed in the
+  // order of (gg % 8, gg / 8): each XCD then holds groups of every batch
+  // entry, which keeps the XCDs equally loaded when the entries' lengths
+  // differ (with equal lengths the plain order is kept).
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int gi = (nwg >> 3) * xcd + min(xcd, nwg & 7) + (static_cast<int>(blockIdx.x) >> 3);
-  const int hb = gi / nqb;
+  const int G = a.Hq / a.Hkv;
+  const int per_group = G * nqb;
+  const int ngroups = a.B * a.Hkv;
+  const int pos = gi / per_group;  // position of the KV group in that order
+  const int rem = gi - pos * per_group;
+  int gg = pos;
+  if (a.lens_k) {
+    int res = 0, first = 0;
+    for (; res < 7; ++res) {
+      const int cnt = (ngroups - res + 7) >> 3;  // groups with gg % 8 == res
+      if (pos < first + cnt) break;
+      first += cnt;
+    }
+    gg = res + 8 * (pos - first);
+  }
+  const int b = gg / a.Hkv;
+  const int g = gg - b * a.Hkv;
+  const int h = g * G + rem / nqb;
   // causal: the longest query tiles of a head first
-  const int qb = CAUSAL ? nqb - 1 - gi % nqb : gi % nqb;
-  const int h = hb % a.Hq;
-  const int b = hb / a.Hq;
-  const int g = h / (a.Hq / a.Hkv);
+  const int qb = CAUSAL ? nqb - 1 - rem % nqb : rem % nqb;
   const int q0 = qb * kMxQTile;
   const int qw0 = q0 + wave * (kQT * 16);  // first query row of this wave
   const int col = lane & 15;   // query column within a 16-query tile

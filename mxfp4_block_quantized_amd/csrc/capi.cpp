@@ -496,6 +496,30 @@ int mxattn_fwd_varlen(const void* q, const void* k, const void* v, int dtype, in
                        dump ? p_scales : nullptr, s, seqlens_q, seqlens_k);
 }
 
+int mxattn_prepare_varlen(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                          int Hkv, int Sq, int Skv, int D, const int32_t* seqlens_k, int mode,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  Layout L;
+  int st = check_attn_call(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode, workspace, ws_bytes,
+                           true, true, &L);
+  if (st != MX_OK) return st;
+  if (mode == MXATTN_FP16) return MX_ERR_UNSUPPORTED;
+  if (!seqlens_k) return MX_ERR_ARG;
+  if (!aligned(seqlens_k, 4)) return MX_ERR_ALIGN;
+  return run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, L, workspace,
+                     as_stream(stream), seqlens_k);
+}
+
+int mxattn_decode_varlen_prepared(const void* q, int dtype, int B, int Hq, int Hkv, int Sq,
+                                  int Skv, int D, const int32_t* seqlens_k, int causal, int mode,
+                                  float* o, void* workspace, size_t ws_bytes, void* stream) {
+  if (!seqlens_k) return MX_ERR_ARG;
+  if (!aligned(seqlens_k, 4)) return MX_ERR_ALIGN;
+  return decode_common(q, nullptr, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, o,
+                       workspace, ws_bytes, nullptr, nullptr, nullptr, false, false, stream,
+                       seqlens_k);
+}
+
 int mxattn_decode_varlen(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
                          int Hkv, int Sq, int Skv, int D, const int32_t* seqlens_k, int causal,
                          int mode, float* o, void* workspace, size_t ws_bytes,

@@ -249,3 +249,19 @@ def make_gemm_inputs(name: str):
 DECODE_CONFIGS = {
     "llm_decode": dict(B=8, Hq=32, Hkv=8, Sq=1, Skv=32768, D=128, causal=True, seed=8),
 }
+
+
+# Padded batches of sequences with their own lengths: the LLM prefill batch
+# with per-entry prompt lengths (causal self-attention, query length = key
+# length) and the decode batch with per-entry KV-cache lengths.
+VARLEN_CONFIGS = {
+    "llm_prefill_varlen": dict(base="llm_prefill", lens_seed=10, lo=512, hi=8192),
+    "llm_decode_varlen": dict(base="llm_decode", lens_seed=11, lo=1024, hi=32768),
+}
+
+
+def seq_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """Per-entry lengths of a padded batch: B integers uniform on [lo, hi]
+    (``rng.integers``), int32."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=B).astype(np.int32)

@@ -163,3 +163,9 @@ def test_varlen_rejects_bad_args():
     assert d(pc=P) == -1
     assert d(Sq=5) == -2            # (Hq/Hkv) * Sq > 16
     assert d(mode=0) == -2
+    assert L.mxattn_prepare_varlen(P, P, P, 1, 2, 8, 2, 1, 4000, 128, None, 3, P, big, None) == -1
+    assert L.mxattn_prepare_varlen(P, P, P, 1, 2, 8, 2, 1, 4000, 128, P, 0, P, big, None) == -2
+    assert L.mxattn_decode_varlen_prepared(P, 1, 2, 8, 2, 1, 4000, 128, None, 1, 3, P, P, big,
+                                           None) == -1
+    assert L.mxattn_decode_varlen_prepared(P, 1, 2, 8, 2, 1, 4000, 128, odd, 1, 3, P, P, big,
+                                           None) == -5

@@ -142,6 +142,11 @@ def test_decode_varlen(case, mode):
     out = torch.full((B, Hq, Sq, D), SENTINEL, dtype=torch.float32, device="cuda")
     o, pc, ps, _ = mx.attn_decode_varlen(qt, kt, vt, lk, causal=causal, mode=mode, out=out,
                                          rows=rows)
+    # the prepared pair (KV cache quantized once) gives the same bits
+    ws2 = mx.attn_prepare_varlen(qt, kt, vt, lk, mode=mode)
+    out2 = torch.full((B, Hq, Sq, D), SENTINEL, dtype=torch.float32, device="cuda")
+    o2 = mx.attn_decode_varlen_prepared(qt, kt, ws2, lk, causal=causal, mode=mode, out=out2)
+    assert torch.equal(o2, o), "prepared varlen decode differs"
     o = o.double().cpu().numpy()
     pc, ps = np_u8(pc), np_u8(ps)
     for b in range(B):
