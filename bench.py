@@ -167,7 +167,7 @@ def bench_quantizer(torch, mx, reps=20):
     return res
 
 
-def bench_decode(torch, mx, reps=20, name="llm_decode"):
+def bench_decode(torch, mx, reps=20, name="llm_decode", varlen=True):
     import mxsynth
     c = mxsynth.DECODE_CONFIGS[name]
     B, Hq, Hkv, Sq, Skv, D = c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Skv"], c["D"]
@@ -204,6 +204,8 @@ def bench_decode(torch, mx, reps=20, name="llm_decode"):
         del ws
     res["algorithmic_bytes"] = alg
     res["traffic"] = read_traffic(kernel_source_sha(ATTN_SOURCES), name, "attn_decode_kernel")
+    if not varlen:
+        return res
 
     # the same cache with per-entry lengths (mxattn_decode_varlen_prepared)
     vc = mxsynth.VARLEN_CONFIGS["llm_decode_varlen"]
@@ -343,7 +345,7 @@ def main():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true",
-                    help="skip the per-sequence-length prefill section")
+                    help="skip the per-sequence-length sections (prefill, decode)")
     ap.add_argument("--no-attention", action="store_true",
                     help="only the standalone quantizer and the GEMM (for profiling them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -379,7 +381,7 @@ def main():
         if not args.no_gemm:
             res["gemm"] = bench_gemm(torch, mx, reps=3)
         if not args.no_decode:
-            res["decode"] = bench_decode(torch, mx, reps=3)
+            res["decode"] = bench_decode(torch, mx, reps=3, varlen=not args.no_varlen)
         print(json.dumps(res), flush=True)
         return
     c = dict(mxsynth.CONFIGS[args.workload])
@@ -444,7 +446,7 @@ def main():
         out["gemm"] = bench_gemm(torch, mx)
         log(f"[bench] gemm: {out['gemm']}")
     if not args.no_decode:
-        out["decode"] = bench_decode(torch, mx)
+        out["decode"] = bench_decode(torch, mx, varlen=not args.no_varlen)
         log(f"[bench] decode: {out['decode']}")
     if not args.no_varlen:
         out["prefill_varlen"] = bench_prefill_varlen(torch, mx)
