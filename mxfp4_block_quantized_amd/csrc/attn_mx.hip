@@ -445,10 +445,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
 
   // This sequence's query rows and keys: the padded extents, or its own
   // lengths.  A sequence in which no row sees a key writes nothing.
+  // (the lengths are read with vector loads; readfirstlane keeps them, and
+  // every bound derived from them, in scalar registers and uniform branches)
   int sq = a.Sq, skv = a.Skv;
   if (a.lens_k) {
-    skv = min(max(a.lens_k[b], 0), a.Skv);
-    sq = min(max(a.lens_q[b], 0), a.Sq);
+    skv = min(max(__builtin_amdgcn_readfirstlane(a.lens_k[b]), 0), a.Skv);
+    sq = min(max(__builtin_amdgcn_readfirstlane(a.lens_q[b]), 0), a.Sq);
     if (skv == 0 || (CAUSAL && sq > skv)) sq = 0;
   }
   if (q0 >= sq) return;  // whole workgroup, before any barrier
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
       quant_q_block<D, UOS, 0>(a, bh * a.Sq + qi, grp, qop, qsc);
   }
   // this sequence's keys: the padded extent, or its own length
-  const int skv = a.lens_k ? min(max(a.lens_k[b], 0), a.Skv) : a.Skv;
+  const int skv = a.lens_k ? min(max(__builtin_amdgcn_readfirstlane(a.lens_k[b]), 0), a.Skv) : a.Skv;
   // causal: end-aligned; a row with no visible key (klim < 0) stays empty
   const int klim = (cvalid && a.causal) ? qi + (skv - a.Sq) : skv - 1;
   const int qrow = cvalid ? qi : a.Sq;  // rows >= Sq are never dumped
