@@ -12,8 +12,6 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxattn.so")
 
 SOURCES = ["capi.cpp", "quant.hip", "attn_mx.hip", "attn_f16.hip", "gemm_mx.hip"]
-HEADERS = ["internal.h"]
-
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
