@@ -84,6 +84,8 @@ PREFILL = [
     (3, 4, 2, 300, 333, 128, [300, 1, 129], [333, 77, 129], True),
     (3, 4, 2, 300, 333, 128, [257, 40, 300], [1, 333, 200], False),
     (2, 2, 2, 200, 200, 64, [200, 130], [200, 170], True),
+    # empty entries: no query rows; no keys; a causal entry with more rows than keys
+    (4, 4, 2, 200, 260, 128, [0, 150, 200, 90], [100, 0, 260, 60], True),
 ]
 
 
@@ -102,10 +104,18 @@ def test_fwd_varlen(case, mode):
     o = o.double().cpu().numpy()
     pc, ps = np_u8(pc), np_u8(ps)
     for b in range(B):
+        if lk[b] == 0 or (causal and lq[b] > lk[b]):
+            # no row of this entry sees a key: nothing is written
+            assert np.all(o[b] == SENTINEL), "an entry without visible keys was written"
+            continue
         assert np.all(o[b][:, lq[b]:] == SENTINEL), "row past the query length written"
+        if lq[b] == 0:
+            continue
         compare_entry(o, pc, ps, b, pos[b], q, k, v, lq[b], lk[b], causal, mode, 0,
                       f"fwd_varlen {mode}")
-    check_q_tilde(ws, mx, q, lq, B, Hq, Hkv, Sq, Skv, D, mode)
+    # the kernel quantizes the rows of the entries that write rows
+    eff = [lq[b] if lk[b] > 0 and not (causal and lq[b] > lk[b]) else 0 for b in range(B)]
+    check_q_tilde(ws, mx, q, eff, B, Hq, Hkv, Sq, Skv, D, mode)
 
 
 def test_fwd_varlen_full_lengths_match_fwd():
@@ -124,6 +134,7 @@ DECODE = [
     (4, 8, 2, 2, 5000, 128, [5000, 1, 2000, 129], True),
     (3, 4, 4, 1, 3000, 64, [3000, 64, 1500], False),
     (2, 16, 2, 2, 2500, 128, [2400, 700], True),
+    (3, 8, 2, 1, 3000, 128, [0, 3000, 700], True),  # an empty cache: its rows stay unwritten
 ]
 
 
@@ -137,7 +148,8 @@ def test_decode_varlen(case, mode):
     qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
     split = mx.decode_split(B, Hkv, Skv)
     # rows that see a key: causal row i sees keys j <= i + lk - Sq
-    first = [max(Sq - l, 0) if causal else 0 for l in lk]
+    first = [min(max(Sq - l, 0), Sq) if causal else 0 for l in lk]
+    first = [Sq if l == 0 else f for f, l in zip(first, lk)]
     rows, pos = flat_rows(Hq, Sq, [Sq] * B, B)
     out = torch.full((B, Hq, Sq, D), SENTINEL, dtype=torch.float32, device="cuda")
     o, pc, ps, _ = mx.attn_decode_varlen(qt, kt, vt, lk, causal=causal, mode=mode, out=out,
@@ -152,6 +164,8 @@ def test_decode_varlen(case, mode):
     for b in range(B):
         f = first[b]
         assert np.all(o[b][:, :f] == SENTINEL), "a row with no visible key was written"
+        if f == Sq:
+            continue
         # the rows that see keys, as an oracle problem of Sq - f rows
         keep = np.array([h * Sq + i for h in range(Hq) for i in range(f, Sq)], dtype=np.int64)
         ref = oracle.attn_rows(q[b:b + 1, :, f:], k[b:b + 1, :, :lk[b]], v[b:b + 1, :, :lk[b]],
