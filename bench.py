@@ -63,6 +63,19 @@ def kernel_source_sha(sources=ATTN_SOURCES) -> str:
     return h.hexdigest()
 
 
+def warm(torch, fn, min_ms=200.0, max_calls=5000):
+    """Untimed calls of fn until min_ms of wall time has passed (at least
+    3): brings the GPU clock back up after host-side input generation."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or ((time.perf_counter() - t0) * 1e3 < min_ms and n < max_calls):
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def attn_flops(c) -> float:
     f = 4.0 * c["B"] * c["Hq"] * c["S"] * c["S"] * c["D"]
     return f / 2 if c["causal"] else f
@@ -119,8 +132,7 @@ def bench_quantizer(torch, mx, reps=20):
                        "along the last dim", "bytes_per_pass": q_bytes}
     # achievable streaming ceiling: a plain device-to-device copy of the same
     # tensor (read + write of n bf16 elements)
-    for _ in range(3):
-        y.copy_(xt.reshape(-1))
+    warm(torch, lambda: y.copy_(xt.reshape(-1)))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -133,8 +145,7 @@ def bench_quantizer(torch, mx, reps=20):
     res["d2d_copy_ceiling"] = {"ms": copy_ms, "gbps": copy_gbps,
                                "frac_hbm": copy_gbps / HBM_PEAK_GBPS}
     for rule in ("uos", "ocp"):
-        for _ in range(3):
-            mx.quantize(xt, rule, codes, scales)
+        warm(torch, lambda: mx.quantize(xt, rule, codes, scales))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -151,8 +162,7 @@ def bench_quantizer(torch, mx, reps=20):
                      "frac_hbm": q_bytes / ms / 1e6 / HBM_PEAK_GBPS,
                      "frac_copy_ceiling": q_bytes / ms / 1e6 / copy_gbps, "rel_frobenius": err}
         del xf
-    for _ in range(3):
-        mx.dequantize(codes, scales, out=y)
+    warm(torch, lambda: mx.dequantize(codes, scales, out=y))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -189,8 +199,7 @@ def bench_decode(torch, mx, reps=20, name="llm_decode", varlen=True):
         ws = mx.alloc_decode_workspace(qt, kt, mode)
         mx.attn_prepare(qt, kt, vt, mode=mode, workspace=ws)
         out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device="cuda")
-        for _ in range(3):
-            mx.attn_decode_prepared(qt, kt, ws, causal=True, mode=mode, out=out)
+        warm(torch, lambda: mx.attn_decode_prepared(qt, kt, ws, causal=True, mode=mode, out=out))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -219,8 +228,8 @@ def bench_decode(torch, mx, reps=20, name="llm_decode", varlen=True):
     ws = mx.alloc_decode_workspace(qt, kt, mode)
     mx.attn_prepare_varlen(qt, kt, vt, lk, mode=mode, workspace=ws)
     out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        mx.attn_decode_varlen_prepared(qt, kt, ws, lk, causal=True, mode=mode, out=out)
+    warm(torch, lambda: mx.attn_decode_varlen_prepared(qt, kt, ws, lk, causal=True, mode=mode,
+                                                        out=out))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -257,8 +266,8 @@ def bench_prefill_varlen(torch, mx, reps=5, name="llm_prefill_varlen"):
     mode = "uos_pnq"
     ws = mx.alloc_workspace(qt, kt, mode)
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        mx.attn_fwd_varlen(qt, kt, vt, lt, lt, causal=True, mode=mode, out=out, workspace=ws)
+    warm(torch, lambda: mx.attn_fwd_varlen(qt, kt, vt, lt, lt, causal=True, mode=mode, out=out,
+                                           workspace=ws))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -290,8 +299,7 @@ def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
     flops = 2.0 * M * N * K
 
     def timed(fn):
-        for _ in range(3):
-            fn()
+        warm(torch, fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -337,7 +345,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit14", choices=["dit14", "dit13", "llm_prefill"])
     ap.add_argument("--modes", default="uos_pnq,uos_efq,fp16,ocp,uos",
                     help="first mode is the headline; the rest run alongside")
