@@ -190,3 +190,63 @@ def test_decode_varlen_full_lengths_match_decode():
     a = mx.attn_decode(qt, kt, vt, causal=True, mode="uos_pnq")
     b = mx.attn_decode_varlen(qt, kt, vt, [Skv] * B, causal=True, mode="uos_pnq")
     assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------- full sizes ----
+
+@pytest.mark.slow
+def test_full_llm_prefill_varlen():
+    """The bench's llm_prefill_varlen call (the llm_prefill tensors, the
+    seeded per-entry lengths, causal, UOS+PNQ); 64 seeded rows per (entry,
+    head) against the oracle on the entry's own rows and keys.  The padding
+    holds the generator's data, which must not leak in."""
+    torch, mx = gpu()
+    vc = mxsynth.VARLEN_CONFIGS["llm_prefill_varlen"]
+    c = mxsynth.CONFIGS[vc["base"]]
+    B, Hq, S, D = c["B"], c["Hq"], c["S"], c["D"]
+    lens = [int(x) for x in mxsynth.seq_lengths(vc["lens_seed"], B, vc["lo"], vc["hi"])]
+    print(f"[case] llm_prefill_varlen lengths {lens}", flush=True)
+    q, k, v = mxsynth.make_attn_inputs(vc["base"])
+    out = mx.attn_fwd_varlen(to_torch(q), to_torch(k), to_torch(v), lens, lens, causal=True,
+                             mode="uos_pnq")
+    o = out.cpu().numpy()
+    rng = np.random.default_rng(vc["lens_seed"] + 100)
+    for b in range(B):
+        n = lens[b]
+        sel = np.concatenate([h * n + np.sort(rng.choice(n, 64, replace=False))
+                              for h in range(Hq)]).astype(np.int64)
+        ref = oracle.attn_rows(q[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n],
+                               causal=True, mode=oracle.MODE_UOS_PNQ, bc=128, rows=sel)
+        got = o[b][:, :n].reshape(-1, D)[sel].astype(np.float64)
+        err = np.abs(got - ref["o"])
+        print(f"[case] llm_prefill_varlen b={b} len={n}: max {err.max():.3e} mean {err.mean():.3e}",
+              flush=True)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+        assert np.all(o[b][:, n:] == 0.0), "row past the length written"
+
+
+@pytest.mark.slow
+def test_full_llm_decode_varlen():
+    """The bench's llm_decode_varlen call (the llm_decode cache with the
+    seeded per-entry lengths, UOS+PNQ, through the prepared pair); every
+    query row against the oracle with the library's split size."""
+    torch, mx = gpu()
+    vc = mxsynth.VARLEN_CONFIGS["llm_decode_varlen"]
+    c = mxsynth.DECODE_CONFIGS[vc["base"]]
+    B, Hq, Hkv, Sq, Skv, D = c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Skv"], c["D"]
+    lens = [int(x) for x in mxsynth.seq_lengths(vc["lens_seed"], B, vc["lo"], vc["hi"])]
+    print(f"[case] llm_decode_varlen lengths {lens}", flush=True)
+    q, k, v = mxsynth.llm_decode(c["seed"], B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, D=D)
+    qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
+    ws = mx.attn_prepare_varlen(qt, kt, vt, lens, mode="uos_pnq")
+    o = mx.attn_decode_varlen_prepared(qt, kt, ws, lens, causal=True, mode="uos_pnq").cpu().numpy()
+    split = mx.decode_split(B, Hkv, Skv)
+    for b in range(B):
+        n = lens[b]
+        ref = oracle.attn_rows(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], causal=True,
+                               mode=oracle.MODE_UOS_PNQ, bc=128,
+                               rows=np.arange(Hq * Sq, dtype=np.int64), split=split)
+        err = np.abs(o[b].reshape(-1, D).astype(np.float64) - ref["o"])
+        print(f"[case] llm_decode_varlen b={b} len={n}: max {err.max():.3e} mean {err.mean():.3e}",
+              flush=True)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
