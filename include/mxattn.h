@@ -290,7 +290,8 @@ int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
  * the split size of the padded Skv; workspace as for mxattn_decode.
  * Both: row_slot, p_codes, p_scales are all NULL (no dump) or all set (the
  * P~ and Q~ dump of mxattn_fwd_dump, rows past an entry's length never
- * dumped); a mix gives MX_ERR_ARG, as does a NULL seqlens pointer.
+ * dumped, nor the Q~ rows of an entry that writes no row); a mix gives
+ * MX_ERR_ARG, as does a NULL seqlens pointer.
  * mxattn_prepare_varlen / mxattn_decode_varlen_prepared: the two halves of
  * mxattn_decode_varlen, for a KV cache quantized once and read by many
  * calls (as mxattn_prepare / mxattn_decode_prepared): the first writes the

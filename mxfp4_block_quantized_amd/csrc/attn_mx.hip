@@ -623,7 +623,52 @@ __device__ __forceinline__ void load_tile_ops(TileOps<D>& t, const uint8_t* st, 
   }
 }
 
-template <int D, int UOS, int PNQ, int DUMP>
+// Splits of entry b: its keys in spans of split_tiles tiles (0 for an entry
+// with no key).
+__device__ __forceinline__ int entry_splits(const MxDecodeArgs& d, int b) {
+  const int span = d.split_tiles * kKvTile;
+  const int skv = min(max(d.at.lens_k[b], 0), d.at.Skv);
+  return (skv + span - 1) / span;
+}
+
+// Per-sequence lengths: the (entry, KV head, split) units that hold keys,
+// numbered consecutively (entry, then KV head, then split).  Consecutive
+// waves then take equal work whatever the lengths, and the round-robin of
+// workgroups over the XCDs spreads it evenly (numbering every split of the
+// padded extent instead puts split s of every group on the same XCD, and the
+// splits that hold keys are the low ones).  The wave walks the entries 64 at
+// a time (B <= kCompactMaxB), one entry per lane, and a wave-wide prefix sum
+// of their unit counts locates unit u.  Returns false when u is past the
+// last unit.  (A rolled loop: unrolled, its exits cost the tile loop
+// registers.)
+__device__ bool busy_unit(const MxDecodeArgs& d, int u, int& b, int& g, int& sp) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+#pragma unroll 1
+  for (int c0 = 0; c0 < d.at.B; c0 += 64) {
+    const int ns = c0 + lane < d.at.B ? entry_splits(d, c0 + lane) : 0;
+    int incl = ns * d.at.Hkv;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const int tot = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    if (u < base + tot) {
+      const int l = __builtin_ctzll(__ballot(base + incl > u));
+      const int n = __builtin_amdgcn_readfirstlane(__shfl(ns, l));
+      const int local = u - (base + __builtin_amdgcn_readfirstlane(__shfl(incl, l)) - n * d.at.Hkv);
+      b = c0 + l;
+      g = local / n;
+      sp = local - g * n;
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
+
+template <int D, int UOS, int PNQ, int DUMP, int COMPACT>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d, float sl2) {
   const MxAttnArgs& a = d.at;
   constexpr int IMG = img_bytes(D);
@@ -632,11 +677,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const int64_t nunits = static_cast<int64_t>(a.B) * a.Hkv * d.nsplit;
-  if (unit >= nunits) return;  // whole wave; no barriers in this kernel
-  const int sp = static_cast<int>(unit % d.nsplit);
-  const int64_t bg = unit / d.nsplit;
-  const int b = static_cast<int>(bg / a.Hkv), g = static_cast<int>(bg % a.Hkv);
+  int b, g, sp;
+  // (a compile-time choice: the scan left in the other form's code costs it
+  // registers in the tile loop)
+  if constexpr (COMPACT) {
+    if (!busy_unit(d, static_cast<int>(unit), b, g, sp)) return;  // whole wave; no barriers here
+  } else {
+    const int64_t nunits = static_cast<int64_t>(a.B) * a.Hkv * d.nsplit;
+    if (unit >= nunits) return;
+    sp = static_cast<int>(unit % d.nsplit);
+    b = static_cast<int>(unit / d.nsplit / a.Hkv);
+    g = static_cast<int>(unit / d.nsplit % a.Hkv);
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
+  sp = __builtin_amdgcn_readfirstlane(sp);
+  const int64_t bg = static_cast<int64_t>(b) * a.Hkv + g;
+  const int64_t slot = bg * d.nsplit + sp;  // partial-state slot
   const int G = a.Hq / a.Hkv;
   const int col = lane & 15, grp = lane >> 4;
 
@@ -699,7 +756,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   const float l = PNQ ? w.lacc[0][0] : xlane_sum4(w.lsum[0]);
   const bool empty = klim < t_begin * kKvTile;  // no visible key in this split
   if (cvalid) {  // unused columns are never merged
-    float* pr = d.part + (unit * 16 + col) * (D + 2);
+    float* pr = d.part + (slot * 16 + col) * (D + 2);
     if (grp == 0) {
       pr[0] = empty ? -INFINITY : w.m[0];
       pr[1] = empty ? 0.0f : l;
@@ -748,29 +805,31 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   const int col = (h % G) * a.Sq + i;
   const float* base = d.part + (bg * d.nsplit * 16 + col) * (D + 2);
   const int64_t stride = 16 * static_cast<int64_t>(D + 2);
+  // per-sequence lengths: only the splits that hold the entry's keys were written
+  const int ns = a.lens_k ? __builtin_amdgcn_readfirstlane(entry_splits(d, b)) : d.nsplit;
   constexpr int PER = D / 64;
-  const int n0 = min(d.nsplit, kMergeChunk);
+  const int n0 = min(ns, kMergeChunk);
   float o0[kMergeChunk][PER];
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u)
 #pragma unroll
     for (int k = 0; k < PER; ++k) o0[u][k] = u < n0 ? base[u * stride + 2 + lane + 64 * k] : 0.0f;
   float ms = -INFINITY, ls = 0.0f;
-  if (lane < d.nsplit) {
+  if (lane < ns) {
     ms = base[lane * stride];
     ls = base[lane * stride + 1];
   }
   float M = ms;
-  for (int s = lane + 64; s < d.nsplit; s += 64) M = fmaxf(M, base[s * stride]);
+  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, base[s * stride]);
   M = wave_max(M);
   if (M == -INFINITY) return;  // no split saw a key: the row is left unwritten
   float L = 0.0f;
-  if (lane < d.nsplit) {
+  if (lane < ns) {
     const float wgt = __builtin_amdgcn_exp2f((ms - M) * sl2);  // 0 when the split is empty
     wts[wv][lane] = wgt;
     L = fmaf(wgt, ls, L);
   }
-  for (int s = lane + 64; s < d.nsplit; s += 64) {
+  for (int s = lane + 64; s < ns; s += 64) {
     const float wgt = __builtin_amdgcn_exp2f((base[s * stride] - M) * sl2);
     wts[wv][s] = wgt;
     L = fmaf(wgt, base[s * stride + 1], L);
@@ -790,7 +849,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
     }
   }
   int s = kMergeChunk;
-  for (; s + 8 <= d.nsplit; s += 8) {
+  for (; s + 8 <= ns; s += 8) {
     float o[8][PER];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -801,7 +860,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
 #pragma unroll
       for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][s + u], o[u][k], acc[k]);
   }
-  for (; s < d.nsplit; ++s)
+  for (; s < ns; ++s)
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][s], base[s * stride + 2 + lane + 64 * k], acc[k]);
   const float inv = 1.0f / L;
@@ -809,11 +868,11 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   for (int k = 0; k < PER; ++k) a.o[row * D + lane + 64 * k] = acc[k] * inv;
 }
 
-template <int D, int UOS, int PNQ, int DUMP>
+template <int D, int UOS, int PNQ, int DUMP, int COMPACT>
 hipError_t launch_decode_t(const MxDecodeArgs& d, hipStream_t s) {
   const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
   const int64_t nunits = static_cast<int64_t>(d.at.B) * d.at.Hkv * d.nsplit;
-  hipLaunchKernelGGL((attn_decode_kernel<D, UOS, PNQ, DUMP>), dim3(static_cast<unsigned>((nunits + kWaves - 1) / kWaves)),
+  hipLaunchKernelGGL((attn_decode_kernel<D, UOS, PNQ, DUMP, COMPACT>), dim3(static_cast<unsigned>((nunits + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, d, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -825,7 +884,9 @@ hipError_t launch_decode_t(const MxDecodeArgs& d, hipStream_t s) {
 
 template <int D, int UOS, int PNQ>
 hipError_t decode_pick_dump(const MxDecodeArgs& d, hipStream_t s) {
-  return d.at.row_slot ? launch_decode_t<D, UOS, PNQ, 1>(d, s) : launch_decode_t<D, UOS, PNQ, 0>(d, s);
+  if (d.compact)
+    return d.at.row_slot ? launch_decode_t<D, UOS, PNQ, 1, 1>(d, s) : launch_decode_t<D, UOS, PNQ, 0, 1>(d, s);
+  return d.at.row_slot ? launch_decode_t<D, UOS, PNQ, 1, 0>(d, s) : launch_decode_t<D, UOS, PNQ, 0, 0>(d, s);
 }
 template <int D>
 hipError_t decode_pick_mode(const MxDecodeArgs& d, hipStream_t s) {

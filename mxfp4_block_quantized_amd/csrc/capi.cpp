@@ -264,6 +264,9 @@ int decode_common(const void* q, const void* k, const void* v, int dtype, int B,
   d.part = reinterpret_cast<float*>(w + dl.part);
   d.split_tiles = dl.split_tiles;
   d.nsplit = dl.nsplit;
+  // the busy splits numbered on the device (unit numbers are int there)
+  d.compact = lens_k && B <= mxk::kCompactMaxB &&
+              static_cast<int64_t>(B) * Hkv * dl.nsplit < (int64_t(1) << 31);
   return to_status(mxk::launch_attn_decode(d, s));
 }
 

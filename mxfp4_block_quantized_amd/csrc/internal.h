@@ -97,7 +97,14 @@ struct MxDecodeArgs {
   float* part;        // [B*Hkv*nsplit][16][D + 2]: m, l, unnormalized O per query slot
   int split_tiles;    // KV tiles (128 keys) per split
   int nsplit;
+  // per-sequence lengths only (at.lens_k set, B <= kCompactMaxB): waves take
+  // the splits that hold keys, numbered consecutively, instead of every
+  // (b, KV head, split) of the padded extent
+  int compact;
 };
+// Largest batch for which the short-query kernel numbers its busy splits
+// (each wave scans the B lengths).
+constexpr int kCompactMaxB = 256;
 hipError_t launch_attn_decode(const MxDecodeArgs& a, hipStream_t stream);
 
 // W4A4 product y[M][N] = a[M][K] b[N][K]^T of MXFP4 operands (codes
