@@ -182,6 +182,37 @@ def test_decode_varlen(case, mode):
         assert st["max_abs"] <= MAX_ABS and st["mean_abs"] <= MEAN_ABS, st
 
 
+@pytest.mark.parametrize("B", [130, 300])
+def test_decode_varlen_many_entries(B):
+    """Batches past one 64-entry step of the busy-split scan (130 entries:
+    three steps) and past the scan's limit of 256 entries (300: every split
+    of the padded extent numbered); lengths uniform on [0, Skv] with a fifth
+    of the entries empty, causal, two splits per full entry."""
+    torch, mx = gpu()
+    Hq, Hkv, Sq, Skv, D = 2, 1, 1, 700, 64
+    rng = np.random.default_rng(500 + B)
+    lk = [int(x) for x in rng.integers(0, Skv + 1, B)]
+    for b in rng.choice(B, B // 5, replace=False):
+        lk[b] = 0
+    print(f"[case] decode_varlen_many_entries B={B}", flush=True)
+    q, k, v = padded_inputs(600 + B, B, Hq, Hkv, Sq, Skv, D, [Sq] * B, lk)
+    qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
+    split = mx.decode_split(B, Hkv, Skv)
+    assert split < Skv  # entries hold up to two splits
+    out = torch.full((B, Hq, Sq, D), SENTINEL, dtype=torch.float32, device="cuda")
+    o = mx.attn_decode_varlen(qt, kt, vt, lk, causal=True, mode="uos_pnq", out=out)
+    o = o.double().cpu().numpy()
+    for b in range(B):
+        if lk[b] == 0:
+            assert np.all(o[b] == SENTINEL), "an entry with no key was written"
+            continue
+        ref = oracle.attn_rows(q[b:b + 1], k[b:b + 1, :, :lk[b]], v[b:b + 1, :, :lk[b]],
+                               causal=True, mode=oracle.MODE_UOS_PNQ, bc=128,
+                               rows=np.arange(Hq * Sq, dtype=np.int64), split=split)
+        err = np.abs(o[b].reshape(-1, D) - ref["o"])
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (b, lk[b], err.max())
+
+
 def test_decode_varlen_full_lengths_match_decode():
     torch, mx = gpu()
     B, Hq, Hkv, Sq, Skv, D = 3, 8, 2, 1, 4100, 128
