@@ -56,7 +56,12 @@ extern "C" {
 enum mx_status {
     MX_OK = 0,
     MX_ERR_ARG = -1,         /* null pointer, bad enum, bad size */
-    MX_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. D not 64/128) */
+    /* valid but not implemented: e.g. D not 64/128, or a size whose element
+       count or launch passes the library's limits (Q or K/V of more than
+       2^40 elements; any launch of 2^32 or more work items in one grid
+       dimension, e.g. mxq_quantize with n >= 2^36, mxq_dequantize with
+       n >= 2^35, K/V tile images of 2^35 or more padded elements) */
+    MX_ERR_UNSUPPORTED = -2,
     MX_ERR_WORKSPACE = -3,   /* workspace missing or too small */
     MX_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
     MX_ERR_ALIGN = -5        /* a device pointer is not 16-byte aligned */

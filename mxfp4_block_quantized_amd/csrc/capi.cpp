@@ -25,6 +25,27 @@ struct Layout {
   int64_t skv_ld;
 };
 
+// A dispatch's work-item count per grid dimension is a 32-bit value on this
+// runtime: shapes whose launches would exceed it are rejected up front.
+constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;
+
+// The attention launches (query-tile workgroups of 256 threads; operand
+// preparation: MX K tile images one thread per 8 elements of the 128-key
+// padded rows, the V images fewer; FP16 images one 256-thread workgroup per
+// 64-key tile, fp32 Q one thread per element).
+bool attn_grids_fit(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, int mode) {
+  const int64_t qt = mode == MXATTN_FP16 ? mxk::kQTile : mxk::kMxQTile;
+  if (static_cast<int64_t>(B) * Hq * ((Sq + qt - 1) / qt) * 256 > kMaxItems) return false;
+  if (mode == MXATTN_FP16) {
+    const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kF16KvTile - 1) / mxk::kF16KvTile;
+    if (static_cast<int64_t>(B) * Hkv * nt * 256 > kMaxItems) return false;
+    if (dtype == MX_F32 && static_cast<int64_t>(B) * Hq * Sq * D > kMaxItems) return false;
+    return true;
+  }
+  const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kKvTile - 1) / mxk::kKvTile;
+  return static_cast<int64_t>(B) * Hkv * nt * mxk::kKvTile * (D / 8) <= kMaxItems;
+}
+
 int check_attn_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                      int causal, int mode) {
   if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
@@ -38,6 +59,9 @@ int check_attn_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D,
   // element counts must fit the kernels' 64-bit indexing comfortably and
   // the per-head row count must fit int32 tiles
   if (static_cast<int64_t>(B) * Hq * Sq * D > (int64_t(1) << 40)) return MX_ERR_UNSUPPORTED;
+  // likewise K and V (this also keeps the workspace size far from overflow)
+  if (static_cast<int64_t>(B) * Hkv * Skv * D > (int64_t(1) << 40)) return MX_ERR_UNSUPPORTED;
+  if (!attn_grids_fit(B, Hq, Hkv, Sq, Skv, D, dtype, mode)) return MX_ERR_UNSUPPORTED;
   return MX_OK;
 }
 
@@ -201,6 +225,13 @@ int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D
   if (causal && Sq > Skv) return MX_ERR_UNSUPPORTED;
   if (B > 65535 || Hq > 65535) return MX_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * Hkv * Skv * D > (int64_t(1) << 40)) return MX_ERR_UNSUPPORTED;
+  // launches: the K/V images as for mxattn_fwd; one 64-lane wave per (b, KV
+  // head, split) and per query row of the merge
+  if (!attn_grids_fit(B, Hq, Hkv, Sq, Skv, D, dtype, mode)) return MX_ERR_UNSUPPORTED;
+  const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kKvTile - 1) / mxk::kKvTile;
+  const int64_t st = decode_split_tiles(B, Hkv, Skv);
+  if (static_cast<int64_t>(B) * Hkv * ((nt + st - 1) / st) * 64 > kMaxItems) return MX_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * Hq * Sq * 64 > kMaxItems) return MX_ERR_UNSUPPORTED;
   return MX_OK;
 }
 
@@ -292,6 +323,7 @@ int mxq_quantize(const void* x, int64_t n, int dtype, int mode, uint8_t* codes,
   if (dtype != MX_F32 && dtype != MX_BF16) return MX_ERR_ARG;
   if (mode != MXQ_OCP && mode != MXQ_UOS) return MX_ERR_ARG;
   if (n == 0) return MX_OK;
+  if (n / 16 + 256 > kMaxItems) return MX_ERR_UNSUPPORTED;  // one thread per 16 elements
   if (!x || !codes || !scales) return MX_ERR_ARG;
   if (!aligned(x, 16) || !aligned(codes, 16)) return MX_ERR_ALIGN;
   const mxk::Dtype dt = dtype == MX_BF16 ? mxk::Dtype::BF16 : mxk::Dtype::F32;
@@ -310,6 +342,7 @@ int mxq_quantize_t(const void* x, int64_t batch, int64_t rows, int64_t cols, int
   if (rows_pad < min_pad || rows_pad % mxk::kBlock != 0) return MX_ERR_ARG;
   if (batch == 0 || cols == 0 || rows_pad == 0) return MX_OK;
   if (batch > 65535 || rows_pad / 64 + 1 > 65535) return MX_ERR_UNSUPPORTED;
+  if ((cols + 127) / 128 * 256 > kMaxItems) return MX_ERR_UNSUPPORTED;  // 128-column tiles
   if (!x || !codes_t || !scales_t) return MX_ERR_ARG;
   if (!aligned(codes_t, 16)) return MX_ERR_ALIGN;
   if (!aligned(x, dtype == MX_F32 ? 4 : 2)) return MX_ERR_ALIGN;
@@ -323,6 +356,7 @@ int mxq_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, int o
   if (n < 0 || n % mxk::kBlock != 0) return MX_ERR_ARG;
   if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
   if (n == 0) return MX_OK;
+  if (n / 8 + 256 > kMaxItems) return MX_ERR_UNSUPPORTED;  // one thread per 8 elements
   if (!codes || !scales || !y) return MX_ERR_ARG;
   if (!aligned(codes, 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
   return to_status(mxk::launch_dequant(codes, scales, n, out_dtype == MX_BF16, y,

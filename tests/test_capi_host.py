@@ -51,6 +51,9 @@ def test_quantize_rejects_bad_args():
     assert L.mxq_quantize_t(FAKE, 1, 64, 8, 1, 1, 32, FAKE, FAKE, None) == -1  # rows_pad < rows
     assert L.mxq_dequantize(FAKE, FAKE, 31, 0, FAKE, None) == -1
     assert L.mxq_dequantize(FAKE, FAKE, 64, 3, FAKE, None) == -1
+    # past one dispatch's 2^32 work items (one thread per 16 / 8 elements)
+    assert L.mxq_quantize(FAKE, 1 << 36, 1, 1, FAKE, FAKE, None) == -2
+    assert L.mxq_dequantize(FAKE, FAKE, 1 << 35, 0, FAKE, None) == -2
 
 
 def test_attention_rejects_bad_args():
@@ -91,6 +94,18 @@ def test_workspace_and_tile_queries():
     assert off64[3] == 13312
     with pytest.raises(mx.MxError):
         mx.workspace_layout(1, 2, 2, 64, 64, 128, "bf16", "fp16")
+    # K/V element count past 2^40 (its image size would overflow): rejected
+    # even when Q is small (Sq = 1)
+    assert L.mxattn_workspace_bytes(65535, 65535, 65535, 1, 1 << 20, 128, 1, 3) == 0
+    assert L.mxattn_workspace_bytes(1, 8, 8, 1, (1 << 31) - 1, 128, 1, 3) == 0
+    # launches whose work-item count would pass 2^32 in one grid dimension:
+    # query tiles (65535 x 65535 heads, one tile each), K images (2^35
+    # elements), fp32 Q of the FP16 mode (2^32 elements)
+    assert L.mxattn_workspace_bytes(65535, 65535, 1, 1, 128, 64, 1, 3) == 0
+    assert L.mxattn_workspace_bytes(1, 1, 1, 1, 1 << 28, 128, 1, 3) == 0
+    assert L.mxattn_workspace_bytes(1, 1, 1, 1, (1 << 28) - 128, 128, 1, 3) > 0
+    assert L.mxattn_workspace_bytes(1, 1, 1, 1 << 25, 128, 128, 0, 0) == 0
+    assert L.mxattn_workspace_bytes(1, 1, 1, 1 << 25, 128, 128, 1, 0) > 0
 
 
 def test_gemm_rejects_bad_args():
