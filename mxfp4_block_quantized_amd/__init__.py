@@ -116,17 +116,66 @@ def _mode(mode, table):
     return table[mode] if isinstance(mode, str) else int(mode)
 
 
+def _dev(t, name, dtype=None, numel=None):
+    """``t`` must be a contiguous GPU tensor (of ``dtype``, with at least
+    ``numel`` elements): the library reads and writes raw device memory."""
+    if not torch.is_tensor(t) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs {numel} elements, has {t.numel()}")
+    return t
+
+
+def _attn_shapes(q, k, v=None, *, k_data=True):
+    """(B, Hq, Hkv, Sq, Skv, D) of q [B,Hq,Sq,D] and k (and v) [B,Hkv,Skv,D],
+    one dtype throughout; ``k_data=False``: k gives the key shape only."""
+    _dev(q, "q")
+    _dtype_code(q)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D: [B, heads, rows, D]")
+    if k_data:
+        _dev(k, "k", q.dtype)
+    if v is not None:
+        _dev(v, "v", q.dtype)
+        if v.shape != k.shape:
+            raise ValueError(f"v {tuple(v.shape)} differs from k {tuple(k.shape)}")
+    B, Hq, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ in batch or D")
+    return B, Hq, k.shape[1], Sq, k.shape[2], D
+
+
+def _out(out, shape, device, zero=False):
+    """The fp32 output [B,Hq,Sq,D]: allocated, or the caller's, checked."""
+    if out is None:
+        return (torch.zeros if zero else torch.empty)(shape, dtype=torch.float32, device=device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out: expected shape {tuple(shape)}, got {tuple(out.shape)}")
+    return out
+
+
+def _ws(workspace):
+    return _dev(workspace, "workspace", torch.uint8)
+
+
 # ------------------------------------------------------------ quantizer ----
 
 def quantize(x: torch.Tensor, mode="uos", codes=None, scales=None, stream=None):
     """Blocks of 32 along the flattened contiguous axis of ``x`` (fp32 or
     bf16, numel % 32 == 0).  Returns (codes uint8[n/2], scales uint8[n/32])."""
-    assert x.is_cuda and x.is_contiguous()
+    _dev(x, "x")
     n = x.numel()
     if codes is None:
         codes = torch.empty(n // 2, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(n // 32, dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes", torch.uint8, n // 2)
+    _dev(scales, "scales", torch.uint8, n // 32)
     _check("mxq_quantize", lib().mxq_quantize(_ptr(x), n, _dtype_code(x), _mode(mode, RULES),
                                               _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
@@ -136,7 +185,9 @@ def quantize_t(x: torch.Tensor, mode="uos", rows_pad: int = 0, stream=None):
     """Blocks of 32 along the rows of ``x`` [batch, rows, cols] (or [rows,
     cols]); returns transposed (codes [batch, cols, rows_pad/2], scales
     [batch, cols, rows_pad/32])."""
-    assert x.is_cuda and x.is_contiguous()
+    _dev(x, "x")
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [rows, cols] or [batch, rows, cols]")
     x3 = x.unsqueeze(0) if x.dim() == 2 else x
     batch, rows, cols = x3.shape
     rp = rows_pad or (rows + 31) // 32 * 32
@@ -153,9 +204,12 @@ def quantize_t(x: torch.Tensor, mode="uos", rows_pad: int = 0, stream=None):
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32,
                out=None, stream=None):
     """Values of packed codes under their E8M0 bytes, as fp32 or bf16."""
+    _dev(codes, "codes", torch.uint8)
     n = codes.numel() * 2
+    _dev(scales, "scales", torch.uint8, n // 32)
     if out is None:
         out = torch.empty(n, dtype=out_dtype, device=codes.device)
+    _dev(out, "out", None, n)
     _check("mxq_dequantize", lib().mxq_dequantize(_ptr(codes), _ptr(scales), n,
                                                   _dtype_code(out), _ptr(out), _stream(stream)))
     return out
@@ -189,8 +243,7 @@ def workspace_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode):
 
 
 def alloc_workspace(q, k, mode):
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, k_data=False)
     nb = workspace_bytes(B, Hq, Hkv, Sq, Skv, D, q.dtype, mode)
     if nb == 0:
         raise ValueError("invalid attention shape")
@@ -202,14 +255,11 @@ def attn_fwd(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
              stream=None):
     """O = softmax(q k^T / sqrt(D)) v in the given mode; fp32 output.
     q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D]; fp32 or bf16, contiguous, on the GPU."""
-    for t in (q, k, v):
-        assert t.is_cuda and t.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
+    out = _out(out, (B, Hq, Sq, D), q.device)
     if workspace is None:
         workspace = alloc_workspace(q, k, mode)
+    _ws(workspace)
     _check("mxattn_fwd", lib().mxattn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -220,10 +270,10 @@ def attn_prepare(q, k, v, *, mode="uos_pnq", workspace=None, stream=None):
     """First half of attn_fwd: quantize (or convert) the key/value operands
     into the workspace (Q is quantized inside the attention kernels).
     Returns the workspace."""
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
     if workspace is None:
         workspace = alloc_workspace(q, k, mode)
+    _ws(workspace)
     _check("mxattn_prepare", lib().mxattn_prepare(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _mode(mode, MODES),
         _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -235,11 +285,9 @@ def attn_fwd_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None
     """Second half of attn_fwd: the fused attention kernel for the queries q
     on a workspace filled by attn_prepare with the same shapes, dtype and
     mode."""
-    assert q.is_cuda and q.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, k_data=False)
+    out = _out(out, (B, Hq, Sq, D), q.device)
+    _ws(workspace)
     _check("mxattn_fwd_prepared", lib().mxattn_fwd_prepared(
         _ptr(q), _ptr(k), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -252,19 +300,12 @@ def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None
     ``rows`` ((b*Hq + h)*Sq + i).  Returns (o, p_codes [n, skv_ld/2],
     p_scales [n, skv_ld/32], workspace); unvisited key blocks stay zero.
     The workspace also holds the kernel's Q~ (workspace_layout off[0:2])."""
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    rows = torch.as_tensor(rows, dtype=torch.int64)
-    n = rows.numel()
-    skv_ld = (Skv + 127) // 128 * 128
-    slot = torch.full((B * Hq * Sq,), -1, dtype=torch.int32)
-    slot[rows] = torch.arange(n, dtype=torch.int32)
-    slot = slot.to(q.device)
-    pc = torch.zeros((max(n, 1), skv_ld // 2), dtype=torch.uint8, device=q.device)
-    ps = torch.zeros((max(n, 1), skv_ld // 32), dtype=torch.uint8, device=q.device)
-    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
+    n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
+    out = _out(None, (B, Hq, Sq, D), q.device)
     if workspace is None:
         workspace = alloc_workspace(q, k, mode)
+    _ws(workspace)
     _check("mxattn_fwd_dump", lib().mxattn_fwd_dump(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _ptr(slot),
@@ -284,8 +325,7 @@ def decode_split(B: int, Hkv: int, Skv: int) -> int:
 
 
 def alloc_decode_workspace(q, k, mode):
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, k_data=False)
     dt = _dtype_code(q)
     nb = lib().mxattn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dt, _mode(mode, MODES))
     if nb == 0:
@@ -298,14 +338,11 @@ def attn_decode(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=No
     """Short-query attention over key splits (fp32 output); causal queries
     are aligned to the end of the keys.  q [B,Hq,Sq,D] with (Hq/Hkv)*Sq <=
     16, k/v [B,Hkv,Skv,D]."""
-    for t in (q, k, v):
-        assert t.is_cuda and t.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
+    out = _out(out, (B, Hq, Sq, D), q.device)
     if workspace is None:
         workspace = alloc_decode_workspace(q, k, mode)
+    _ws(workspace)
     _check("mxattn_decode", lib().mxattn_decode(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -316,11 +353,9 @@ def attn_decode_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=N
                          stream=None):
     """attn_decode of the queries q on a workspace filled by attn_prepare
     (the key shape from k, whose data is not read)."""
-    assert q.is_cuda and q.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, k_data=False)
+    out = _out(out, (B, Hq, Sq, D), q.device)
+    _ws(workspace)
     _check("mxattn_decode_prepared", lib().mxattn_decode_prepared(
         _ptr(q), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)), _mode(mode, MODES),
         _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -332,19 +367,12 @@ def attn_decode_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=N
     """attn_decode plus the P~ codes / E8M0 bytes of the flattened query
     rows ``rows``; returns (o, p_codes, p_scales, workspace), the workspace
     holding the kernel's Q~ as for attn_fwd_dump."""
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    rows = torch.as_tensor(rows, dtype=torch.int64)
-    n = rows.numel()
-    skv_ld = (Skv + 127) // 128 * 128
-    slot = torch.full((B * Hq * Sq,), -1, dtype=torch.int32)
-    slot[rows] = torch.arange(n, dtype=torch.int32)
-    slot = slot.to(q.device)
-    pc = torch.zeros((max(n, 1), skv_ld // 2), dtype=torch.uint8, device=q.device)
-    ps = torch.zeros((max(n, 1), skv_ld // 32), dtype=torch.uint8, device=q.device)
-    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
+    n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
+    out = _out(None, (B, Hq, Sq, D), q.device)
     if workspace is None:
         workspace = alloc_decode_workspace(q, k, mode)
+    _ws(workspace)
     _check("mxattn_decode_dump", lib().mxattn_decode_dump(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _ptr(slot),
@@ -366,15 +394,16 @@ def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
          out_dtype=torch.float32, out=None, workspace=None, stream=None):
     """y [M, N] = deq(a) deq(b)^T for MXFP4 operands stored as ``quantize``
     writes row-major a [M, K] and b [N, K] (K % 128 == 0)."""
+    _dev(a_codes, "a_codes", torch.uint8, M * K // 2)
+    _dev(a_scales, "a_scales", torch.uint8, M * K // 32)
+    _dev(b_codes, "b_codes", torch.uint8, N * K // 2)
+    _dev(b_scales, "b_scales", torch.uint8, N * K // 32)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _dev(out, "out", None, M * N)
     if workspace is None:
         workspace = gemm_workspace(M, N, K, a_codes.device)
-    assert out.is_contiguous() and out.numel() == M * N
-    for t in (a_codes, a_scales, b_codes, b_scales):
-        assert t.is_cuda and t.is_contiguous() and t.dtype == torch.uint8
-    assert a_codes.numel() == M * K // 2 and b_codes.numel() == N * K // 2
-    assert a_scales.numel() == M * K // 32 and b_scales.numel() == N * K // 32
+    _ws(workspace)
     _check("mxgemm", lib().mxgemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
                                   M, N, K, _dtype_code(out), _ptr(out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)))
@@ -385,6 +414,8 @@ def linear_w4a4(x: torch.Tensor, w_codes, w_scales, N: int, mode="uos",
                 out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
     """x [M, K] (fp32 or bf16) quantized along K with ``mode``, times the
     MXFP4 weight (w_codes [N, K/2], w_scales [N, K/32]): y [M, N]."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
     M, K = x.shape
     xc, xs = quantize(x.contiguous(), mode, stream=stream)
     return gemm(xc, xs, w_codes, w_scales, M, N, K, out_dtype=out_dtype, out=out,
@@ -394,8 +425,11 @@ def linear_w4a4(x: torch.Tensor, w_codes, w_scales, N: int, mode="uos",
 # ------------------------------------------------ per-sequence lengths ----
 
 def _dump_buffers(q, rows, B, Hq, Sq, skv_ld):
-    rows = torch.as_tensor(rows, dtype=torch.int64)
+    """Slot table and P~ buffers of the flattened query rows ``rows``."""
+    rows = torch.as_tensor(rows, dtype=torch.int64).reshape(-1)
     n = rows.numel()
+    if n and (int(rows.min()) < 0 or int(rows.max()) >= B * Hq * Sq):
+        raise ValueError("rows: flattened query rows must lie in [0, B*Hq*Sq)")
     slot = torch.full((B * Hq * Sq,), -1, dtype=torch.int32)
     slot[rows] = torch.arange(n, dtype=torch.int32)
     slot = slot.to(q.device)
@@ -405,9 +439,15 @@ def _dump_buffers(q, rows, B, Hq, Sq, skv_ld):
 
 
 def _lens(x, B, device):
-    t = torch.as_tensor(x, dtype=torch.int32)
-    assert t.numel() == B
-    return t.to(device).contiguous()
+    """Per-entry lengths as a device int32 array of B entries (a GPU int32
+    tensor of that size is used as is)."""
+    if torch.is_tensor(x) and x.is_cuda and x.dtype == torch.int32 and x.is_contiguous():
+        t = x
+    else:
+        t = torch.as_tensor(x).to(dtype=torch.int32, device=device).contiguous()
+    if t.numel() != B:
+        raise ValueError(f"lengths: expected {B} entries, got {t.numel()}")
+    return t
 
 
 def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_k, *, causal=False, mode="uos_pnq", out=None,
@@ -417,15 +457,12 @@ def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_k, *, causal=False, mode="uos_pn
     [B,Hkv,Skv,D] padded).  Rows past an entry's length are not written
     (``out`` defaults to zeros).  With ``rows`` (flattened query rows), also
     returns the P~ dump: (o, p_codes, p_scales, workspace)."""
-    for t in (q, k, v):
-        assert t.is_cuda and t.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
     lq, lk = _lens(seqlens_q, B, q.device), _lens(seqlens_k, B, q.device)
-    if out is None:
-        out = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    out = _out(out, (B, Hq, Sq, D), q.device, zero=True)
     if workspace is None:
         workspace = alloc_workspace(q, k, mode)
+    _ws(workspace)
     slot = pc = ps = None
     if rows is not None:
         n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
@@ -444,15 +481,12 @@ def attn_decode_varlen(q, k, v, seqlens_k, *, causal=False, mode="uos_pnq", out=
     entry b holds seqlens_k[b] keys (q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D]).
     Rows that see no key are not written (``out`` defaults to zeros).  With
     ``rows``, also returns the P~ dump: (o, p_codes, p_scales, workspace)."""
-    for t in (q, k, v):
-        assert t.is_cuda and t.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
     lk = _lens(seqlens_k, B, q.device)
-    if out is None:
-        out = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    out = _out(out, (B, Hq, Sq, D), q.device, zero=True)
     if workspace is None:
         workspace = alloc_decode_workspace(q, k, mode)
+    _ws(workspace)
     slot = pc = ps = None
     if rows is not None:
         n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
@@ -469,11 +503,11 @@ def attn_prepare_varlen(q, k, v, seqlens_k, *, mode="uos_pnq", workspace=None, s
     """KV tile images of a padded KV cache whose entry b holds seqlens_k[b]
     keys (keys past it quantized as zero), for attn_decode_varlen_prepared.
     Returns the workspace (decode-sized unless one is given)."""
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
     lk = _lens(seqlens_k, B, q.device)
     if workspace is None:
         workspace = alloc_decode_workspace(q, k, mode)
+    _ws(workspace)
     _check("mxattn_prepare_varlen", lib().mxattn_prepare_varlen(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _ptr(lk),
         _mode(mode, MODES), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -484,12 +518,10 @@ def attn_decode_varlen_prepared(q, k, workspace, seqlens_k, *, causal=False, mod
                                 out=None, stream=None):
     """attn_decode_varlen on a workspace filled by attn_prepare_varlen with
     the same lengths (the key shape from k, whose data is not read)."""
-    assert q.is_cuda and q.is_contiguous()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    lk = seqlens_k if (torch.is_tensor(seqlens_k) and seqlens_k.is_cuda) else _lens(seqlens_k, B, q.device)
-    if out is None:
-        out = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, k_data=False)
+    lk = _lens(seqlens_k, B, q.device)
+    out = _out(out, (B, Hq, Sq, D), q.device, zero=True)
+    _ws(workspace)
     _check("mxattn_decode_varlen_prepared", lib().mxattn_decode_varlen_prepared(
         _ptr(q), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, _ptr(lk), int(bool(causal)),
         _mode(mode, MODES), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
