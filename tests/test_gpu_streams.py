@@ -1,8 +1,8 @@
 """The C ABI's stream argument: every call is enqueued on the stream it is
 given (a side stream, a graph-capturing stream), and the library neither
 allocates, synchronizes nor issues memsets, so the attention, short-query
-attention, W4A4 product and quantizer calls can be captured into one HIP
-graph and replayed.
+attention, W4A4 product, quantizer and per-sequence-length calls can be
+captured into one HIP graph and replayed.
 
 Checked: results on a side stream (inputs produced on that same stream just
 before the call) equal the default-stream results bit for bit; a captured
@@ -58,6 +58,14 @@ def test_graph_capture_and_replay():
     ws_g = mx.gemm_workspace(M, N, K)
     o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     od = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    # per-sequence lengths (device arrays read by the kernels at run time)
+    lq = torch.tensor([253], dtype=torch.int32, device="cuda")
+    lk = torch.tensor([260], dtype=torch.int32, device="cuda")
+    lk_d = torch.tensor([2500, 1333], dtype=torch.int32, device="cuda")
+    ws_v = mx.alloc_workspace(q, k, "uos_pnq")
+    ws_dv = mx.alloc_decode_workspace(qd, kd, "uos_efq")
+    ov = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    odv = torch.zeros(qd.shape, dtype=torch.float32, device="cuda")
     xc = torch.empty(M * K // 2, dtype=torch.uint8, device="cuda")
     xs = torch.empty(M * K // 32, dtype=torch.uint8, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -68,10 +76,15 @@ def test_graph_capture_and_replay():
                        stream=stream)
         mx.quantize(xt, "uos", xc, xs, stream=stream)
         mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=ws_g, stream=stream)
+        mx.attn_fwd_varlen(q, k, v, lq, lk, causal=True, mode="uos_pnq", out=ov,
+                           workspace=ws_v, stream=stream)
+        mx.attn_decode_varlen(qd, kd, vd, lk_d, causal=True, mode="uos_efq", out=odv,
+                              workspace=ws_dv, stream=stream)
 
+    outs = (o, od, xc, xs, y, ov, odv)
     work()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (o, od, xc, xs, y)]
+    ref = [t.clone() for t in outs]
 
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -84,10 +97,10 @@ def test_graph_capture_and_replay():
         work(stream=s)
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (o, od, xc, xs, y):
+        for t in outs:
             t.zero_()  # eager device work between the replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for got, want in zip((o, od, xc, xs, y), ref):
-            assert torch.equal(got, want), f"replay {rep}"
+        for i, (got, want) in enumerate(zip(outs, ref)):
+            assert torch.equal(got, want), f"replay {rep}, output {i}"
