@@ -118,6 +118,46 @@ def test_fwd_varlen(case, mode):
     check_q_tilde(ws, mx, q, eff, B, Hq, Hkv, Sq, Skv, D, mode)
 
 
+@pytest.mark.parametrize("mode", ["uos_pnq", "uos_efq"])
+def test_varlen_fp32_inputs(mode):
+    """fp32 inputs (NaN past each length): the kernels quantize fp32 query
+    rows in their prologue and the image quantizer fp32 keys and values
+    under the lengths; prefill (non-causal) and decode (causal)."""
+    torch, mx = gpu()
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 190, 261, 128
+    lq, lk = [190, 77], [261, 100]
+    rng = np.random.default_rng(33)
+    q = (rng.standard_normal((B, Hq, Sq, D)) * 1.4).astype(np.float32)
+    k = (rng.standard_normal((B, Hkv, Skv, D)) * 1.4).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Skv, D)).astype(np.float32)
+    for b in range(B):
+        q[b, :, lq[b]:] = np.nan
+        k[b, :, lk[b]:] = np.nan
+        v[b, :, lk[b]:] = np.nan
+    qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
+    rows, pos = flat_rows(Hq, Sq, lq, B)
+    out = torch.full((B, Hq, Sq, D), SENTINEL, dtype=torch.float32, device="cuda")
+    o, pc, ps, ws = mx.attn_fwd_varlen(qt, kt, vt, lq, lk, causal=False, mode=mode, out=out,
+                                       rows=rows)
+    o = o.double().cpu().numpy()
+    pc, ps = np_u8(pc), np_u8(ps)
+    for b in range(B):
+        assert np.all(o[b][:, lq[b]:] == SENTINEL), "row past the query length written"
+        compare_entry(o, pc, ps, b, pos[b], q, k, v, lq[b], lk[b], False, mode, 0,
+                      f"varlen_fp32 {mode}")
+    # decode: two query rows per entry against the same cache, causal
+    qd = np.ascontiguousarray(q[:, :, :2])
+    out_d = mx.attn_decode_varlen(to_torch(qd), kt, vt, lk, causal=True, mode=mode)
+    od = out_d.double().cpu().numpy()
+    split = mx.decode_split(B, Hkv, Skv)
+    for b in range(B):
+        ref = oracle.attn_rows(qd[b:b + 1], k[b:b + 1, :, :lk[b]], v[b:b + 1, :, :lk[b]],
+                               causal=True, mode=MODE_IDS[mode], bc=128,
+                               rows=np.arange(Hq * 2, dtype=np.int64), split=split)
+        err = np.abs(od[b].reshape(-1, D) - ref["o"])
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (b, err.max())
+
+
 def test_fwd_varlen_full_lengths_match_fwd():
     torch, mx = gpu()
     B, Hq, Hkv, S, D = 2, 4, 2, 300, 128
