@@ -208,7 +208,7 @@ def test_full_dit14(mode):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("mode", ["uos_pnq", "fp16"])
+@pytest.mark.parametrize("mode", ["uos_pnq", "uos_efq", "ocp", "fp16"])
 def test_full_dit13(mode):
     c = mxsynth.CONFIGS["dit13"]
     q, k, v = full_inputs("dit13")
