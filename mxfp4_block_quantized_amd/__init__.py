@@ -10,6 +10,7 @@ the library is missing this module raises at first use.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -108,6 +109,22 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run ``fn`` with its ``stream`` argument as torch's current stream, so
+    that every temporary it makes (workspace, length arrays, dump buffers,
+    zero-filled outputs) is allocated, filled and released on the stream
+    the kernels are launched on.  Without this, the caching allocator could
+    hand a freed temporary to work on another stream while a kernel still
+    reads it.  The caller orders its own inputs with that stream."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -165,6 +182,7 @@ def _ws(workspace):
 
 # ------------------------------------------------------------ quantizer ----
 
+@_on_stream
 def quantize(x: torch.Tensor, mode="uos", codes=None, scales=None, stream=None):
     """Blocks of 32 along the flattened contiguous axis of ``x`` (fp32 or
     bf16, numel % 32 == 0).  Returns (codes uint8[n/2], scales uint8[n/32])."""
@@ -181,6 +199,7 @@ def quantize(x: torch.Tensor, mode="uos", codes=None, scales=None, stream=None):
     return codes, scales
 
 
+@_on_stream
 def quantize_t(x: torch.Tensor, mode="uos", rows_pad: int = 0, stream=None):
     """Blocks of 32 along the rows of ``x`` [batch, rows, cols] (or [rows,
     cols]); returns transposed (codes [batch, cols, rows_pad/2], scales
@@ -201,6 +220,7 @@ def quantize_t(x: torch.Tensor, mode="uos", rows_pad: int = 0, stream=None):
     return codes, scales
 
 
+@_on_stream
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32,
                out=None, stream=None):
     """Values of packed codes under their E8M0 bytes, as fp32 or bf16."""
@@ -251,6 +271,7 @@ def alloc_workspace(q, k, mode):
     return torch.empty(nb, dtype=torch.uint8, device=q.device)
 
 
+@_on_stream
 def attn_fwd(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
              stream=None):
     """O = softmax(q k^T / sqrt(D)) v in the given mode; fp32 output.
@@ -266,6 +287,7 @@ def attn_fwd(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
     return out
 
 
+@_on_stream
 def attn_prepare(q, k, v, *, mode="uos_pnq", workspace=None, stream=None):
     """First half of attn_fwd: quantize (or convert) the key/value operands
     into the workspace (Q is quantized inside the attention kernels).
@@ -280,6 +302,7 @@ def attn_prepare(q, k, v, *, mode="uos_pnq", workspace=None, stream=None):
     return workspace
 
 
+@_on_stream
 def attn_fwd_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None,
                       stream=None):
     """Second half of attn_fwd: the fused attention kernel for the queries q
@@ -294,6 +317,7 @@ def attn_fwd_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None
     return out
 
 
+@_on_stream
 def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None,
                   stream=None):
     """attn_fwd plus the P~ codes / E8M0 bytes of the flattened query rows
@@ -333,6 +357,7 @@ def alloc_decode_workspace(q, k, mode):
     return torch.empty(nb, dtype=torch.uint8, device=q.device)
 
 
+@_on_stream
 def attn_decode(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=None,
                 stream=None):
     """Short-query attention over key splits (fp32 output); causal queries
@@ -349,6 +374,7 @@ def attn_decode(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=No
     return out
 
 
+@_on_stream
 def attn_decode_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=None,
                          stream=None):
     """attn_decode of the queries q on a workspace filled by attn_prepare
@@ -362,6 +388,7 @@ def attn_decode_prepared(q, k, workspace, *, causal=False, mode="uos_pnq", out=N
     return out
 
 
+@_on_stream
 def attn_decode_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None,
                      stream=None):
     """attn_decode plus the P~ codes / E8M0 bytes of the flattened query
@@ -390,6 +417,7 @@ def gemm_workspace(M: int, N: int, K: int, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
          out_dtype=torch.float32, out=None, workspace=None, stream=None):
     """y [M, N] = deq(a) deq(b)^T for MXFP4 operands stored as ``quantize``
@@ -410,6 +438,7 @@ def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
     return out
 
 
+@_on_stream
 def linear_w4a4(x: torch.Tensor, w_codes, w_scales, N: int, mode="uos",
                 out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
     """x [M, K] (fp32 or bf16) quantized along K with ``mode``, times the
@@ -450,6 +479,7 @@ def _lens(x, B, device):
     return t
 
 
+@_on_stream
 def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_k, *, causal=False, mode="uos_pnq", out=None,
                     workspace=None, rows=None, stream=None):
     """Padded batch of sequences with their own lengths: entry b has
@@ -475,6 +505,7 @@ def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_k, *, causal=False, mode="uos_pn
     return out, pc[:n], ps[:n], workspace
 
 
+@_on_stream
 def attn_decode_varlen(q, k, v, seqlens_k, *, causal=False, mode="uos_pnq", out=None,
                        workspace=None, rows=None, stream=None):
     """Short-query attention over key splits for a padded KV cache whose
@@ -499,6 +530,7 @@ def attn_decode_varlen(q, k, v, seqlens_k, *, causal=False, mode="uos_pnq", out=
     return out, pc[:n], ps[:n], workspace
 
 
+@_on_stream
 def attn_prepare_varlen(q, k, v, seqlens_k, *, mode="uos_pnq", workspace=None, stream=None):
     """KV tile images of a padded KV cache whose entry b holds seqlens_k[b]
     keys (keys past it quantized as zero), for attn_decode_varlen_prepared.
@@ -514,6 +546,7 @@ def attn_prepare_varlen(q, k, v, seqlens_k, *, mode="uos_pnq", workspace=None, s
     return workspace
 
 
+@_on_stream
 def attn_decode_varlen_prepared(q, k, workspace, seqlens_k, *, causal=False, mode="uos_pnq",
                                 out=None, stream=None):
     """attn_decode_varlen on a workspace filled by attn_prepare_varlen with

@@ -434,6 +434,9 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return MX_ERR_ARG;
   if (K % 128 != 0) return MX_ERR_UNSUPPORTED;
   if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
+  // the kernel's per-lane load offsets are 32-bit: a row within a 256-row
+  // tile times the row pitch K/2, plus a 16-byte chunk of a 128-byte line
+  if (255 * (K / 2) + 128 >= (int64_t(1) << 32)) return MX_ERR_UNSUPPORTED;
   // workgroup count (256 x 256 output tiles) must fit a 1-D grid
   if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
   return MX_OK;

@@ -148,10 +148,12 @@ __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
   constexpr int OPR = D / 8;  // octets per row
   constexpr int IMG = img_bytes(D);
   const int bgi = blockIdx.x / blocks_per_batch;
-  const int o = (blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
-  const int kr = o / OPR;
-  if (kr >= ntiles * kKvTile) return;  // whole quads: OPR is a multiple of 4
-  const int w = o % OPR;
+  // octet index within this (b, KV head): up to ntiles * 128 * D/8, past
+  // 32 bits for the longest key extents
+  const int64_t o = static_cast<int64_t>(blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
+  if (o >= static_cast<int64_t>(ntiles) * kKvTile * OPR) return;  // whole quads: OPR is a multiple of 4
+  const int kr = static_cast<int>(o / OPR);
+  const int w = static_cast<int>(o % OPR);
   // rows of this sequence: all, or its own length (rows past it are zeros)
   const int valid = lens ? min(max(lens[bgi / per_len], 0), rows) : rows;
   uint32_t f[8];
@@ -209,9 +211,9 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
   constexpr int NT = D / 16;
   constexpr int IMG = img_bytes(D);
   const int bgi = blockIdx.x / blocks_per_batch;
-  const int i = (blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
-  const int cg = i % NCG, kb = i / NCG;
-  if (kb >= ntiles * (kKvTile / kBlock)) return;
+  const int64_t i = static_cast<int64_t>(blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
+  if (i >= static_cast<int64_t>(ntiles) * (kKvTile / kBlock) * NCG) return;
+  const int cg = static_cast<int>(i % NCG), kb = static_cast<int>(i / NCG);
   const int valid = lens ? min(max(lens[bgi / per_len], 0), rows) : rows;
   const In* src = x + (static_cast<int64_t>(bgi) * rows + kb * kBlock) * D + cg * CPT;
   uint4 r[kBlock];
@@ -287,14 +289,16 @@ template <typename In, int UOS, int D>
 hipError_t launch_kv_images_t(const void* k, const void* v, int64_t batch, int rows,
                               int ntiles, uint8_t* img, const int32_t* lens, int per_len,
                               hipStream_t stream) {
-  const int kper = (ntiles * kKvTile * (D / 8) + kThreads - 1) / kThreads;
+  // work items per (b, KV head) in 64 bits; the C ABI has checked that
+  // batch * per-batch blocks fits the grid's 32-bit dimension
+  const int64_t kper = (static_cast<int64_t>(ntiles) * kKvTile * (D / 8) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((quant_kimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * kper)),
-                     dim3(kThreads), 0, stream, static_cast<const In*>(k), rows, ntiles, kper, img,
+                     dim3(kThreads), 0, stream, static_cast<const In*>(k), rows, ntiles, static_cast<int>(kper), img,
                      lens, per_len);
   constexpr int CPT = 16 / static_cast<int>(sizeof(In));
-  const int vper = (ntiles * (kKvTile / kBlock) * (D / CPT) + kThreads - 1) / kThreads;
+  const int64_t vper = (static_cast<int64_t>(ntiles) * (kKvTile / kBlock) * (D / CPT) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((quant_vimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * vper)),
-                     dim3(kThreads), 0, stream, static_cast<const In*>(v), rows, ntiles, vper, img,
+                     dim3(kThreads), 0, stream, static_cast<const In*>(v), rows, ntiles, static_cast<int>(vper), img,
                      lens, per_len);
   return hipGetLastError();
 }

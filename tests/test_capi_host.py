@@ -104,6 +104,10 @@ def test_workspace_and_tile_queries():
     assert L.mxattn_workspace_bytes(65535, 65535, 1, 1, 128, 64, 1, 3) == 0
     assert L.mxattn_workspace_bytes(1, 1, 1, 1, 1 << 28, 128, 1, 3) == 0
     assert L.mxattn_workspace_bytes(1, 1, 1, 1, (1 << 28) - 128, 128, 1, 3) > 0
+    # past 2^31 K-image work items per (b, KV head): the image launches
+    # count them in 64 bits (accepted shapes, D = 128 and 64)
+    assert L.mxattn_workspace_bytes(1, 1, 1, 1, (1 << 27) + 128, 128, 1, 3) > 0
+    assert L.mxattn_workspace_bytes(1, 1, 1, 1, (1 << 28) + 128, 64, 1, 3) > 0
     assert L.mxattn_workspace_bytes(1, 1, 1, 1 << 25, 128, 128, 0, 0) == 0
     assert L.mxattn_workspace_bytes(1, 1, 1, 1 << 25, 128, 128, 1, 0) > 0
 
@@ -122,6 +126,12 @@ def test_gemm_rejects_bad_args():
     assert g(a=None) == -1
     assert g(y=None) == -1
     assert g(M=1 << 31) == -2
+    # the per-lane 32-bit load offsets (row in tile x K/2) bound K
+    kmax = ((((1 << 32) - 129) // 255) * 2) // 128 * 128
+    assert 255 * (kmax // 2) + 128 < (1 << 32) <= 255 * ((kmax + 128) // 2) + 128
+    assert L.mxgemm_workspace_bytes(64, 64, kmax) > 0
+    assert L.mxgemm_workspace_bytes(64, 64, kmax + 128) == 0
+    assert g(K=kmax + 128) == -2
     assert g(y=ctypes.c_void_p((1 << 20) + 8)) == -5   # y not 16-byte aligned
     assert g(ws=None) == -3
     assert g(wsb=16) == -3

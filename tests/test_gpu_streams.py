@@ -44,6 +44,49 @@ def test_side_stream():
     assert torch.equal(out_d, ref_d)
 
 
+def test_stream_argument_not_current():
+    """stream=s while another stream is current: the temporaries the binding
+    makes (workspace, length arrays, dump buffers, zero-filled outputs) live
+    on s, so allocations and fills on the current stream right after the
+    call cannot take them over while the kernels still run."""
+    torch, mx = gpu()
+    q, k, v = qkv(64, 1, 4, 2, 700, 700, 128)
+    qd, kd, vd = qkv(65, 2, 8, 2, 1, 6000, 128)
+    lq = [640, 600]
+    lk = [700, 650]
+    q2, k2, v2 = (torch.cat([t, t]) for t in (q, k, v))
+    rows = [5, 699, 2 * 700 + 3]
+    ref = mx.attn_fwd(q, k, v, causal=True, mode="uos_pnq")
+    ref_v = mx.attn_fwd_varlen(q2, k2, v2, lq, lk, causal=True, mode="uos_pnq")
+    ref_dump = mx.attn_fwd_dump(q, k, v, rows, causal=False, mode="uos")
+    ref_d = mx.attn_decode(qd, kd, vd, causal=True, mode="uos_efq")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    junk = []
+
+    def churn():
+        # current-stream allocations and writes while s may still be busy
+        for _ in range(4):
+            junk.append(torch.full((1 << 24,), 7, dtype=torch.uint8, device="cuda"))
+
+    out = mx.attn_fwd(q, k, v, causal=True, mode="uos_pnq", stream=s)
+    churn()
+    out_v = mx.attn_fwd_varlen(q2, k2, v2, lq, lk, causal=True, mode="uos_pnq", stream=s)
+    churn()
+    out_dump = mx.attn_fwd_dump(q, k, v, rows, causal=False, mode="uos", stream=s)
+    churn()
+    out_d = mx.attn_decode(qd, kd, vd, causal=True, mode="uos_efq", stream=s)
+    churn()
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(out_v, ref_v)
+    for got, want in zip(out_dump[:3], ref_dump[:3]):
+        assert torch.equal(got, want)
+    assert torch.equal(out_d, ref_d)
+
+
 def test_graph_capture_and_replay():
     torch, mx = gpu()
     q, k, v = qkv(62, 1, 4, 2, 260, 260, 128)
