@@ -1,18 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of MXFP4 UOS+PNQ attention on one MI355X.
 
-A step is one mxattn_fwd call in UOS+PNQ mode on the video-DiT 14B
-self-attention shape (B=1, H=40, S=32760, D=128, bf16 inputs, non-causal):
-quantize K (blocks along D) and V (blocks along keys), then the fused FP4
-attention kernel, which quantizes Q (blocks along D) as it loads it.  Inputs are seeded synthetic tensors (mxsynth) already
-resident in HBM.  Prints ONE JSON line on stdout; progress goes to stderr.
+A step is one mxattn_fwd call in UOS+PNQ mode on the long video-DiT 13B
+self-attention shape (B=1, H=24, S=118800, D=128, bf16 inputs, non-causal),
+the largest configuration that runs on one GPU: quantize K (blocks along D)
+and V (blocks along keys), then the fused FP4 attention kernel, which
+quantizes Q (blocks along D) as it loads it.  Inputs are seeded synthetic
+tensors (mxsynth) already resident in HBM.  Prints ONE JSON line on stdout;
+progress goes to stderr.
 
 value      = attention TFLOP/s of the whole step, 4*B*H*Sq*Skv*D / time
              (halved when causal);
 roofline   = the fused attention kernel alone, timed with stream events,
              against the 10.1 PFLOP/s dense FP4 MFMA peak;
-alongside  = the UOS+EFQ (exp-free P~), FP16, OCP and UOS modes on the same
-             inputs;
+alongside  = the FP16 (unquantized), OCP and UOS+EFQ (exp-free P~) modes on
+             the same inputs;
+attention  = the video-DiT 14B shape (B=1, H=40, S=32760) in every mode and
+             the causal LLM prefill (B=4, 32 query / 8 KV heads, S=8192) in
+             the OCP, UOS, UOS+PNQ and UOS+EFQ modes, whole step and kernel
+             alone;
 quantizer  = the standalone quantize / dequantize of the 8192 x 28672 bf16
              roundtrip tensor, GB/s against 8 TB/s HBM;
 decode     = short-query attention over key splits (mxattn_decode_prepared,
@@ -26,7 +32,8 @@ prefill_varlen = the LLM prefill batch (B=4, causal) with per-entry prompt
 gemm       = the W4A4 product (mxgemm) on the DiT feed-forward up-projection
              (32760 tokens x 5120 -> 13824, UOS operands, bf16 output), alone
              and with the activation quantization, against 10.1 PFLOP/s;
-cpu_baseline = the binary64 oracle on a bounded row sample, host cores.
+cpu_baseline = the binary64 oracle on a bounded row sample of the headline
+             workload, host cores.
 """
 from __future__ import annotations
 
@@ -81,13 +88,18 @@ def attn_flops(c) -> float:
     return f / 2 if c["causal"] else f
 
 
-def time_attention(torch, mx, qt, kt, vt, c, mode, steps, warmup):
-    """Returns (ms per whole step, ms of prepare, ms of the attention kernel)."""
+def time_attention(torch, mx, qt, kt, vt, c, mode, steps, warmup, min_warm_ms=0.0):
+    """Returns (ms per whole step, ms of prepare, ms of the attention kernel).
+    ``warmup`` untimed steps first (and more, up to ``min_warm_ms`` of wall
+    time, for the sections that follow host-side input generation)."""
     causal = c["causal"]
     ws = mx.alloc_workspace(qt, kt, mode)
     out = torch.empty(qt.shape, dtype=torch.float32, device=qt.device)
     for _ in range(warmup):
         mx.attn_fwd(qt, kt, vt, causal=causal, mode=mode, out=out, workspace=ws)
+    if min_warm_ms > 0:
+        warm(torch, lambda: mx.attn_fwd(qt, kt, vt, causal=causal, mode=mode, out=out,
+                                        workspace=ws), min_ms=min_warm_ms)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -104,6 +116,37 @@ def time_attention(torch, mx, qt, kt, vt, c, mode, steps, warmup):
     return wall / steps * 1e3, prep, attn
 
 
+def mode_peak(mode: str) -> float:
+    return BF16_PEAK_TFLOPS if mode == "fp16" else FP4_PEAK_TFLOPS
+
+
+def describe(name: str, c) -> str:
+    return (f"{name}: B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} Sq=Skv={c['S']} D={c['D']} "
+            f"causal={c['causal']} bf16 inputs")
+
+
+def bench_attention(torch, mx, name, qt, kt, vt, modes, steps, warmup, min_warm_ms=0.0):
+    """Every mode of one attention workload: whole step (K/V quantize +
+    attention kernel) and the attention kernel alone, each against the peak
+    of the mode's matrix-core type (FP4, or bf16 for the FP16 mode)."""
+    c = dict(__import__("mxsynth").CONFIGS[name])
+    flops = attn_flops(c)
+    res = {"workload": describe(name, c), "flops": flops, "modes": {}}
+    sha = kernel_source_sha()
+    for mode in modes:
+        ms, prep, attn = time_attention(torch, mx, qt, kt, vt, c, mode, steps, warmup, min_warm_ms)
+        peak = mode_peak(mode)
+        r = {"ms_per_step": ms, "tflops": flops / ms / 1e9, "prepare_ms": prep,
+             "attn_kernel_ms": attn, "attn_kernel_tflops": flops / attn / 1e9,
+             "attn_kernel_frac_peak": flops / attn / 1e9 / peak, "peak_tflops": peak,
+             "steps": steps}
+        if mode != "fp16":
+            r["traffic"] = read_traffic(sha, f"{name}:{mode}")
+        res["modes"][mode] = r
+        log(f"[bench] {name} {mode}: {r}")
+    return res
+
+
 def read_traffic(sha: str, workload: str, kernel="attn_mx_kernel"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     summary, if it was taken on this kernel source."""
@@ -112,9 +155,12 @@ def read_traffic(sha: str, workload: str, kernel="attn_mx_kernel"):
             t = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("src_sha256") != sha or t.get("workload") != workload:
+    entry = t.get(workload) if isinstance(t, dict) and "src_sha256" not in t else t
+    if not isinstance(entry, dict) or entry.get("src_sha256") != sha:
         return None
-    return t.get("hbm_bytes_per_launch")
+    if entry.get("workload", workload) != workload:
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def bench_quantizer(torch, mx, reps=20):
@@ -324,21 +370,55 @@ def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
             "linear_w4a4_ms": lin_ms, "linear_w4a4_tflops": flops / lin_ms / 1e9}
 
 
-def cpu_baseline(q, k, v, c, name, rows_per_head=2048):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Query rows per head of the oracle sample: about 10-30 s of host work.
+CPU_ROWS_PER_HEAD = {"dit13": 512, "dit14": 2048, "llm_prefill": 1024}
+
+
+def cpu_baseline(q, k, v, c, name):
     """The oracle (as it stands) on a bounded, seeded sample of query rows of
-    every head (about 10-20 s of CPU work at the DiT14 shape)."""
+    every head of the workload, against all keys."""
     import mxsynth
     import oracle
+    rows_per_head = CPU_ROWS_PER_HEAD[name]
     rows = mxsynth.sample_rows(c["seed"], c["B"], c["Hq"], c["S"], rows_per_head)
     t0 = time.perf_counter()
     oracle.attn_rows(q, k, v, causal=c["causal"], mode=oracle.MODE_UOS_PNQ, bc=128, rows=rows)
     dt = time.perf_counter() - t0
     flops = 4.0 * rows.size * c["S"] * c["D"] * (0.5 if c["causal"] else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle", "seconds": dt,
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": dt,
             "sample": f"{name} UOS+PNQ, {rows.size} seeded query rows ({rows_per_head} from each "
                       f"of the {c['B'] * c['Hq']} heads) against all {c['S']} keys, binary64, "
                       f"including the K/V quantization of those heads"}
+
+
+# Modes timed per attention workload (the first is the headline when the
+# workload is the headline one).
+WORKLOAD_MODES = {
+    "dit13": ("uos_pnq", "fp16", "ocp", "uos_efq"),
+    "dit14": ("uos_pnq", "uos_efq", "fp16", "ocp", "uos"),
+    "llm_prefill": ("uos_pnq", "uos_efq", "ocp", "uos"),
+}
+SECTION_STEPS = {"dit13": 5, "dit14": 10, "llm_prefill": 20}
+
+
+def load_inputs(torch, name):
+    import mxsynth
+    log(f"[bench] generating {name} inputs")
+    q, k, v = mxsynth.make_attn_inputs(name)
+    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
+    return (q, k, v), (to(q), to(k), to(v))
 
 
 def main():
@@ -346,16 +426,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dit14", choices=["dit14", "dit13", "llm_prefill"])
-    ap.add_argument("--modes", default="uos_pnq,uos_efq,fp16,ocp,uos",
-                    help="first mode is the headline; the rest run alongside")
+    ap.add_argument("--workload", default="dit13", choices=sorted(WORKLOAD_MODES))
+    ap.add_argument("--modes", default=None,
+                    help="comma list; the first is the headline, the rest run alongside "
+                         "(default: every mode of the workload, UOS+PNQ first)")
+    ap.add_argument("--sections", default="dit14,llm_prefill",
+                    help="other attention workloads timed in every mode ('' for none)")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the per-sequence-length sections (prefill, decode)")
     ap.add_argument("--no-attention", action="store_true",
-                    help="only the standalone quantizer and the GEMM (for profiling them alone)")
+                    help="only the standalone quantizer, the GEMM and the decode sections "
+                         "(for profiling them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size "
@@ -377,12 +461,12 @@ def main():
 
     mx.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     if args.no_attention:
-        if args.calibrate_copy:
-            src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-            torch.empty_like(src).copy_(src)
-            torch.cuda.synchronize()
-            del src
         res = {}
         if not args.no_quantizer:
             res["quantizer"] = bench_quantizer(torch, mx, reps=3)
@@ -392,37 +476,26 @@ def main():
             res["decode"] = bench_decode(torch, mx, reps=3, varlen=not args.no_varlen)
         print(json.dumps(res), flush=True)
         return
-    c = dict(mxsynth.CONFIGS[args.workload])
-    log(f"[bench] generating {args.workload} inputs")
-    q, k, v = mxsynth.make_attn_inputs(args.workload)
-    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
-    qt, kt, vt = to(q), to(k), to(v)
-    flops = attn_flops(c)
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    modes = args.modes.split(",")
-    results = {}
-    for mode in modes:
-        steps = args.steps if mode == modes[0] else max(3, args.steps // 2)
-        warm = args.warmup if mode == modes[0] else max(1, args.warmup // 2)
-        ms, prep, attn = time_attention(torch, mx, qt, kt, vt, c, mode, steps, warm)
-        results[mode] = {"ms_per_step": ms, "tflops": flops / ms / 1e9,
-                         "prepare_ms": prep, "attn_kernel_ms": attn,
-                         "attn_kernel_tflops": flops / attn / 1e9, "steps": steps}
-        log(f"[bench] {mode}: {results[mode]}")
 
+    c = dict(mxsynth.CONFIGS[args.workload])
+    host, (qt, kt, vt) = load_inputs(torch, args.workload)
+    modes = args.modes.split(",") if args.modes else list(WORKLOAD_MODES[args.workload])
     head = modes[0]
-    hr = results[head]
-    sha = kernel_source_sha()
-    peak = BF16_PEAK_TFLOPS if head == "fp16" else FP4_PEAK_TFLOPS
+    # the headline mode: --warmup untimed steps, then exactly --steps timed
+    # steps; the modes alongside: half as many
+    headline = bench_attention(torch, mx, args.workload, qt, kt, vt, [head], args.steps,
+                               args.warmup)
+    along = bench_attention(torch, mx, args.workload, qt, kt, vt, modes[1:],
+                            max(3, args.steps // 2), max(1, args.warmup // 2)) if modes[1:] else None
+    del qt, kt, vt
+    torch.cuda.empty_cache()
+    hr = headline["modes"][head]
+    flops = headline["flops"]
+    peak = mode_peak(head)
     roofline = {"bound": "mfma", "kernel": "attn_mx_kernel" if head != "fp16" else "attn_f16_kernel",
                 "achieved": hr["attn_kernel_tflops"], "peak": peak, "unit": "TFLOP/s",
                 "frac": hr["attn_kernel_tflops"] / peak,
-                "traffic": read_traffic(sha, f"{args.workload}:{head}"),
+                "traffic": hr.get("traffic"),
                 "algorithmic_flops_per_launch": flops,
                 "launch_ms": hr["attn_kernel_ms"]}
     out = {
@@ -438,15 +511,23 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4" if head != "fp16" else "bf16/fp16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} "
-                               f"Sq=Skv={c['S']} D={c['D']} causal={c['causal']} bf16 inputs, "
-                               f"mode {head}",
+        "config": {"workload": f"{describe(args.workload, c)}, mode {head}",
                    "B": c["B"], "Hq": c["Hq"], "Hkv": c["Hkv"], "S": c["S"], "D": c["D"],
                    "causal": c["causal"], "mode": head, "kv_tile": mx.kv_tile(c["D"], head)},
         "pct_fp4_peak": 100.0 * hr["tflops"] / FP4_PEAK_TFLOPS,
         "roofline": roofline,
-        "alongside": {m: results[m] for m in modes[1:]},
+        "alongside": along["modes"] if along else {},
     }
+    sections = [w for w in args.sections.split(",") if w and w != args.workload]
+    if sections:
+        out["attention"] = {}
+    for name in sections:
+        _, (sq, sk, sv) = load_inputs(torch, name)
+        out["attention"][name] = bench_attention(torch, mx, name, sq, sk, sv,
+                                                 list(WORKLOAD_MODES[name]),
+                                                 SECTION_STEPS.get(name, 5), 3, min_warm_ms=200.0)
+        del sq, sk, sv
+        torch.cuda.empty_cache()
     if not args.no_quantizer:
         out["quantizer"] = bench_quantizer(torch, mx)
         log(f"[bench] quantizer: {out['quantizer']}")
@@ -461,6 +542,7 @@ def main():
         log(f"[bench] prefill varlen: {out['prefill_varlen']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
+        q, k, v = host
         out["cpu_baseline"] = cpu_baseline(q, k, v, c, args.workload)
     print(json.dumps(out), flush=True)
 
