@@ -361,6 +361,26 @@ int mxgemm(const uint8_t *a_codes, const uint8_t *a_scales,
            int64_t N, int64_t K, int out_dtype, void *y, void *workspace,
            size_t ws_bytes, void *stream);
 
+/*
+ * mxgemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and errors as
+ * mxgemm minus workspace/ws_bytes; the same kernels run.  The staging that
+ * mxgemm keeps in the caller's workspace lives instead in a scratch array of
+ * the library: 32 MiB of device memory per GPU, reserved when the library
+ * is loaded on that GPU and held until the process ends.  Shapes whose
+ * staging, mxgemm_workspace_bytes(M, N, K), exceeds 32 MiB give
+ * MX_ERR_UNSUPPORTED (e.g. M = 32760, N = 13824 fits up to K = 23040).  The
+ * call allocates and frees nothing; the first call on a GPU looks up that
+ * GPU's address of the array (MX_ERR_HIP if the lookup fails).  Every call
+ * on one GPU uses that GPU's one array, so calls that can run at the same
+ * time on one GPU (different streams, or host threads) race and give wrong
+ * results: serialize them, or use mxgemm with separate workspaces.
+ */
+int mxgemm_noalloc(const uint8_t *a_codes, const uint8_t *a_scales,
+                   const uint8_t *b_codes, const uint8_t *b_scales, int64_t M,
+                   int64_t N, int64_t K, int out_dtype, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

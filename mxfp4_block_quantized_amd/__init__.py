@@ -33,6 +33,7 @@ EXPORTS = (
     "mxgemm_workspace_bytes", "mxattn_decode_split", "mxattn_decode_workspace_bytes",
     "mxattn_decode", "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
     "mxattn_decode_varlen", "mxattn_prepare_varlen", "mxattn_decode_varlen_prepared",
+    "mxgemm_noalloc",
 )
 
 _lib = None
@@ -79,13 +80,15 @@ def lib():
     L.mxattn_decode_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, ci, ci, P, P, sz, P, P, P, P]
     L.mxattn_prepare_varlen.argtypes = [P, P, P] + [ci] * 7 + [P, ci, P, sz, P]
     L.mxattn_decode_varlen_prepared.argtypes = [P] + [ci] * 7 + [P, ci, ci, P, P, sz, P]
+    L.mxgemm_noalloc.argtypes = [P, P, P, P, i64, i64, i64, ci, P, P]
     L.mxgemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.mxgemm_workspace_bytes.restype = sz
     for f in ("mxq_quantize", "mxq_quantize_t", "mxq_dequantize", "mxattn_workspace_layout",
               "mxattn_kv_tile", "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare",
               "mxattn_fwd_prepared", "mxgemm", "mxattn_decode_split", "mxattn_decode",
               "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
-              "mxattn_decode_varlen", "mxattn_prepare_varlen", "mxattn_decode_varlen_prepared"):
+              "mxattn_decode_varlen", "mxattn_prepare_varlen", "mxattn_decode_varlen_prepared",
+              "mxgemm_noalloc"):
         getattr(L, f).restype = ci
     _lib = L
     return L
@@ -439,6 +442,23 @@ def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
 
 
 @_on_stream
+@_on_stream
+def gemm_noalloc(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, out,
+                 stream=None):
+    """``gemm`` into the caller's ``out`` [M, N] (fp32 or bf16) with the
+    library's own scratch instead of a workspace: the C call allocates
+    nothing.  Calls that overlap on one GPU race (one shared scratch)."""
+    _dev(a_codes, "a_codes", torch.uint8, M * K // 2)
+    _dev(a_scales, "a_scales", torch.uint8, M * K // 32)
+    _dev(b_codes, "b_codes", torch.uint8, N * K // 2)
+    _dev(b_scales, "b_scales", torch.uint8, N * K // 32)
+    _dev(out, "out", None, M * N)
+    _check("mxgemm_noalloc", lib().mxgemm_noalloc(
+        _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _dtype_code(out),
+        _ptr(out), _stream(stream)))
+    return out
+
+
 def linear_w4a4(x: torch.Tensor, w_codes, w_scales, N: int, mode="uos",
                 out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
     """x [M, K] (fp32 or bf16) quantized along K with ``mode``, times the

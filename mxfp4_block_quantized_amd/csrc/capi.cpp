@@ -463,6 +463,22 @@ int mxgemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_cod
                                        as_stream(stream)));
 }
 
+int mxgemm_noalloc(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                   const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, int out_dtype,
+                   void* y, void* stream) {
+  if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
+  const int st = check_gemm_shape(M, N, K);
+  if (st != MX_OK) return st;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return MX_ERR_ARG;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
+  // the scale images must fit the library's scratch array
+  if (mxk::gemm_workspace_bytes(M, N, K) > mxk::kGemmScratchBytes) return MX_ERR_UNSUPPORTED;
+  uint8_t* ws = nullptr;
+  if (mxk::gemm_scratch(&ws) != hipSuccess) return MX_ERR_HIP;
+  return to_status(mxk::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K,
+                                       out_dtype == MX_BF16, y, ws, as_stream(stream)));
+}
+
 int mxattn_decode_split(int B, int Hkv, int Skv) {
   if (B < 1 || Hkv < 1 || Skv < 1) return MX_ERR_ARG;
   return decode_split_tiles(B, Hkv, Skv) * mxk::kKvTile;

@@ -34,6 +34,7 @@
 // Rows past M or N read the last valid row (their outputs are not stored).
 // K must be a positive multiple of 128.
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 
@@ -508,7 +509,38 @@ hipError_t launch_scale_image(const uint8_t* sc, int64_t rows, int64_t K, uint8_
   return hipGetLastError();
 }
 
+// Scale images of the product without a caller workspace: a file-scope
+// device array, one copy per GPU, kept until the process ends.  In host code
+// the name `scratch` is not a device address; the device address is fetched
+// per device (gemm_scratch) and only that is passed to kernels.
+__device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
+
 }  // namespace
+
+hipError_t gemm_scratch(uint8_t** out) {
+  static std::atomic<uint8_t*> addr[64];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  uint8_t* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      // with `dev` current: this device's copy of the array
+      void* sym = nullptr;
+      e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (sym == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<uint8_t*>(sym);
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (scale_image_bytes(M, K) + 255) / 256 * 256 + scale_image_bytes(N, K);

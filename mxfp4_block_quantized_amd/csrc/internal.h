@@ -115,6 +115,10 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, int out_bf16,
                           void* y, uint8_t* ws, hipStream_t stream);
+// The library's own GEMM scratch (gemm_mx.hip): kGemmScratchBytes per GPU;
+// *out = this device's address of it (looked up once per device).
+constexpr size_t kGemmScratchBytes = size_t(32) << 20;
+hipError_t gemm_scratch(uint8_t** out);
 
 // Operands of the 16-bit attention kernel.
 struct F16AttnArgs {
