@@ -183,9 +183,32 @@ __device__ __forceinline__ void mask_tile(v4f (&s)[kSub], int lim) {
     for (int r = 0; r < 4; ++r) s[t][r] = (t * 4 + r > lim) ? -INFINITY : s[t][r];
 }
 
+// Largest of the 32 scores this lane holds (its P~ block of one query):
+// a tree of v_max3 (depth 4) rather than one dependent chain.
+__device__ __forceinline__ float block_max32(const v4f (&s)[kSub]) {
+  // (the empty asm statements keep the compiler from re-associating the
+  // tree into a chain)
+  float a[kSub];
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) a[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
+  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+               "+v"(a[7]));
+  // 16 values: a[0..7] and s[t][3]
+  float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  float b2 = fmaxf(fmaxf(a[6], a[7]), s[0][3]);
+  float b3 = fmaxf(fmaxf(s[1][3], s[2][3]), s[3][3]);
+  float b4 = fmaxf(fmaxf(s[4][3], s[5][3]), s[6][3]);
+  asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3), "+v"(b4));
+  float c0 = fmaxf(fmaxf(b0, b1), b2);
+  float c1 = fmaxf(fmaxf(b3, b4), s[7][3]);
+  asm volatile("" : "+v"(c0), "+v"(c1));
+  return fmaxf(c0, c1);
+}
+
 // Online-softmax step of one query tile: row max, history factor alpha,
 // this lane's P~ block scale (X, e) and the offset kofs of the scaled
-// domain; rescales the history when any row's max moved.
+// domain.  The history itself is rescaled by rescale_o.
 struct TileStats {
   float alpha, kofs;
   int X;
@@ -193,15 +216,10 @@ struct TileStats {
 // PNQ: 0 = denominator from the unquantized p (OCP, UOS); 1 = PNQ; 2 = PNQ
 // with the exp-free EFQ codes.
 template <int D, int UOS, int PNQ>
-__device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
-  constexpr int NT = D / 16;
-  // row max: in-lane over this lane's 32-key block (a v_max3 chain), then
-  // across the four lanes holding this query
-  float bmax = s[0][0];
-#pragma unroll
-  for (int i = 1; i + 1 < 4 * kSub; i += 2)
-    bmax = fmaxf(fmaxf(bmax, s[i >> 2][i & 3]), s[(i + 1) >> 2][(i + 1) & 3]);
-  bmax = fmaxf(bmax, s[kSub - 1][3]);
+__device__ __forceinline__ TileStats tile_stats_nr(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
+  // row max: in-lane over this lane's 32-key block, then across the four
+  // lanes holding this query
+  const float bmax = block_max32(s);
   // delta = new max - mref.  Before the first tile the running max is -inf
   // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
   const float delta = fmaxf(w.m[u] - w.mref[u], xlane_max4(bmax));
@@ -217,15 +235,28 @@ __device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4
   r.X = static_cast<int>(e) + 127;
   // EFQ: 2 r + beta = d * 2c + (beta - 2 (delta c + e)); else the exp2 offset
   r.kofs = PNQ == 2 ? kEfqBeta - 2.0f * fmaf(delta, sl2, e) : fmaf(delta, sl2, e);
-  // history rescale: alpha == 1 exactly leaves the history unchanged, so
-  // the multiplies are skipped when that holds for the whole wave
-  if (__builtin_amdgcn_ballot_w64(r.alpha != 1.0f) != 0) {
+  return r;
+}
+
+// History rescale by alpha: alpha == 1 exactly leaves the history
+// unchanged, so the multiplies are skipped when that holds for the whole
+// wave (a uniform branch).
+template <int D, int PNQ>
+__device__ __forceinline__ void rescale_o(WaveState<D>& w, int u, float alpha) {
+  constexpr int NT = D / 16;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) w.oacc[u][n] *= r.alpha;
+    for (int n = 0; n < NT; ++n) w.oacc[u][n] *= alpha;
     // the four lanes of a lacc column hold the same sum; only element 0 is
     // read at the end, so only it is kept rescaled (the others stay finite)
-    if (PNQ) w.lacc[u][0] *= r.alpha;
+    if (PNQ) w.lacc[u][0] *= alpha;
   }
+}
+
+template <int D, int UOS, int PNQ>
+__device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
+  const TileStats r = tile_stats_nr<D, UOS, PNQ>(w, u, s, sl2);
+  rescale_o<D, PNQ>(w, u, r.alpha);
   return r;
 }
 
@@ -276,6 +307,39 @@ __device__ __forceinline__ uint4 p_tile(const v4f (&s)[kSub], float sl2, float k
   return make_uint4(pw[0], pw[1], pw[2], pw[3]);
 }
 
+// Half h of dword q of p_tile's result: keys 8q + 4h .. 8q + 4h + 3 of this
+// lane's block (subtile 2q + h), into bytes 2h and 2h+1 of x (the other
+// half's bytes kept); vsum accumulates the unquantized v (non-PNQ modes).
+// EFQ writes its code bytes into a (even keys) and b (odd keys) instead.
+template <int PNQ, int h>
+__device__ __forceinline__ void p_half(const v4f (&s)[kSub], int q, float sl2, float kofs, uint32_t& x,
+                                       uint32_t& b, float& vsum) {
+  const v4f& sv = s[2 * q + h];
+  if (PNQ == 2) {
+    const float c2 = 2.0f * sl2;
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = fmaf(sv[i], c2, kofs);
+    // all four bytes of each word are written over the two halves
+    x = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 2 * h, h ? x : __float_as_uint(t[0]));
+    x = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 2 * h + 1, x);
+    b = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 2 * h, h ? b : __float_as_uint(t[1]));
+    b = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 2 * h + 1, b);
+    if (h) x |= b << 4;
+    return;
+  }
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -kofs));
+    if (!PNQ) vsum += v[i];
+  }
+  // all four bytes are written over the two halves, so the first write may
+  // start from any value
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h ? x : __float_as_uint(v[0]), v[0], v[1], 1.0f, 2 * h);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 2 * h + 1);
+}
+
 // Denominator and O^T += V~^T P~^T for one query tile.
 template <int D, int PNQ>
 __device__ __forceinline__ void pv_tile(WaveState<D>& w, int u, const uint4& pop, const TileStats& ts,
@@ -321,71 +385,237 @@ __device__ __forceinline__ void quant_q_block(const MxAttnArgs& a, int64_t row, 
 }
 
 // Interleave n matrix-core instructions with the vector work around them
-// (k VALU instructions after each), so that the transcendental unit runs
-// while the matrix core is busy.
+// (k vector or transcendental instructions after each), so that no wave
+// issues matrix instructions back to back: a wave waiting for a busy
+// matrix core holds up the other wave's vector instructions on its SIMD.
 template <int N, int K>
 __device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x402, K, 0);  // VALU or TRANS
   }
 }
 
-// One KV tile (keys j0 .. j0+127) for this wave's two query tiles, as a
-// two-stage software pipeline: S^T of query tile 1 runs on the matrix core
-// while P~ of query tile 0 is formed, and O^T of tile 0 while P~ of tile 1
-// is formed.  mask: keys beyond klim[u] (sequence end, causal diagonal) are
-// excluded.  visit: the rows reach this tile (only the P~ dump uses it).
-template <int D, int UOS, int PNQ, int DUMP>
-__device__ __forceinline__ void compute_tile(WaveState<D>& w, const uint8_t* st, const uint4 (&qop)[kQT],
-                                             const int (&qsc)[kQT], const int (&qrow)[kQT],
-                                             const int (&klim)[kQT], bool mask, bool visit, int j0, int lane,
-                                             float sl2, const MxAttnArgs& a, int64_t bh) {
-  static_assert(kQT == 2, "two query tiles per wave");
+// K~ and V~ operands of one KV tile, read from its LDS stage.
+template <int D>
+struct KOps {
+  uint4 op[kSub];
+  uint2 sc;
+};
+template <int D>
+struct VOps {
+  uint4 op[D / 16];
+  uint32_t sc[(D / 16 + 3) / 4];
+};
+template <int D>
+__device__ __forceinline__ void read_k(KOps<D>& k, const uint8_t* st, int lane) {
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) k.op[t] = *reinterpret_cast<const uint4*>(st + kImgKc + t * 1024 + lane * 16);
+  k.sc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
+}
+template <int D>
+__device__ __forceinline__ void read_v(VOps<D>& v, const uint8_t* st, int lane) {
   constexpr int NT = D / 16;
-  const int grp = lane >> 4;
-
-  uint4 kop[kSub];
 #pragma unroll
-  for (int t = 0; t < kSub; ++t) kop[t] = *reinterpret_cast<const uint4*>(st + kImgKc + t * 1024 + lane * 16);
-  const uint2 ksc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
-  uint4 vop[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) vop[n] = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
-  uint32_t vsc[(NT + 3) / 4];
+  for (int n = 0; n < NT; ++n) v.op[n] = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
   if (NT == 8) {
     const uint2 v2 = *reinterpret_cast<const uint2*>(st + img_vs(D) + lane * 8);
-    vsc[0] = v2.x;
-    vsc[(NT + 3) / 4 - 1] = v2.y;
+    v.sc[0] = v2.x;
+    v.sc[(NT + 3) / 4 - 1] = v2.y;
   } else {
-    vsc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
+    v.sc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
   }
+}
 
-  v4f s0[kSub], s1[kSub];
-  s_tile(s0, kop, ksc, qop[0], qsc[0], w.mref[0]);
-  if (mask) mask_tile(s0, klim[0] - (j0 + grp * 32));
-  const TileStats t0 = tile_stats<D, UOS, PNQ>(w, 0, s0, sl2);
+// The two query tiles of a wave (A = 0, B = 1) run as a software pipeline
+// with B half a KV tile behind A, so that every group of matrix
+// instructions has independent vector work beside it.  For KV tile j:
+//   step 1: P~V of B for tile j-1          | row max and scales of A, tile j
+//   step 2: S^T of B for tile j            | P~ of A, tile j
+//   step 3: P~V of A for tile j            | row max and scales of B, tile j
+//   step 4: S^T of A for tile j+1          | P~ of B, tile j
+// The history of A is rescaled between steps 1 and 2, that of B between
+// steps 3 and 4 (a uniform branch, skipped when no row's max moved).  Each
+// step's operands are read from LDS one step ahead and kept in registers
+// while they are needed: V~ of tile j (read in step 2) serves steps 3 and
+// the next step 1, K~ of tile j+1 (read in step 3) steps 4 and the next
+// step 2.  At the last tile step 3 reads a stage with no pending loads and
+// step 4's S^T is unused.
+template <int D, int UOS, int PNQ>
+struct Pipe {
+  v4f sA[kSub], sB[kSub];  // S^T of A (tile j, from step 4 before) and of B
+  TileStats tA, tB;
+  uint4 pA, pB;            // P~ of A and B
+  float vA, vB;            // sums of the unquantized p (non-PNQ modes)
+  KOps<D> kk;              // K~ operands for steps 4 and 2
+  VOps<D> vv;              // V~ operands for steps 3 and 1
+};
 
-  float vsum0, vsum1;
-  s_tile(s1, kop, ksc, qop[1], qsc[1], w.mref[1]);
-  uint4 pop0 = p_tile<PNQ>(s0, sl2, t0.kofs, vsum0);
-  interleave_mfma_valu<kSub, 8>();
-  // keep P~ of tile 0 here, beside the S^T products of tile 1, instead of
-  // letting the compiler sink it next to its matrix-core use
-  asm volatile("" : "+v"(pop0.x), "+v"(pop0.y), "+v"(pop0.z), "+v"(pop0.w));
-  if (!PNQ) asm volatile("" : "+v"(vsum0));
-  dump_tile<DUMP>(a, bh, qrow[0], visit, j0, grp, pop0, t0.X);
+// One fenced scheduling region: the compiler may order instructions within
+// it but moves nothing across, so the interleave of matrix and vector work
+// follows the source.  (This file is built with instruction selection in
+// source order and without machine sinking, which would otherwise gather
+// the side-effect-free matrix instructions ahead of the first fence or move
+// them past the uniform rescale branches.)
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+// Results passed through pin_out must exist at that point (an empty asm
+// statement), so a fenced region's vector work stays inside it.
+__device__ __forceinline__ void pin_out(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin_out(float& v) { asm volatile("" : "+v"(v)); }
 
-  if (mask) mask_tile(s1, klim[1] - (j0 + grp * 32));
-  const TileStats t1 = tile_stats<D, UOS, PNQ>(w, 1, s1, sl2);
+// One P~V matrix instruction of query tile u: channel tile n < D/16, or
+// (n == D/16, PNQ modes) the denominator against an all-ones operand.
+template <int D, int PNQ>
+__device__ __forceinline__ void pv_one(WaveState<D>& w, int u, int n, const uint4& pop, int X,
+                                       const VOps<D>& vv) {
+  constexpr int NT = D / 16;
+  if (n < NT) {
+    w.oacc[u][n] = mfma_fp4_sel(vv.op[n], pop, w.oacc[u][n], vv.sc[n >> 2], n & 3, X);
+  } else if (PNQ) {
+    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
+    w.lacc[u] = mfma_fp4<0>(ones, pop, w.lacc[u], 127, X);
+  }
+}
+// Non-PNQ denominator: l = alpha l + sum of the unquantized p of the tile.
+template <int D, int PNQ>
+__device__ __forceinline__ void l_plain(WaveState<D>& w, int u, const TileStats& ts, float vsum) {
+  if (!PNQ) w.lsum[u] = fmaf(w.lsum[u], ts.alpha, __builtin_amdgcn_ldexpf(vsum, ts.X - 127));
+}
+// One S^T matrix instruction: key subtile t of query tile with operand qop.
+__device__ __forceinline__ void s_one(v4f (&s)[kSub], int t, const uint4 (&kop)[kSub], const uint2& ksc,
+                                      const uint4& qop, int qsc, const v4f& cneg) {
+  s[t] = mfma_fp4_sel(kop[t], qop, cneg, t < 4 ? ksc.x : ksc.y, t & 3, qsc);
+}
 
-  pv_tile<D, PNQ>(w, 0, pop0, t0, vsum0, vop, vsc);
-  const uint4 pop1 = p_tile<PNQ>(s1, sl2, t1.kofs, vsum1);
-  interleave_mfma_valu<NT + PNQ, 6>();
-  dump_tile<DUMP>(a, bh, qrow[1], visit, j0, grp, pop1, t1.X);
+// Steps 1 / 3: P~V of the other tile (NPV matrix instructions) beside the
+// row max and block scales of tile u (a dependent chain of vector work).
+template <int D, int UOS, int PNQ, int MASK>
+__device__ __forceinline__ TileStats stats_step(WaveState<D>& w, int u, v4f (&s)[kSub], int lim, int uo,
+                                               const uint4& pop, const TileStats& to, float vo,
+                                               const VOps<D>& vv, float sl2) {
+  constexpr int NT = D / 16;
+  if (MASK) mask_tile(s, lim);
+  fence();
+  pv_one<D, PNQ>(w, uo, 0, pop, to.X, vv);
+  float a[kSub];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pin_out(a[t]);
+  fence();
+  pv_one<D, PNQ>(w, uo, 1, pop, to.X, vv);
+#pragma unroll
+  for (int t = 4; t < 8; ++t) a[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
+#pragma unroll
+  for (int t = 4; t < 8; ++t) pin_out(a[t]);
+  fence();
+  pv_one<D, PNQ>(w, uo, 2, pop, to.X, vv);
+  float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  float b2 = fmaxf(fmaxf(a[6], a[7]), s[0][3]);
+  pin_out(b0);
+  pin_out(b1);
+  pin_out(b2);
+  fence();
+  pv_one<D, PNQ>(w, uo, 3, pop, to.X, vv);
+  const float b3 = fmaxf(fmaxf(s[1][3], s[2][3]), s[3][3]);
+  const float b4 = fmaxf(fmaxf(s[4][3], s[5][3]), s[6][3]);
+  const float c0 = fmaxf(fmaxf(b0, b1), b2);
+  const float c1 = fmaxf(fmaxf(b3, b4), s[7][3]);
+  float bmax = fmaxf(c0, c1);
+  pin_out(bmax);
+  fence();
+  if (NT > 4) pv_one<D, PNQ>(w, uo, 4, pop, to.X, vv);
+  // across the four lanes holding this query
+  auto x1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+  float r1 = fmaxf(__uint_as_float(x1[0]), __uint_as_float(x1[1]));
+  pin_out(r1);
+  fence();
+  if (NT > 5) pv_one<D, PNQ>(w, uo, 5, pop, to.X, vv);
+  auto x2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1), __float_as_uint(r1), false, false);
+  const float rowmax = fmaxf(__uint_as_float(x2[0]), __uint_as_float(x2[1]));
+  // delta = new max - mref.  Before the first tile the running max is -inf
+  // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
+  float delta = fmaxf(w.m[u] - w.mref[u], rowmax);
+  pin_out(delta);
+  fence();
+  if (NT > 6) pv_one<D, PNQ>(w, uo, 6, pop, to.X, vv);
+  TileStats r;
+  r.alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);  // 0 at first
+  w.m[u] = w.mref[u] + delta;
+  w.mref[u] = w.m[u];
+  // scale of this lane's P~ block (the block holding the row maximum gets
+  // x = 0 exactly); log2 v = d*c - (delta*c + e) in the scaled domain
+  const float x = (bmax - delta) * sl2;
+  float e = PNQ == 2 ? efq_block_exp(x) : p_block_exp<UOS>(x);
+  pin_out(e);
+  fence();
+  if (NT > 7) pv_one<D, PNQ>(w, uo, 7, pop, to.X, vv);
+  r.X = static_cast<int>(e) + 127;
+  r.kofs = PNQ == 2 ? kEfqBeta - 2.0f * fmaf(delta, sl2, e) : fmaf(delta, sl2, e);
+  l_plain<D, PNQ>(w, uo, to, vo);
+  fence();
+  pv_one<D, PNQ>(w, uo, NT, pop, to.X, vv);
+  fence();
+  return r;
+}
 
-  pv_tile<D, PNQ>(w, 1, pop1, t1, vsum1, vop, vsc);
+// Steps 2 / 4: S^T of query tile us (eight matrix instructions) beside P~
+// of tile u (per score one FMA, one exp2, half an FP4 conversion).
+template <int D, int PNQ>
+__device__ __forceinline__ uint4 ptile_step(v4f (&sn)[kSub], const KOps<D>& kk, const uint4& qop, int qsc,
+                                           float mref, const v4f (&s)[kSub], float sl2, float kofs,
+                                           float& vsum) {
+  const v4f cneg = {-mref, -mref, -mref, -mref};
+  uint32_t pw[4];
+  vsum = 0.0f;
+  fence();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t b = 0;
+    s_one(sn, 2 * q, kk.op, kk.sc, qop, qsc, cneg);
+    p_half<PNQ, 0>(s, q, sl2, kofs, pw[q], b, vsum);
+    pin_out(pw[q]);
+    if (PNQ == 2) pin_out(b);
+    if (!PNQ) pin_out(vsum);
+    fence();
+    s_one(sn, 2 * q + 1, kk.op, kk.sc, qop, qsc, cneg);
+    p_half<PNQ, 1>(s, q, sl2, kofs, pw[q], b, vsum);
+    pin_out(pw[q]);
+    if (!PNQ) pin_out(vsum);
+    fence();
+  }
+  return make_uint4(pw[0], pw[1], pw[2], pw[3]);
+}
+
+template <int D, int UOS, int PNQ, int DUMP, int MASK>
+__device__ __forceinline__ void kv_step(WaveState<D>& w, Pipe<D, UOS, PNQ>& p, const uint8_t* st_cur,
+                                        const uint8_t* st_next, const uint4 (&qop)[kQT], const int (&qsc)[kQT],
+                                        const int (&qrow)[kQT], const int (&klim)[kQT], bool visit, int j0,
+                                        int lane, float sl2, const MxAttnArgs& a, int64_t bh) {
+  const int grp = lane >> 4;
+
+  // ---- step 1: P~V of B (tile j-1) | stats of A (tile j).  At tile 0, P~
+  // of B is all zero codes (alpha 1, sum 0): the products add nothing.
+  p.tA = stats_step<D, UOS, PNQ, MASK>(w, 0, p.sA, klim[0] - (j0 + grp * 32), 1, p.pB, p.tB, p.vB, p.vv,
+                                       sl2);
+  rescale_o<D, PNQ>(w, 0, p.tA.alpha);
+
+  // ---- step 2: S^T of B (tile j) | P~ of A (tile j); V~ of tile j
+  read_v<D>(p.vv, st_cur, lane);
+  p.pA = ptile_step<D, PNQ>(p.sB, p.kk, qop[1], qsc[1], w.mref[1], p.sA, sl2, p.tA.kofs, p.vA);
+  dump_tile<DUMP>(a, bh, qrow[0], visit, j0, grp, p.pA, p.tA.X);
+
+  // ---- step 3: P~V of A (tile j) | stats of B (tile j); K~ of tile j+1
+  read_k<D>(p.kk, st_next, lane);
+  p.tB = stats_step<D, UOS, PNQ, MASK>(w, 1, p.sB, klim[1] - (j0 + grp * 32), 0, p.pA, p.tA, p.vA, p.vv,
+                                       sl2);
+  rescale_o<D, PNQ>(w, 1, p.tB.alpha);
+
+  // ---- step 4: S^T of A (tile j+1) | P~ of B (tile j)
+  p.pB = ptile_step<D, PNQ>(p.sA, p.kk, qop[0], qsc[0], w.mref[0], p.sB, sl2, p.tB.kofs, p.vB);
+  dump_tile<DUMP>(a, bh, qrow[1], visit, j0, grp, p.pB, p.tB.X);
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
@@ -397,6 +627,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[IMG];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[IMG];
   static_assert(kStages == 3, "one LDS object per stage");
+  // stage of ring position i (a constant after unrolling)
+  auto lds_stage = [&](int i) -> uint8_t* {
+    const int r = i % kStages;
+    return r == 0 ? lds0 : r == 1 ? lds1 : lds2;
+  };
   constexpr int DC = D / 32;  // 32-element blocks per Q~ row
   constexpr int NT = D / 16;  // output channel tiles
 
@@ -501,34 +736,75 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   const uint8_t* img = a.img + bg * nt * static_cast<int64_t>(IMG);
   const int nl = loads_per_tile<D>(wave);
 
-  // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  At the
-  // top of iteration jt the wave waits for its own loads of tile jt (the
-  // loads of tile jt+1 may stay in flight), then the barrier makes every
-  // wave's loads of tile jt visible and releases the stage of tile jt-1,
-  // which the loads of tile jt+2 then refill.
+  // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  Tiles 0
+  // and 1 are requested up front, and S^T of A for tile 0 is formed once
+  // tile 0 has landed.  At the top of iteration jt the wave waits for all
+  // its loads (those of tile jt+1, requested an iteration earlier); the
+  // barrier then makes every wave's loads visible and tells that every wave
+  // has finished iteration jt-1, the last to read the stage of tile jt-1
+  // (its V~, in step 2), which the loads of tile jt+2 then refill.
   issue_tile<D>(lds0, img, wave, lane);
-  if (ntiles > 1) issue_tile<D>(lds1, img + IMG, wave, lane);
-  for (int jb = 0; jb < ntiles; jb += kStages) {
+  if (ntiles > 1) {
+    issue_tile<D>(lds1, img + IMG, wave, lane);
+    if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else wait_vmcnt<3>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  Pipe<D, UOS, PNQ> p;
+  // P~ of B before tile 0: zero codes under scale 1 against zero V~ operands
+  p.pB = make_uint4(0, 0, 0, 0);
+  p.tB.alpha = 1.0f;
+  p.tB.kofs = 0.0f;
+  p.tB.X = 127;
+  p.vA = 0.0f;
+  p.vB = 0.0f;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) p.vv.op[n] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int n = 0; n < (NT + 3) / 4; ++n) p.vv.sc[n] = 0x7F7F7F7Fu;
+  read_k<D>(p.kk, lds0, lane);
+  s_tile(p.sA, p.kk.op, p.kk.sc, qop[0], qsc[0], w.mref[0]);
+
+  // tiles [0, nmain): no key masked; the ring position of each is a
+  // compile-time constant (the loop is unrolled by the stage count)
+  for (int jb = 0; jb < nmain; jb += kStages) {
 #pragma unroll
     for (int k = 0; k < kStages; ++k) {
       const int jt = jb + k;
-      if (jt < ntiles) {
-        if (jt + 1 < ntiles) {
-          if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else wait_vmcnt<3>();
-        } else {
-          wait_vmcnt<0>();
-        }
+      if (jt < nmain) {
+        wait_vmcnt<0>();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        uint8_t* nxt = k == 0 ? lds2 : k == 1 ? lds0 : lds1;  // stage of tile jt + 2
-        if (jt + 2 < ntiles) issue_tile<D>(nxt, img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
-        const uint8_t* st = k == 0 ? lds0 : k == 1 ? lds1 : lds2;
-        compute_tile<D, UOS, PNQ, DUMP>(w, st, qop, qsc, qrow, klim, jt >= nmain, jt <= last_w,
-                                        jt * kKvTile, lane, sl2, a, bh);
+        if (jt + 2 < ntiles)
+          issue_tile<D>(lds_stage(k + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
+        kv_step<D, UOS, PNQ, DUMP, 0>(w, p, lds_stage(k), lds_stage(k + 1), qop, qsc, qrow, klim,
+                                      jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
       }
     }
   }
+  // tiles [nmain, ntiles): the sequence end or the causal diagonal (one or
+  // two tiles), keys masked per row; stages picked at run time
+  for (int jt = nmain; jt < ntiles; ++jt) {
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (jt + 2 < ntiles)
+      issue_tile<D>(lds_stage(jt + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
+    // every load of the ring has landed here except tile jt+2's, which
+    // targets neither stage read below
+    kv_step<D, UOS, PNQ, DUMP, 1>(w, p, lds_stage(jt), lds_stage(jt + 1), qop, qsc, qrow, klim,
+                                  jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
+  }
+  // P~V of B for the last tile (its V~ still in registers)
+#pragma unroll
+  for (int n = 0; n <= NT; ++n) pv_one<D, PNQ>(w, 1, n, p.pB, p.tB.X, p.vv);
+  l_plain<D, PNQ>(w, 1, p.tB, p.vB);
 
   // The epilogue stores under a per-lane condition.  Pin the accumulators
   // here so that the matrix-core instructions producing them are not moved
