@@ -114,20 +114,28 @@ int mxq_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n,
                    int out_dtype, void *y, void *stream);
 
 /*
- * Workspace needed by mxattn_fwd for these sizes and mode (bytes; 0 for
- * invalid arguments).  The workspace holds the quantized operands (MX modes)
- * or the 16-bit operands (FP16 mode).
+ * Workspace needed by mxattn_fwd (and mxattn_prepare, mxattn_fwd_prepared,
+ * mxattn_fwd_varlen without a dump) for these sizes and mode (bytes; 0 for
+ * invalid arguments).  The workspace holds the quantized K/V operands (MX
+ * modes: the KV tile images) or the 16-bit operands (FP16 mode).
+ * mxattn_dump_workspace_bytes: the larger workspace of the dump entry points
+ * (mxattn_fwd_dump, mxattn_fwd_varlen with a dump), which also receives the
+ * kernel's Q~; 0 for the FP16 mode, which has no dump.
  */
 size_t mxattn_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                               int dtype, int mode);
+size_t mxattn_dump_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv,
+                                   int D, int dtype, int mode);
 
 /*
  * Where the quantized operands of an MX mode lie inside the workspace (host
  * array `off` of 6 entries):
+ *   off[2] KV tile images [B][Hkv][skv_ld/128][off[3]], at offset 0
  *   off[0] Q~ codes [B][Hq][Sq][D/2]      off[1] Q~ scales [B][Hq][Sq][D/32]
- *          (written only by the dump entry points: the attention kernels
- *          quantize Q themselves, and the dump variants store that Q~ here)
- *   off[2] KV tile images [B][Hkv][skv_ld/128][off[3]]
+ *          after the images, inside the dump workspace only (written only
+ *          by the dump entry points: the attention kernels quantize Q
+ *          themselves, and the dump variants store that Q~ here; the
+ *          short-query workspace always holds these regions)
  *   off[3] bytes per image (17408 for D = 128, 13312 for D = 64)
  *   off[4] = off[5] = 0
  * and *skv_ld (host) = Skv rounded up to a multiple of the 128-key tile.
@@ -218,7 +226,8 @@ int mxattn_fwd_prepared(const void *q, const void *k, int dtype, int B,
  * [nslots][skv_ld/2] and p_scales [nslots][skv_ld/32] receive, for every
  * key block a slot's row visits, its packed codes and E8M0 byte; blocks the
  * row never visits (beyond the causal diagonal tile) are left untouched.
- * The kernel's Q~ (every row) is stored at off[0] / off[1] of the workspace.
+ * The kernel's Q~ (every row) is stored at off[0] / off[1] of the workspace,
+ * which must hold mxattn_dump_workspace_bytes(...) bytes (MX_ERR_WORKSPACE).
  */
 int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
                     int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
@@ -289,7 +298,8 @@ int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
  *
  * mxattn_fwd_varlen: the prefill form (per-entry query and key lengths); MX
  * modes only (MXATTN_FP16 gives MX_ERR_UNSUPPORTED); Sq and Skv may differ
- * also when causal.  Workspace as for mxattn_fwd.
+ * also when causal.  Workspace as for mxattn_fwd (mxattn_fwd_dump's size
+ * with a dump).
  * mxattn_decode_varlen: the short-query form (every entry has Sq query
  * rows, seqlens_k[b] keys: a padded KV cache), split as mxattn_decode with
  * the split size of the padded Skv; workspace as for mxattn_decode.

@@ -28,7 +28,8 @@ RULES = {"ocp": MXQ_OCP, "uos": MXQ_UOS}
 # Symbols the header declares; the CPU tests check the library exports them.
 EXPORTS = (
     "mx_strerror", "mxq_quantize", "mxq_quantize_t", "mxq_dequantize",
-    "mxattn_workspace_bytes", "mxattn_workspace_layout", "mxattn_kv_tile",
+    "mxattn_workspace_bytes", "mxattn_dump_workspace_bytes", "mxattn_workspace_layout",
+    "mxattn_kv_tile",
     "mxattn_fwd", "mxattn_fwd_dump", "mxattn_prepare", "mxattn_fwd_prepared", "mxgemm",
     "mxgemm_workspace_bytes", "mxattn_decode_split", "mxattn_decode_workspace_bytes",
     "mxattn_decode", "mxattn_decode_prepared", "mxattn_decode_dump", "mxattn_fwd_varlen",
@@ -63,6 +64,8 @@ def lib():
     L.mxq_dequantize.argtypes = [P, P, i64, ci, P, P]
     L.mxattn_workspace_bytes.argtypes = [ci] * 8
     L.mxattn_workspace_bytes.restype = sz
+    L.mxattn_dump_workspace_bytes.argtypes = [ci] * 8
+    L.mxattn_dump_workspace_bytes.restype = sz
     L.mxattn_workspace_layout.argtypes = [ci] * 8 + [ctypes.POINTER(sz), ctypes.POINTER(i64)]
     L.mxattn_kv_tile.argtypes = [ci, ci]
     L.mxattn_fwd.argtypes = [P, P, P] + [ci] * 9 + [P, P, sz, P]
@@ -248,15 +251,19 @@ def kv_tile(D: int, mode="uos_pnq") -> int:
     return r
 
 
-def workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dtype, mode) -> int:
+def workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dtype, mode, dump=False) -> int:
+    """Workspace of attn_fwd (``dump``: of the dump entry points, which also
+    store the kernel's Q~)."""
     dt = MX_BF16 if dtype in (torch.bfloat16, "bf16", MX_BF16) else MX_F32
-    return lib().mxattn_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, dt, _mode(mode, MODES))
+    f = lib().mxattn_dump_workspace_bytes if dump else lib().mxattn_workspace_bytes
+    return f(B, Hq, Hkv, Sq, Skv, D, dt, _mode(mode, MODES))
 
 
 def workspace_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode):
-    """([Q~ codes offset, Q~ scales offset, KV tile images offset, bytes per
-    image, 0, 0], skv_ld) — for reading the quantized operands back (image
-    layout in include/mxattn.h)."""
+    """([Q~ codes offset, Q~ scales offset, KV tile images offset (0), bytes
+    per image, 0, 0], skv_ld) — for reading the quantized operands back
+    (image layout in include/mxattn.h; the Q~ regions exist in a dump-sized
+    workspace)."""
     dt = MX_BF16 if dtype in (torch.bfloat16, "bf16", MX_BF16) else MX_F32
     off = (ctypes.c_size_t * 6)()
     ld = ctypes.c_int64()
@@ -265,9 +272,9 @@ def workspace_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode):
     return list(off), ld.value
 
 
-def alloc_workspace(q, k, mode):
+def alloc_workspace(q, k, mode, dump=False):
     B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, k_data=False)
-    nb = workspace_bytes(B, Hq, Hkv, Sq, Skv, D, q.dtype, mode)
+    nb = workspace_bytes(B, Hq, Hkv, Sq, Skv, D, q.dtype, mode, dump)
     if nb == 0:
         raise ValueError("invalid attention shape")
     # torch's caching allocator returns >= 512-byte aligned blocks
@@ -331,7 +338,7 @@ def attn_fwd_dump(q, k, v, rows, *, causal=False, mode="uos_pnq", workspace=None
     n, slot, pc, ps = _dump_buffers(q, rows, B, Hq, Sq, (Skv + 127) // 128 * 128)
     out = _out(None, (B, Hq, Sq, D), q.device)
     if workspace is None:
-        workspace = alloc_workspace(q, k, mode)
+        workspace = alloc_workspace(q, k, mode, dump=True)
     _ws(workspace)
     _check("mxattn_fwd_dump", lib().mxattn_fwd_dump(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
@@ -511,7 +518,7 @@ def attn_fwd_varlen(q, k, v, seqlens_q, seqlens_k, *, causal=False, mode="uos_pn
     lq, lk = _lens(seqlens_q, B, q.device), _lens(seqlens_k, B, q.device)
     out = _out(out, (B, Hq, Sq, D), q.device, zero=True)
     if workspace is None:
-        workspace = alloc_workspace(q, k, mode)
+        workspace = alloc_workspace(q, k, mode, dump=rows is not None)
     _ws(workspace)
     slot = pc = ps = None
     if rows is not None:

@@ -18,10 +18,13 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int to_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// Byte layout of the workspace used by mxattn_fwd.
+// Byte layout of the workspace used by mxattn_fwd.  MX modes: the KV tile
+// images first, then the Q~ codes and E8M0 bytes that only the dump
+// variants write (total: images only; total_dump: with Q~).
 struct Layout {
   size_t off[6];  // MX: qc qs images img-bytes | FP16: images, q16
   size_t total;
+  size_t total_dump;
   int64_t skv_ld;
 };
 
@@ -79,32 +82,33 @@ Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, in
     const size_t nt = (static_cast<size_t>(Skv) + mxk::kF16KvTile - 1) / mxk::kF16KvTile;
     L.off[0] = take(static_cast<size_t>(B) * Hkv * nt * mxk::f16_img_bytes(D));  // K / V^T images
     if (dtype == MX_F32) L.off[1] = take(static_cast<size_t>(B) * Hq * Sq * D * 2);  // Q fp16
+    L.total = L.total_dump = cur;
   } else {
-    // one extra query tile of zero rows after Q~ so the last tile's loads
-    // stay inside the buffer
-    const size_t q_rows = static_cast<size_t>(B) * Hq * Sq + mxk::kMxQTile;
+    L.off[2] = take(static_cast<size_t>(B) * Hkv * (skv_ld / mxk::kKvTile) * mxk::img_bytes(D));
+    L.total = cur;
+    // the kernel's Q~ (dump variants only), one row per query row
+    const size_t q_rows = static_cast<size_t>(B) * Hq * Sq;
     L.off[0] = take(q_rows * D / 2);
     L.off[1] = take(q_rows * D / 32);
-    L.off[2] = take(static_cast<size_t>(B) * Hkv * (skv_ld / mxk::kKvTile) * mxk::img_bytes(D));
     L.off[3] = static_cast<size_t>(mxk::img_bytes(D));
     L.off[4] = 0;
     L.off[5] = 0;
+    L.total_dump = cur;
   }
-  L.total = cur;
   return L;
 }
 
 // Validation shared by every attention entry point.
 int check_attn_call(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
                     int Hkv, int Sq, int Skv, int D, int causal, int mode, const void* ws,
-                    size_t ws_bytes, bool need_qk, bool need_v, Layout* L) {
+                    size_t ws_bytes, bool need_qk, bool need_v, Layout* L, bool dump = false) {
   int st = check_attn_shape(dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode);
   if (st != MX_OK) return st;
   if ((need_qk && (!q || !k)) || (need_v && !v)) return MX_ERR_ARG;
   if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
     return MX_ERR_ALIGN;
   *L = make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode);
-  if (!ws || ws_bytes < L->total) return MX_ERR_WORKSPACE;
+  if (!ws || ws_bytes < (dump ? L->total_dump : L->total)) return MX_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MX_ERR_ALIGN;
   return MX_OK;
 }
@@ -182,12 +186,13 @@ int attn_common(const void* q, const void* k, const void* v, int dtype, int B, i
                 size_t ws_bytes, const int32_t* row_slot, uint8_t* p_codes,
                 uint8_t* p_scales, bool dump, void* stream) {
   Layout L;
+  if (dump && mode == MXATTN_FP16) return MX_ERR_ARG;
   int st = check_attn_call(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, ws, ws_bytes,
-                           true, true, &L);
+                           true, true, &L, dump);
   if (st != MX_OK) return st;
   if (!o) return MX_ERR_ARG;
   if (!aligned(o, 16)) return MX_ERR_ALIGN;
-  if (dump && (mode == MXATTN_FP16 || !row_slot || !p_codes || !p_scales)) return MX_ERR_ARG;
+  if (dump && (!row_slot || !p_codes || !p_scales)) return MX_ERR_ARG;
   if (dump && (!aligned(p_codes, 16) || !aligned(row_slot, 4))) return MX_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
   st = run_prepare(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, mode, L, ws, s);
@@ -236,7 +241,7 @@ int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D
 }
 
 struct DecodeLayout {
-  Layout L;        // Q~ and KV images as for mxattn_prepare
+  Layout L;        // KV images and Q~ as for mxattn_fwd_dump
   size_t part;     // partial states
   size_t total;
   int split_tiles, nsplit;
@@ -249,7 +254,9 @@ DecodeLayout make_decode_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, 
   dl.split_tiles = decode_split_tiles(B, Hkv, Skv);
   const int64_t nt = dl.L.skv_ld / mxk::kKvTile;
   dl.nsplit = static_cast<int>((nt + dl.split_tiles - 1) / dl.split_tiles);
-  dl.part = round_up(dl.L.total, 256);
+  // the Q~ regions of a decode shape are a few hundred bytes per query row:
+  // always reserved, the partial states follow them
+  dl.part = round_up(dl.L.total_dump, 256);
   dl.total = dl.part + static_cast<size_t>(B) * Hkv * dl.nsplit * 16 * (D + 2) * sizeof(float);
   return dl;
 }
@@ -367,6 +374,13 @@ size_t mxattn_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, in
                               int mode) {
   if (check_attn_shape(dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode) != MX_OK) return 0;
   return make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode).total;
+}
+
+size_t mxattn_dump_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                                   int mode) {
+  if (mode == MXATTN_FP16) return 0;
+  if (check_attn_shape(dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode) != MX_OK) return 0;
+  return make_layout(B, Hq, Hkv, Sq, Skv, D, dtype, mode).total_dump;
 }
 
 int mxattn_workspace_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
@@ -538,7 +552,7 @@ int mxattn_fwd_varlen(const void* q, const void* k, const void* v, int dtype, in
   // shape checks as for mxattn_fwd, except that causal queries are aligned
   // to the end of each sequence's keys, so Sq and Skv may differ
   st = check_attn_call(q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, 0, mode, workspace, ws_bytes,
-                       true, true, &L);
+                       true, true, &L, dump && mode != MXATTN_FP16);
   if (st != MX_OK) return st;
   if (mode == MXATTN_FP16) return MX_ERR_UNSUPPORTED;
   if (!o || !seqlens_q || !seqlens_k) return MX_ERR_ARG;

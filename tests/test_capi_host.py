@@ -73,6 +73,10 @@ def test_attention_rejects_bad_args():
     assert fwd(ws_bytes=16) == -3
     assert fwd(ws=None) == -3
     assert fwd(ws=ctypes.c_void_p((1 << 20) + 16)) == -5
+    # the dump entry point needs the larger (Q~-holding) workspace
+    nb = L.mxattn_workspace_bytes(1, 2, 1, 64, 64, 128, 1, 3)
+    assert L.mxattn_fwd_dump(P, P, P, 1, 1, 2, 1, 64, 64, 128, 0, 3, P, P,
+                             ctypes.c_size_t(nb), P, P, P, None) == -3
     # dump entry: FP16 mode has no P~ to dump
     assert L.mxattn_fwd_dump(P, P, P, 1, 1, 1, 1, 64, 64, 128, 0, 0, P, P,
                              ctypes.c_size_t(1 << 40), P, P, P, None) == -1
@@ -84,12 +88,16 @@ def test_workspace_and_tile_queries():
     assert L.mxattn_kv_tile(96, 3) == -2
     assert L.mxattn_workspace_bytes(1, 2, 1, 64, 64, 96, 1, 3) == 0
     nb = L.mxattn_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
-    # Q~ + K~ + V~^T at 0.53125 bytes per element, plus padding
-    assert 3 * 40 * 32760 * 128 * 17 // 32 <= nb < 3 * 40 * 32768 * 128 * 17 // 32 + 4096 * 128
+    # K~ + V~^T tile images: 17408 bytes per 128 keys (0.53125 B per element
+    # each, rounded up to 1 KiB per image); the Q~ regions only in the dump size
+    assert nb == 40 * 256 * 17408
+    nd = L.mxattn_dump_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
+    assert nd >= nb + 40 * 32760 * 128 * 17 // 32
     off, ld = mx.workspace_layout(1, 40, 40, 32760, 32760, 128, "bf16", "uos_pnq")
-    assert ld == 32768 and off[0] < off[1] < off[2] and off[3:] == [17408, 0, 0]
+    assert ld == 32768 and off[2] == 0 and nb <= off[0] < off[1] and off[3:] == [17408, 0, 0]
     assert all(o % 256 == 0 for o in off[:3])
-    assert off[2] + 40 * 256 * 17408 <= nb
+    assert off[1] + 40 * 32760 * 4 <= nd
+    assert L.mxattn_dump_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 0) == 0  # FP16
     off64, _ = mx.workspace_layout(1, 2, 2, 100, 100, 64, "f32", "ocp")
     assert off64[3] == 13312
     with pytest.raises(mx.MxError):
