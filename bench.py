@@ -163,60 +163,60 @@ def read_traffic(sha: str, workload: str, kernel="attn_mx_kernel"):
     return entry.get("hbm_bytes_per_launch")
 
 
-def bench_quantizer(torch, mx, reps=20):
+def bench_quantizer(torch, mx, reps=21, copies=3):
+    """Quantize / dequantize the roundtrip tensor.  The timed loops rotate
+    over ``copies`` distinct copies of it (flipped along rows: the same
+    values at other addresses, 1.4 GB of input for three), so no pass finds
+    its input in the 256 MB Infinity Cache left by the previous one."""
     import mxsynth
     log("[bench] quantizer: generating the 8192 x 28672 bf16 roundtrip tensor")
     x = mxsynth.roundtrip_tensor(2)
-    xt = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    x0 = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
     del x
-    n = xt.numel()
-    codes = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
-    scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
-    y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    xs = [x0] + [torch.flip(x0, dims=(0,)).contiguous() if i % 2 else x0.clone()
+                 for i in range(1, copies)]
+    n = x0.numel()
+    codes = [torch.empty(n // 2, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    scales = [torch.empty(n // 32, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    ys = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
     q_bytes = n * 2 + n // 2 + n // 32
     res = {"workload": "8192x28672 bf16, Student-t(3)*0.02 with 0.1% x50 outliers, blocks of 32 "
-                       "along the last dim", "bytes_per_pass": q_bytes}
-    # achievable streaming ceiling: a plain device-to-device copy of the same
-    # tensor (read + write of n bf16 elements)
-    warm(torch, lambda: y.copy_(xt.reshape(-1)))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        y.copy_(xt.reshape(-1))
-    e1.record()
-    torch.cuda.synchronize()
-    copy_ms = e0.elapsed_time(e1) / reps
-    copy_gbps = 2 * n * 2 / copy_ms / 1e6
-    res["d2d_copy_ceiling"] = {"ms": copy_ms, "gbps": copy_gbps,
-                               "frac_hbm": copy_gbps / HBM_PEAK_GBPS}
-    for rule in ("uos", "ocp"):
-        warm(torch, lambda: mx.quantize(xt, rule, codes, scales))
+                       "along the last dim", "bytes_per_pass": q_bytes,
+           "rotation": f"{copies} distinct input copies ({copies * n * 2 / 1e9:.2f} GB) taken in "
+                       f"turn by the timed passes"}
+
+    def timed(fn):
+        warm(torch, lambda: [fn(i) for i in range(copies)])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(reps):
-            mx.quantize(xt, rule, codes, scales)
+        for r in range(reps):
+            fn(r % copies)
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        mx.dequantize(codes, scales, out=y)
-        xf = xt.float().reshape(-1)
-        err = (torch.linalg.vector_norm((xf - y.float()).double()) /
+        return e0.elapsed_time(e1) / reps
+
+    # streaming ceilings on the same tensors: a device-to-device copy (read
+    # and write n bf16 elements) and a read-mostly pass (a max reduction)
+    copy_ms = timed(lambda i: ys[i].copy_(xs[i].reshape(-1)))
+    copy_gbps = 2 * n * 2 / copy_ms / 1e6
+    red_ms = timed(lambda i: torch.amax(xs[i]))
+    res["d2d_copy_ceiling"] = {"ms": copy_ms, "gbps": copy_gbps, "frac_hbm": copy_gbps / HBM_PEAK_GBPS}
+    res["read_reduction"] = {"kernel": "torch.amax over the tensor (a library reduction, not a "
+                                       "tuned streaming kernel: a lower bound on the read rate)",
+                             "ms": red_ms,
+                           "gbps": n * 2 / red_ms / 1e6, "frac_hbm": n * 2 / red_ms / 1e6 / HBM_PEAK_GBPS}
+    for rule in ("uos", "ocp"):
+        ms = timed(lambda i: mx.quantize(xs[i], rule, codes[i], scales[i]))
+        mx.dequantize(codes[0], scales[0], out=ys[0])
+        xf = x0.float().reshape(-1)
+        err = (torch.linalg.vector_norm((xf - ys[0].float()).double()) /
                torch.linalg.vector_norm(xf.double())).item()
         res[rule] = {"quantize_ms": ms, "gbps": q_bytes / ms / 1e6,
                      "frac_hbm": q_bytes / ms / 1e6 / HBM_PEAK_GBPS,
                      "frac_copy_ceiling": q_bytes / ms / 1e6 / copy_gbps, "rel_frobenius": err}
         del xf
-    warm(torch, lambda: mx.dequantize(codes, scales, out=y))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        mx.dequantize(codes, scales, out=y)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms = timed(lambda i: mx.dequantize(codes[i], scales[i], out=ys[i]))
     res["dequantize_bf16"] = {"ms": ms, "gbps": q_bytes / ms / 1e6,
                               "frac_hbm": q_bytes / ms / 1e6 / HBM_PEAK_GBPS,
                               "frac_copy_ceiling": q_bytes / ms / 1e6 / copy_gbps}
