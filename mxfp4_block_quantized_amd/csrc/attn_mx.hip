@@ -141,17 +141,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
 
+// A wave-uniform address kept in scalar registers, so that a direct load
+// takes the scalar-base + 32-bit lane-offset form (one VGPR per lane for
+// every load instead of a 64-bit address each).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Issue the direct loads of one KV tile image into an LDS stage: wave w
 // moves the 1 KiB rows w, w + kWaves, ... of the image, lane l bytes
 // [16 l, 16 l + 16) of each.
 template <int D>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* src, int wave, int lane) {
   constexpr int NL = img_bytes(D) / 1024;
+  const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
   for (int i = 0; i < (NL + kWaves - 1) / kWaves; ++i) {
     const int row = wave + i * kWaves;
     if (row < NL)
-      __builtin_amdgcn_global_load_lds(src + row * 1024 + lane * 16, stage + row * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(uniform_ptr(src + row * 1024) + lo, stage + row * 1024, 16, 0, 0);
   }
 }
 
@@ -641,17 +652,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin
   // over the 8 XCDs (each with its own L2), workgroup i to XCD i % 8.  Each
   // XCD is given a contiguous run of a list of (KV group, query head of the
-  // group, query tile), so a KV head's K~/V~ tile images are fetched from
+  // group, query tile or causal pair), so a KV head's K~/V~ tile images are fetched from
   // HBM by one XCD (two at a run boundary) instead of all eight.  With
   // per-sequence lengths the KV groups gg = b * Hkv + g are listed in the
   // order of (gg % 8, gg / 8): each XCD then holds groups of every batch
   // entry, which keeps the XCDs equally loaded when the entries' lengths
   // differ (with equal lengths the plain order is kept).
+  // Causal: one workgroup takes the query tiles p and nqb-1-p of a head
+  // (nqb+1 KV tiles in all, the longer one first), so every workgroup of a
+  // head does the same work and the fixed cost per workgroup is spread over
+  // twice the tiles.
+  const int nslot = CAUSAL ? (nqb + 1) / 2 : nqb;  // workgroups per query head
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int gi = (nwg >> 3) * xcd + min(xcd, nwg & 7) + (static_cast<int>(blockIdx.x) >> 3);
   const int G = a.Hq / a.Hkv;
-  const int per_group = G * nqb;
+  const int per_group = G * nslot;
   const int ngroups = a.B * a.Hkv;
   const int pos = gi / per_group;  // position of the KV group in that order
   const int rem = gi - pos * per_group;
@@ -667,11 +683,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   }
   const int b = gg / a.Hkv;
   const int g = gg - b * a.Hkv;
-  const int h = g * G + rem / nqb;
-  // causal: the longest query tiles of a head first
-  const int qb = CAUSAL ? nqb - 1 - rem % nqb : rem % nqb;
-  const int q0 = qb * kMxQTile;
-  const int qw0 = q0 + wave * (kQT * 16);  // first query row of this wave
+  const int h = g * G + rem / nslot;
+  const int slot = rem % nslot;
+  const int njobs = (CAUSAL && 2 * slot + 1 != nqb) ? 2 : 1;
   const int col = lane & 15;   // query column within a 16-query tile
   const int grp = lane >> 4;   // K-block / lane group
 
@@ -688,156 +702,173 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     sq = min(max(__builtin_amdgcn_readfirstlane(a.lens_q[b]), 0), a.Sq);
     if (skv == 0 || (CAUSAL && sq > skv)) sq = 0;
   }
-  if (q0 >= sq) return;  // whole workgroup, before any barrier
   const int koff = CAUSAL ? skv - sq : 0;  // causal: row i sees keys j <= i + koff
 
-  // Q~ operands (B of S^T): query column `col`, d-block `grp`, quantized
-  // here; rows past the sequence (and d-blocks past D) are zero codes.
-  uint4 qop[kQT];
-  int qsc[kQT];
-  int qrow[kQT];
-#pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    qrow[t] = qw0 + t * 16 + col;
-    qop[t] = make_uint4(0, 0, 0, 0);
-    qsc[t] = 127;
-    if (grp < DC && qrow[t] < sq)
-      quant_q_block<D, UOS, DUMP>(a, bh * a.Sq + qrow[t], grp, qop[t], qsc[t]);
-  }
-
-  WaveState<D> w;
-#pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    w.m[t] = -INFINITY;
-    w.mref[t] = 0.0f;
-    w.lsum[t] = 0.0f;
-    w.lacc[t] = v4f{0, 0, 0, 0};
-#pragma unroll
-    for (int n = 0; n < NT; ++n) w.oacc[t][n] = v4f{0, 0, 0, 0};
-  }
-
-  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
-  const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
-  // tiles this workgroup visits: all, or up to its last causal diagonal tile
-  const int ntiles = CAUSAL ? min(ntk, (q0 + kMxQTile - 1 + koff) / kKvTile + 1) : ntk;
-  // Tiles [0, nmain) are unmasked for every wave (whole tiles at or below
-  // the first row's limit); the rest are computed masked.  A wave dumps P~
-  // only up to its own last tile (the sequence end, or the causal limit of
-  // its last row); a wave whose rows all lie past the sequence dumps none.
-  const int nmain = CAUSAL ? min((q0 + koff + 1) / kKvTile, skv / kKvTile) : skv / kKvTile;
-  const int last_w = qw0 >= sq ? -1 : (CAUSAL ? min((qw0 + kQT * 16 - 1 + koff) / kKvTile, ntk - 1) : ntk - 1);
-  int klim[kQT];
-#pragma unroll
-  for (int t = 0; t < kQT; ++t) {
-    klim[t] = CAUSAL ? min(skv - 1, qrow[t] + koff) : skv - 1;
-    if (qrow[t] >= sq) qrow[t] = a.Sq;  // past the sequence: never dumped or stored
-  }
-
-  const uint8_t* img = a.img + bg * nt * static_cast<int64_t>(IMG);
-  const int nl = loads_per_tile<D>(wave);
-
-  // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  Tiles 0
-  // and 1 are requested up front, and S^T of A for tile 0 is formed once
-  // tile 0 has landed.  At the top of iteration jt the wave waits for all
-  // its loads (those of tile jt+1, requested an iteration earlier); the
-  // barrier then makes every wave's loads visible and tells that every wave
-  // has finished iteration jt-1, the last to read the stage of tile jt-1
-  // (its V~, in step 2), which the loads of tile jt+2 then refill.
-  issue_tile<D>(lds0, img, wave, lane);
-  if (ntiles > 1) {
-    issue_tile<D>(lds1, img + IMG, wave, lane);
-    if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else wait_vmcnt<3>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-
-  Pipe<D, UOS, PNQ> p;
-  // P~ of B before tile 0: zero codes under scale 1 against zero V~ operands
-  p.pB = make_uint4(0, 0, 0, 0);
-  p.tB.alpha = 1.0f;
-  p.tB.kofs = 0.0f;
-  p.tB.X = 127;
-  p.vA = 0.0f;
-  p.vB = 0.0f;
-#pragma unroll
-  for (int n = 0; n < NT; ++n) p.vv.op[n] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int n = 0; n < (NT + 3) / 4; ++n) p.vv.sc[n] = 0x7F7F7F7Fu;
-  read_k<D>(p.kk, lds0, lane);
-  s_tile(p.sA, p.kk.op, p.kk.sc, qop[0], qsc[0], w.mref[0]);
-
-  // tiles [0, nmain): no key masked; the ring position of each is a
-  // compile-time constant (the loop is unrolled by the stage count)
-  for (int jb = 0; jb < nmain; jb += kStages) {
-#pragma unroll
-    for (int k = 0; k < kStages; ++k) {
-      const int jt = jb + k;
-      if (jt < nmain) {
-        wait_vmcnt<0>();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (jt + 2 < ntiles)
-          issue_tile<D>(lds_stage(k + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
-        kv_step<D, UOS, PNQ, DUMP, 0>(w, p, lds_stage(k), lds_stage(k + 1), qop, qsc, qrow, klim,
-                                      jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
-      }
+  for (int job = 0; job < njobs; ++job) {
+    // the query tile of this job (causal: the longer one first)
+    const int qb = CAUSAL ? (job == 0 ? nqb - 1 - slot : slot) : slot;
+    const int q0 = qb * kMxQTile;
+    const int qw0 = q0 + wave * (kQT * 16);  // first query row of this wave
+    if (q0 >= sq) continue;  // whole workgroup (uniform), before any barrier of the job
+    // every wave is done with the previous job's stages before they refill
+    if (job > 0) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-  }
-  // tiles [nmain, ntiles): the sequence end or the causal diagonal (one or
-  // two tiles), keys masked per row; stages picked at run time
-  for (int jt = nmain; jt < ntiles; ++jt) {
-    wait_vmcnt<0>();
+
+    // Q~ operands (B of S^T): query column `col`, d-block `grp`, quantized
+    // here; rows past the sequence (and d-blocks past D) are zero codes.
+    uint4 qop[kQT];
+    int qsc[kQT];
+    int qrow[kQT];
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      qrow[t] = qw0 + t * 16 + col;
+      qop[t] = make_uint4(0, 0, 0, 0);
+      qsc[t] = 127;
+      if (grp < DC && qrow[t] < sq)
+        quant_q_block<D, UOS, DUMP>(a, bh * a.Sq + qrow[t], grp, qop[t], qsc[t]);
+    }
+
+    WaveState<D> w;
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      w.m[t] = -INFINITY;
+      w.mref[t] = 0.0f;
+      w.lsum[t] = 0.0f;
+      w.lacc[t] = v4f{0, 0, 0, 0};
+#pragma unroll
+      for (int n = 0; n < NT; ++n) w.oacc[t][n] = v4f{0, 0, 0, 0};
+    }
+
+    const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
+    const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
+    // tiles this workgroup visits: all, or up to its last causal diagonal tile
+    const int ntiles = CAUSAL ? min(ntk, (q0 + kMxQTile - 1 + koff) / kKvTile + 1) : ntk;
+    // Tiles [0, nmain) are unmasked for every wave (whole tiles at or below
+    // the first row's limit); the rest are computed masked.  A wave dumps P~
+    // only up to its own last tile (the sequence end, or the causal limit of
+    // its last row); a wave whose rows all lie past the sequence dumps none.
+    const int nmain = CAUSAL ? min((q0 + koff + 1) / kKvTile, skv / kKvTile) : skv / kKvTile;
+    const int last_w = qw0 >= sq ? -1 : (CAUSAL ? min((qw0 + kQT * 16 - 1 + koff) / kKvTile, ntk - 1) : ntk - 1);
+    int klim[kQT];
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      klim[t] = CAUSAL ? min(skv - 1, qrow[t] + koff) : skv - 1;
+      if (qrow[t] >= sq) qrow[t] = a.Sq;  // past the sequence: never dumped or stored
+    }
+
+    // wave-uniform (the divisions above run on the vector unit): scalar
+    // registers, so the tile loads take the scalar-base form
+    const uint8_t* img = uniform_ptr(a.img + bg * nt * static_cast<int64_t>(IMG));
+    const int nl = loads_per_tile<D>(wave);
+
+    // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  Tiles 0
+    // and 1 are requested up front, and S^T of A for tile 0 is formed once
+    // tile 0 has landed.  At the top of iteration jt the wave waits for all
+    // its loads (those of tile jt+1, requested an iteration earlier); the
+    // barrier then makes every wave's loads visible and tells that every wave
+    // has finished iteration jt-1, the last to read the stage of tile jt-1
+    // (its V~, in step 2), which the loads of tile jt+2 then refill.
+    issue_tile<D>(lds0, img, wave, lane);
+    if (ntiles > 1) {
+      issue_tile<D>(lds1, img + IMG, wave, lane);
+      if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else wait_vmcnt<3>();
+    } else {
+      wait_vmcnt<0>();
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (jt + 2 < ntiles)
-      issue_tile<D>(lds_stage(jt + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
-    // every load of the ring has landed here except tile jt+2's, which
-    // targets neither stage read below
-    kv_step<D, UOS, PNQ, DUMP, 1>(w, p, lds_stage(jt), lds_stage(jt + 1), qop, qsc, qrow, klim,
-                                  jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
-  }
-  // P~V of B for the last tile (its V~ still in registers)
-#pragma unroll
-  for (int n = 0; n <= NT; ++n) pv_one<D, PNQ>(w, 1, n, p.pB, p.tB.X, p.vv);
-  l_plain<D, PNQ>(w, 1, p.tB, p.vB);
 
-  // The epilogue stores under a per-lane condition.  Pin the accumulators
-  // here so that the matrix-core instructions producing them are not moved
-  // into that divergent region: an MFMA issued with part of EXEC disabled
-  // would drop the operands of the disabled lanes, which other lanes' results
-  // depend on.
+    Pipe<D, UOS, PNQ> p;
+    // P~ of B before tile 0: zero codes under scale 1 against zero V~ operands
+    p.pB = make_uint4(0, 0, 0, 0);
+    p.tB.alpha = 1.0f;
+    p.tB.kofs = 0.0f;
+    p.tB.X = 127;
+    p.vA = 0.0f;
+    p.vB = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kQT; ++u) {
+    for (int n = 0; n < NT; ++n) p.vv.op[n] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[u][n]));
-    asm volatile("" : "+v"(w.lacc[u]));
-  }
+    for (int n = 0; n < (NT + 3) / 4; ++n) p.vv.sc[n] = 0x7F7F7F7Fu;
+    read_k<D>(p.kk, lds0, lane);
+    s_tile(p.sA, p.kk.op, p.kk.sc, qop[0], qsc[0], w.mref[0]);
 
-  // ---- epilogue: O = O_acc / l ----
+    // tiles [0, nmain): no key masked; the ring position of each is a
+    // compile-time constant (the loop is unrolled by the stage count)
+    for (int jb = 0; jb < nmain; jb += kStages) {
 #pragma unroll
-  for (int u = 0; u < kQT; ++u) {
-    const float l = PNQ ? w.lacc[u][0] : xlane_sum4(w.lsum[u]);
-    const float inv = 1.0f / l;
-    if (qrow[u] < a.Sq) {
-      float* orow = a.o + (bh * a.Sq + qrow[u]) * D;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        float4 v = make_float4(w.oacc[u][n][0] * inv, w.oacc[u][n][1] * inv, w.oacc[u][n][2] * inv,
-                               w.oacc[u][n][3] * inv);
-        *reinterpret_cast<float4*>(orow + n * 16 + grp * 4) = v;
+      for (int k = 0; k < kStages; ++k) {
+        const int jt = jb + k;
+        if (jt < nmain) {
+          wait_vmcnt<0>();
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (jt + 2 < ntiles)
+            issue_tile<D>(lds_stage(k + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
+          kv_step<D, UOS, PNQ, DUMP, 0>(w, p, lds_stage(k), lds_stage(k + 1), qop, qsc, qrow, klim,
+                                        jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
+        }
       }
     }
-  }
+    // tiles [nmain, ntiles): the sequence end or the causal diagonal (one or
+    // two tiles), keys masked per row; stages picked at run time
+    for (int jt = nmain; jt < ntiles; ++jt) {
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (jt + 2 < ntiles)
+        issue_tile<D>(lds_stage(jt + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
+      // every load of the ring has landed here except tile jt+2's, which
+      // targets neither stage read below
+      kv_step<D, UOS, PNQ, DUMP, 1>(w, p, lds_stage(jt), lds_stage(jt + 1), qop, qsc, qrow, klim,
+                                    jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
+    }
+    // P~V of B for the last tile (its V~ still in registers)
+#pragma unroll
+    for (int n = 0; n <= NT; ++n) pv_one<D, PNQ>(w, 1, n, p.pB, p.tB.X, p.vv);
+    l_plain<D, PNQ>(w, 1, p.tB, p.vB);
+
+    // The epilogue stores under a per-lane condition.  Pin the accumulators
+    // here so that the matrix-core instructions producing them are not moved
+    // into that divergent region: an MFMA issued with part of EXEC disabled
+    // would drop the operands of the disabled lanes, which other lanes' results
+    // depend on.
+#pragma unroll
+    for (int u = 0; u < kQT; ++u) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[u][n]));
+      asm volatile("" : "+v"(w.lacc[u]));
+    }
+
+    // ---- epilogue: O = O_acc / l ----
+#pragma unroll
+    for (int u = 0; u < kQT; ++u) {
+      const float l = PNQ ? w.lacc[u][0] : xlane_sum4(w.lsum[u]);
+      const float inv = 1.0f / l;
+      if (qrow[u] < a.Sq) {
+        float* orow = a.o + (bh * a.Sq + qrow[u]) * D;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          float4 v = make_float4(w.oacc[u][n][0] * inv, w.oacc[u][n][1] * inv, w.oacc[u][n][2] * inv,
+                                 w.oacc[u][n][3] * inv);
+          *reinterpret_cast<float4*>(orow + n * 16 + grp * 4) = v;
+        }
+      }
+    }
+  }  // job
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
 hipError_t launch_t(const MxAttnArgs& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((a.Sq + kMxQTile - 1) / kMxQTile) * a.Hq * a.B);
+  const int nqb = (a.Sq + kMxQTile - 1) / kMxQTile;
+  // causal: query tiles in pairs (see attn_mx_kernel)
+  dim3 grid(static_cast<unsigned>(CAUSAL ? (nqb + 1) / 2 : nqb) * a.Hq * a.B);
   const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
   hipLaunchKernelGGL((attn_mx_kernel<D, UOS, PNQ, CAUSAL, DUMP>), grid, dim3(kThreads), 0, s, a, sl2);
   return hipGetLastError();

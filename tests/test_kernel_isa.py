@@ -5,10 +5,12 @@ held by other lanes.  If the compiler moves one into a region entered under a
 partial EXEC mask (e.g. the per-row store condition of the epilogue), the
 disabled lanes' operands are dropped and valid rows come out wrong.  The
 kernels pin their accumulators before such regions; this test checks, on the
-generated gfx950 assembly, that no MFMA sits inside the epilogue's store
-region (from the last s_and_saveexec before the kernel's s_endpgm to that
-s_endpgm; a loop the compiler lays out after s_endpgm is not part of it),
-and that the benchmarked kernels do not spill.
+generated gfx950 assembly, that no MFMA sits in a store's divergent region:
+walking back from each global store (the O rows, the P~ / Q~ dumps, the
+short-query partial states) to the nearest instruction that changes EXEC,
+no MFMA may be passed when that instruction is the s_and_saveexec opening
+the store's region.  It also checks that the benchmarked kernels do not
+spill.
 """
 import os
 import re
@@ -41,19 +43,32 @@ def kernels(asm):
         yield name, asm[m.end():end]
 
 
-def mfma_in_epilogue_region(body):
-    """MFMAs placed between the last s_and_saveexec that precedes the
-    kernel's (last) s_endpgm and that s_endpgm, i.e. inside the epilogue's
-    per-row store region (the last divergent region before every attention
-    kernel ends)."""
+def _writes_exec(t):
+    op = t.split()[0]
+    if op.startswith("s_and_saveexec") or op.startswith("s_or_saveexec"):
+        return True
+    parts = t.replace(",", " ").split()
+    return op.startswith("s_") and len(parts) > 1 and parts[1] == "exec"
+
+
+def mfma_in_store_regions(body):
+    """MFMAs between a global store and the s_and_saveexec that opens its
+    divergent region (no other EXEC change in between)."""
     lines = [l.strip() for l in body.splitlines()
              if l.strip() and not l.strip().startswith((";", ".", "//"))]
-    ends = [i for i, t in enumerate(lines) if t.split()[0] == "s_endpgm"]
-    end = ends[-1] if ends else len(lines)
-    saves = [i for i, t in enumerate(lines[:end]) if t.split()[0].startswith("s_and_saveexec")]
-    if not saves:
-        return []
-    return [t for t in lines[saves[-1]:end] if t.split()[0].startswith("v_mfma")]
+    found = []
+    for i, t in enumerate(lines):
+        if not t.startswith("global_store"):
+            continue
+        seen = []
+        for u in reversed(lines[:i]):
+            if _writes_exec(u):
+                if u.split()[0].startswith("s_and_saveexec"):
+                    found += seen
+                break
+            if u.startswith("v_mfma"):
+                seen.append(u)
+    return found
 
 
 def template_args(name):
@@ -79,7 +94,7 @@ def test_no_mfma_under_partial_exec(src, tmp_path):
     found = 0
     for name, body in kernels(asm):
         found += 1
-        assert not mfma_in_epilogue_region(body), name
+        assert not mfma_in_store_regions(body), name
     assert found > 0
 
 
@@ -96,3 +111,23 @@ def test_no_register_spills_in_benchmarked_kernels(src, tmp_path):
         else:
             scratch = int(m.group(1))
         assert scratch == 0, (name, scratch)
+
+
+def test_store_region_check_sees_a_moved_mfma():
+    """The check itself: an MFMA placed between a store's s_and_saveexec and
+    the store (the failure once seen) is reported; above the saveexec it is
+    not."""
+    bad = """
+     s_and_saveexec_b64 s[4:5], vcc
+     s_cbranch_execz .LBB0_2
+     v_mfma_scale_f32_16x16x128_f8f6f4 v[0:3], v[4:7], v[8:11], v[0:3], v12, v13
+     global_store_dwordx4 v[20:21], v[0:3], off
+    .LBB0_2:
+     s_or_b64 exec, exec, s[4:5]
+     s_endpgm
+    """
+    good = bad.replace(
+        "s_and_saveexec_b64 s[4:5], vcc\n     s_cbranch_execz .LBB0_2\n     v_mfma",
+        "v_mfma").replace("global_store", "s_and_saveexec_b64 s[4:5], vcc\n     global_store")
+    assert len(mfma_in_store_regions(bad)) == 1
+    assert mfma_in_store_regions(good) == []
