@@ -382,7 +382,7 @@ def cpu_model() -> str:
 
 
 # Query rows per head of the oracle sample: about 10-30 s of host work.
-CPU_ROWS_PER_HEAD = {"dit13": 512, "dit14": 2048, "llm_prefill": 1024}
+CPU_ROWS_PER_HEAD = {"dit13": 1024, "dit14": 2048, "llm_prefill": 1024}
 
 
 def cpu_baseline(q, k, v, c, name):
