@@ -151,15 +151,23 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 
 __device__ __forceinline__ void issue_stage(uint8_t* st, const LoadPtrs& lp, int64_t off, bool half,
                                             int wave) {
-  const uint8_t* ab = uniform_ptr(lp.abase + off);
-  const uint8_t* bb = uniform_ptr(lp.bbase + off);
+  // Buffer loads over the stage's row bases (every offset is in range by
+  // construction).  Not the global form: with a global load-to-LDS in
+  // flight the compiler makes every LDS wait a full lgkmcnt(0), so each
+  // operand read would also wait for the next stage's loads.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(uniform_ptr(lp.abase + off)), 0, 0xFFFFFFFFu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(uniform_ptr(lp.bbase + off)), 0, 0xFFFFFFFFu, 0x00020000);
   const uint32_t fix = half ? lp.half_fix : 0u;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_global_load_lds(ab + (lp.aoff[q] - fix), st + kStA + (wave + 8 * q) * 1024, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, st + kStA + (wave + 8 * q) * 1024, 16,
+                                             lp.aoff[q] - fix, 0, 0, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_global_load_lds(bb + (lp.boff[q] - fix), st + kStB + (wave + 8 * q) * 1024, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, st + kStB + (wave + 8 * q) * 1024, 16,
+                                             lp.boff[q] - fix, 0, 0, 0);
 }
 
 // The 32 MFMAs of K-step h (0/1) of stage `st`, with E8M0 byte SEL of the
