@@ -153,16 +153,21 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 
 // Issue the direct loads of one KV tile image into an LDS stage: wave w
 // moves the 1 KiB rows w, w + kWaves, ... of the image, lane l bytes
-// [16 l, 16 l + 16) of each.
+// [16 l, 16 l + 16) of each.  Buffer loads (a raw resource over the image,
+// no range check), not the global form: with a global load-to-LDS in
+// flight the compiler turns every LDS wait into a full lgkmcnt(0), so each
+// operand read would also wait for the reads issued after it.
 template <int D>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* src, int wave, int lane) {
   constexpr int NL = img_bytes(D) / 1024;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uniform_ptr(src)), 0, 0xFFFFFFFFu, 0x00020000);
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
   for (int i = 0; i < (NL + kWaves - 1) / kWaves; ++i) {
     const int row = wave + i * kWaves;
     if (row < NL)
-      __builtin_amdgcn_global_load_lds(uniform_ptr(src + row * 1024) + lo, stage + row * 1024, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, stage + row * 1024, 16, lo, row * 1024, 0, 0);
   }
 }
 
