@@ -136,20 +136,24 @@ size_t mxattn_dump_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv,
  *          by the dump entry points: the attention kernels quantize Q
  *          themselves, and the dump variants store that Q~ here; the
  *          short-query workspace always holds these regions)
- *   off[3] bytes per image (17408 for D = 128, 13312 for D = 64)
+ *   off[3] bytes per image (17408 for D = 128, 9216 for D = 64)
  *   off[4] = off[5] = 0
  * and *skv_ld (host) = Skv rounded up to a multiple of the 128-key tile.
- * Image of KV tile T (keys 128T .. 128T+127), all offsets in bytes:
- *   [0, 8192)           K~ codes, [subtile t < 8][lane l < 64][16]: lane l
- *                       of subtile t holds key 128T + 32*((l%16)/4) + 4t
- *                       + l%4, elements 32*(l/16) .. 32*(l/16)+31 (zero for
- *                       D = 64 and l >= 32)
- *   [8192, 8192+64D)    V~ codes, [channel tile n < D/16][lane l][16]: lane l
- *                       of tile n holds channel 16n + l%16, keys 128T +
- *                       32*(l/16) .. +31 (one 32-key block along keys)
- *   [8192+64D, +512)    K~ scales [lane l][subtile t], E8M0
- *   [8704+64D, +4D)     V~ scales [lane l][channel tile n], E8M0
- *   then zero padding to the image size.
+ * Image of KV tile T (keys 128T .. 128T+127), all offsets in bytes, in the
+ * operand order of the 32 x 32 x 64 block-scaled FP4 matrix instruction
+ * (lane l of an operand: row l%32, 32 elements of K-block l/32):
+ *   [0, 64D)        K~ codes, [subtile t < 4][d-half i < D/64][lane l < 64]
+ *                   [16]: lane l of (t, i) holds key 128T + 64*(t/2) +
+ *                   32*((R/4)%2) + 16*(t%2) + 4*(R/8) + R%4 with R = l%32,
+ *                   elements 32*(2i + l/32) .. +31 (one 32-element block
+ *                   along D)
+ *   [64D, 128D)     V~ codes, [channel tile c < D/32][key step s < 2][lane l]
+ *                   [16]: lane l of (c, s) holds channel 32c + l%32, keys
+ *                   128T + 64s + 32*(l/32) .. +31 (one 32-key block along
+ *                   keys)
+ *   [128D, 132D)    K~ scales [lane l][t*(D/64) + i], E8M0
+ *   [132D, 136D)    V~ scales [lane l][2c + s], E8M0
+ *   then zero padding to a multiple of 1 KiB.
  * Codes pack two E2M1 elements per byte, the lower-indexed one in the low
  * nibble.  Keys at or past Skv are quantized as zeros (codes 0, scale 0).
  * Returns MX_ERR_ARG for the FP16 mode.
@@ -249,7 +253,7 @@ int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
  *
  * Arguments as for mxattn_fwd, except: causal queries are aligned to the
  * end of the keys (query i sees keys j <= i + Skv - Sq; Sq <= Skv);
- * (Hq/Hkv) * Sq <= 16 and an MX mode (MXATTN_OCP .. MXATTN_UOS_EFQ), else
+ * (Hq/Hkv) * Sq <= 32 and an MX mode (MXATTN_OCP .. MXATTN_UOS_EFQ), else
  * MX_ERR_UNSUPPORTED (FP16 mode and longer query blocks: mxattn_fwd); the
  * workspace holds mxattn_decode_workspace_bytes(...) bytes (the
  * mxattn_prepare layout followed by the per-split partial states).

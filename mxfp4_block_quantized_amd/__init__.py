@@ -372,7 +372,7 @@ def attn_decode(q, k, v, *, causal=False, mode="uos_pnq", out=None, workspace=No
                 stream=None):
     """Short-query attention over key splits (fp32 output); causal queries
     are aligned to the end of the keys.  q [B,Hq,Sq,D] with (Hq/Hkv)*Sq <=
-    16, k/v [B,Hkv,Skv,D]."""
+    32, k/v [B,Hkv,Skv,D]."""
     B, Hq, Hkv, Sq, Skv, D = _attn_shapes(q, k, v)
     out = _out(out, (B, Hq, Sq, D), q.device)
     if workspace is None:

@@ -11,37 +11,41 @@
 // same P~ (computed on the matrix core against an all-ones operand);
 // otherwise it sums the unquantized p.
 //
-// Mapping onto v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4, fp32 accum):
-// an operand lane l holds row (l % 16) and the 32 K-elements of K-block
-// (l / 16) plus that block's E8M0 scale (one byte of a register, picked by
-// the instruction's op_sel); the accumulator lane l, register r holds row
-// 4*(l/16) + r, column l % 16.
-//  * S^T = K~ Q~^T: A = 16 keys x 128 d, B = 128 d x 16 queries, one MFMA
-//    covers D = 128.  The 16 A-rows of key subtile t (0..7) of a 128-key tile
-//    are the keys 32*(row/4) + 4*t + row%4, so accumulator lane l holds, over
-//    t and r, exactly the 32 keys 32*(l/16) + 4*t + r: one whole P~ block of
-//    query l % 16.  Block maxima and the fp4 packing are therefore in-lane;
-//    only the row max needs two cross-lane swaps.
-//  * O^T = V~^T P~^T: A = 16 channels x 128 keys, B = P~ (128 keys x 16
-//    queries) straight from the registers above, with one E8M0 byte per
-//    lane.  The accumulator keeps query l % 16 in every lane of a column,
+// Mapping onto v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4, fp32 accum): an
+// operand lane l holds row (l % 32) and the 32 K-elements of K-block (l / 32)
+// plus that block's E8M0 scale (one byte of a register, picked by the
+// instruction's op_sel); the accumulator lane l, register r holds row
+// 8 (r/4) + 4 (l/32) + r%4, column l % 32.
+//  * S^T = K~ Q~^T: A = 32 keys x 64 d, B = 64 d x 32 queries; D/64
+//    instructions per 32-key subtile.  The 32 A-rows of subtile t (0..3) of a
+//    128-key tile are keys chosen (in the quantizer's image order) so that
+//    accumulator lane l holds, over the subtiles 2s and 2s+1, exactly the 32
+//    keys 64 s + 32 (l/32) + 0..31 in register order: one whole P~ block of
+//    query l % 32.  Block maxima and the FP4 packing stay in-lane; the row
+//    max needs one swap between the two lane halves.
+//  * O^T = V~^T P~^T: A = 32 channels x 64 keys, B = P~ (64 keys x 32
+//    queries) straight from the registers above, with the lane's own block
+//    scale.  The accumulator keeps query l % 32 in every register of a lane,
 //    matching the softmax state.
-// Q is quantized in the kernel's prologue: each lane holds exactly one
-// 32-element block of its query row (the B operand layout), so it applies
-// the block rule of the mode to the raw bf16/fp32 elements it loads
-// (mx_block.h, the same code as the standalone quantizer).
+//  * Under PNQ the denominator is one v_mfma_scale_f32_16x16x128_f8f6f4 per
+//    64 keys with the same P~ register as B and a constant A that is 1.0
+//    where (A-row / 4) and the K-block have the same parity and 0 elsewhere:
+//    output lane l then receives the sum over the 64 keys of query l % 32.
+// Q is quantized in the kernel's prologue: each lane holds whole 32-element
+// blocks of its query row (the B operand layout), so it applies the block
+// rule of the mode to the raw bf16/fp32 elements it loads (mx_block.h, the
+// same code as the standalone quantizer).
 // The quantizer writes K~ and V~ as KV tile images already in these operand
 // orders, so a tile moves to LDS with contiguous 16-byte-per-lane direct
-// loads (global_load_lds) and every operand read is one ds_read per lane.
+// loads and every operand read is one ds_read per lane.
 //
 // P~ is formed in the scaled domain: for a block with scale exponent e,
 // v = exp2((s - m) * log2(e)/sqrt(D) - e) is rounded by
-// v_cvt_scalef32_pk_fp4_f32 (round to nearest even,
-// saturating).  This keeps blocks whose probabilities lie below fp32's
-// normal range exact in the same way the binary64 definition treats them.
-// The UOS+EFQ mode skips the exp: the code of each score is an affine
-// function of its log2 residual to the block's exponent, rounded and
-// clamped by v_cvt_pk_u8_f32 (efq_block_exp, tile_stats, p_tile).
+// v_cvt_scalef32_pk_fp4_f32 (round to nearest even, saturating).  This keeps
+// blocks whose probabilities lie below fp32's normal range exact in the same
+// way the binary64 definition treats them.  The UOS+EFQ mode skips the exp:
+// the code of each score is an affine function of its log2 residual to the
+// block's exponent, rounded and clamped by v_cvt_pk_u8_f32.
 #include "internal.h"
 #include "mx_block.h"
 
@@ -50,47 +54,63 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQT = 2;              // 16-query tiles per wave
-constexpr int kSub = kKvTile / 16;  // key subtiles per KV tile (8)
-constexpr int kStages = 3;          // LDS ring of KV tile images
-static_assert(kMxQTile == kWaves * kQT * 16, "query tile = waves x q-tiles x 16");
+constexpr int kQW = 32;              // query rows per wave (one 32-column tile)
+constexpr int kSub = kKvTile / 32;   // 32-key subtiles per KV tile (4)
+constexpr int kStages = 4;           // LDS ring of KV tile images
+static_assert(kMxQTile == kWaves * kQW, "query tile = waves x 32");
 static_assert(kMxQTile % kKvTile == 0, "query tiles start on KV tile boundaries");
+static_assert(kDecodeCols == kQW, "short-query waves use one 32-column tile");
 
-template <int SEL_A>
-__device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, uint32_t sa, int sb) {
-  v8i av = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
-            static_cast<int>(a.w), 0, 0, 0, 0};
-  v8i bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
-            static_cast<int>(b.w), 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL_A,
-                                                          static_cast<int>(sa), 0, sb);
+template <int SA, int SB>
+__device__ __forceinline__ v16f mfma32_t(const uint4& a, const uint4& b, const v16f& c, uint32_t sa, uint32_t sb) {
+  const v8i av = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
+                  static_cast<int>(a.w), 0, 0, 0, 0};
+  const v8i bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
+                  static_cast<int>(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, SA, static_cast<int>(sa), SB,
+                                                         static_cast<int>(sb));
 }
-// A-scale taken from byte `sel` (a constant after unrolling) of `sa`.
-__device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, const uint4& b, v4f c, uint32_t sa,
-                                            int sel, int sb) {
+// A-scale from byte `sel` of `sa` (a constant after unrolling), B-scale from
+// byte SB of `sb`.
+template <int SB>
+__device__ __forceinline__ v16f mfma32(const uint4& a, const uint4& b, const v16f& c, uint32_t sa, int sel,
+                                       uint32_t sb) {
   switch (sel) {
-    case 0: return mfma_fp4<0>(a, b, c, sa, sb);
-    case 1: return mfma_fp4<1>(a, b, c, sa, sb);
-    case 2: return mfma_fp4<2>(a, b, c, sa, sb);
-    default: return mfma_fp4<3>(a, b, c, sa, sb);
+    case 0: return mfma32_t<0, SB>(a, b, c, sa, sb);
+    case 1: return mfma32_t<1, SB>(a, b, c, sa, sb);
+    case 2: return mfma32_t<2, SB>(a, b, c, sa, sb);
+    default: return mfma32_t<3, SB>(a, b, c, sa, sb);
   }
 }
-
-// max / sum over the four lanes l, l^16, l^32, l^48 (same query column)
-__device__ __forceinline__ float xlane_max4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// PNQ denominator: the 16x16x128 product of the lane-parity ones operand
+// `ones` with a P~ register (B-scale: the lane's block byte).
+__device__ __forceinline__ v4f mfma_rowsum(uint32_t ones, const uint4& b, const v4f& c, uint32_t sb) {
+  const v8i av = {static_cast<int>(ones), static_cast<int>(ones), static_cast<int>(ones),
+                  static_cast<int>(ones), 0, 0, 0, 0};
+  const v8i bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
+                  static_cast<int>(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, 127, 0, static_cast<int>(sb));
 }
-__device__ __forceinline__ float xlane_sum4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// The ones operand of lane l: A-row l%16, K-block l/16; 1.0 (E2M1 code 2 in
+// every nibble) where ((l%16)/4) % 2 == (l/16) % 2.  Output row 4(l/16)+r
+// then sums the K-blocks of its own parity, i.e. the lanes l%16 + 16 p and
+// l%16 + 16 p + 32 of the P~ operand (p = (l/16) % 2): both hold query l % 32.
+__device__ __forceinline__ uint32_t rowsum_ones(int lane) {
+  return (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x22222222u : 0u;
+}
+
+// max over the lanes l and l ^ 32 (same query)
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 // Scale exponent e of a P~ block from x = log2 of its largest element,
@@ -124,15 +144,30 @@ __device__ __forceinline__ float efq_block_exp(float x) {
   return fmaxf(__builtin_floorf(x - kEfqRho) + 1.0f, -127.0f);
 }
 
-// Per-wave softmax state and accumulators for kQT query tiles.
+// Per-wave softmax state and accumulators of one 32-query tile.
 template <int D>
 struct WaveState {
-  v4f oacc[kQT][D / 16];
-  v4f lacc[kQT];
-  float m[kQT];     // running row max (raw score units), -inf before the first tile
-  float mref[kQT];  // value subtracted from S on the matrix core
-  float lsum[kQT];
+  v16f oacc[D / 32];
+  v4f lacc;       // PNQ denominator (element 0 is kept rescaled)
+  v16f cneg;      // -mref in every element: the accumulator input of S^T
+  float m;        // running row max (raw score units), -inf before the first tile
+  float mref;     // value subtracted from S on the matrix core
+  float lsum;     // non-PNQ denominator (this lane's blocks)
 };
+
+template <int D>
+__device__ __forceinline__ void init_state(WaveState<D>& w) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.oacc[c][r] = 0.0f;
+  w.lacc = v4f{0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) w.cneg[r] = 0.0f;
+  w.m = -INFINITY;
+  w.mref = 0.0f;
+  w.lsum = 0.0f;
+}
 
 // s_waitcnt on the vector-memory counter only (expcnt, lgkmcnt left at max).
 template <int N>
@@ -140,6 +175,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at max).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // A wave-uniform address kept in scalar registers, so that a direct load
 // takes the scalar-base + 32-bit lane-offset form (one VGPR per lane for
@@ -151,26 +188,29 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Issue the direct loads of one KV tile image into an LDS stage: wave w
-// moves the 1 KiB rows w, w + kWaves, ... of the image, lane l bytes
+// Direct loads of 1 KiB rows of a KV tile image into an LDS stage: rows
+// r0, r0 + step, ... below the image's row count, lane l bytes
 // [16 l, 16 l + 16) of each.  Buffer loads (a raw resource over the image,
 // no range check), not the global form: with a global load-to-LDS in
 // flight the compiler turns every LDS wait into a full lgkmcnt(0), so each
 // operand read would also wait for the reads issued after it.
-template <int D>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* src, int wave, int lane) {
+template <int D, int STEP>
+__device__ __forceinline__ void issue_rows(uint8_t* stage, const uint8_t* src, int r0, int lane) {
   constexpr int NL = img_bytes(D) / 1024;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uniform_ptr(src)), 0, 0xFFFFFFFFu, 0x00020000);
   const uint32_t lo = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
-  for (int i = 0; i < (NL + kWaves - 1) / kWaves; ++i) {
-    const int row = wave + i * kWaves;
-    if (row < NL)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, stage + row * 1024, 16, lo, row * 1024, 0, 0);
+  for (int i = 0; i < (NL + STEP - 1) / STEP; ++i) {
+    const int row = r0 + i * STEP;
+    if (row < NL) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, stage + row * 1024, 16, lo, row * 1024, 0, 0);
   }
 }
-
+// A workgroup's share: wave w moves rows w, w + kWaves, ...
+template <int D>
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* src, int wave, int lane) {
+  issue_rows<D, kWaves>(stage, src, wave, lane);
+}
 // Loads this wave issues per tile.
 template <int D>
 __device__ __forceinline__ int loads_per_tile(int wave) {
@@ -178,207 +218,221 @@ __device__ __forceinline__ int loads_per_tile(int wave) {
   return NL / kWaves + (wave < NL % kWaves ? 1 : 0);
 }
 
-// S^T of one 16-query tile on the matrix core: d = S - mref, with -mref
-// (the running max of the previous tiles, 0 before the first) as the
-// accumulator input, so the subtraction happens before the single rounding
-// of the result and elements near the maximum keep full relative precision.
-__device__ __forceinline__ void s_tile(v4f (&s)[kSub], const uint4 (&kop)[kSub], const uint2& ksc,
-                                       const uint4& qop, int qsc, float mref) {
-  const v4f cneg = {-mref, -mref, -mref, -mref};
-#pragma unroll
-  for (int t = 0; t < kSub; ++t)
-    s[t] = mfma_fp4_sel(kop[t], qop, cneg, t < 4 ? ksc.x : ksc.y, t & 3, qsc);
+// ---- operand reads from an LDS stage ---------------------------------------
+// E8M0 bytes of one lane: D/16 per image part (8 or 4), as 32-bit words.
+template <int D>
+struct Sc {
+  uint32_t w[(D / 16 + 3) / 4];
+};
+template <int D>
+__device__ __forceinline__ Sc<D> read_sc(const uint8_t* st, int off, int lane) {
+  Sc<D> s;
+  if (D == 128) {
+    const uint2 v = *reinterpret_cast<const uint2*>(st + off + lane * 8);
+    s.w[0] = v.x;
+    s.w[(D / 16 + 3) / 4 - 1] = v.y;
+  } else {
+    s.w[0] = *reinterpret_cast<const uint32_t*>(st + off + lane * 4);
+  }
+  return s;
+}
+// K~ operand of (subtile t, d-half i); V~ operand of (channel tile c, key step s)
+template <int D>
+__device__ __forceinline__ uint4 k_op(const uint8_t* st, int t, int i, int lane) {
+  return *reinterpret_cast<const uint4*>(st + kImgKc + (t * (D / 64) + i) * 1024 + lane * 16);
+}
+template <int D>
+__device__ __forceinline__ uint4 v_op(const uint8_t* st, int c, int s, int lane) {
+  return *reinterpret_cast<const uint4*>(st + img_vc(D) + (c * 2 + s) * 1024 + lane * 16);
 }
 
-// Keys past `lim` (relative to this lane's 32-key block) are excluded.
-__device__ __forceinline__ void mask_tile(v4f (&s)[kSub], int lim) {
+// One S^T subtile t: d = S - mref, with -mref (the running max of the
+// previous tiles, 0 before the first) as the accumulator input, so the
+// subtraction happens inside the matrix core's accumulation and elements
+// near the maximum keep their relative precision.
+template <int D>
+__device__ __forceinline__ v16f s_sub(int t, const uint4 (&kop)[D / 64], const Sc<D>& ksc,
+                                      const uint4 (&qop)[D / 64], uint32_t qsc, const v16f& cneg);
+
+// Contraction half I of S^T subtile t (accumulator input c).
+template <int D, int I>
+__device__ __forceinline__ v16f s_part(int t, const uint4& kop, const Sc<D>& ksc, const uint4 (&qop)[D / 64],
+                                       uint32_t qsc, const v16f& c) {
+  const int bi = t * (D / 64) + I;
+  return mfma32<I>(kop, qop[I], c, ksc.w[bi >> 2], bi & 3, qsc);
+}
+
+template <int D>
+__device__ __forceinline__ v16f s_sub(int t, const uint4 (&kop)[D / 64], const Sc<D>& ksc,
+                                      const uint4 (&qop)[D / 64], uint32_t qsc, const v16f& cneg) {
+  v16f r = s_part<D, 0>(t, kop[0], ksc, qop, qsc, cneg);
+  if constexpr (D / 64 == 2) r = s_part<D, 1>(t, kop[1], ksc, qop, qsc, r);
+  return r;
+}
+
+// Keys past `lim` (relative to the first key of this lane's blocks,
+// 32 (l/32) into the tile) are excluded: register r of subtile t is key
+// 64 (t/2) + 16 (t%2) + r past that.
+__device__ __forceinline__ void mask_tile(v16f (&s)[kSub], int lim) {
   asm volatile("" : "+v"(lim));  // keeps the compares inside the caller's branch
 #pragma unroll
   for (int t = 0; t < kSub; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[t][r] = (t * 4 + r > lim) ? -INFINITY : s[t][r];
+    for (int r = 0; r < 16; ++r) s[t][r] = (64 * (t >> 1) + 16 * (t & 1) + r > lim) ? -INFINITY : s[t][r];
 }
 
-// Largest of the 32 scores this lane holds (its P~ block of one query):
-// a tree of v_max3 (depth 4) rather than one dependent chain.
-__device__ __forceinline__ float block_max32(const v4f (&s)[kSub]) {
-  // (the empty asm statements keep the compiler from re-associating the
-  // tree into a chain)
-  float a[kSub];
-#pragma unroll
-  for (int t = 0; t < kSub; ++t) a[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
-  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
-               "+v"(a[7]));
-  // 16 values: a[0..7] and s[t][3]
-  float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  float b2 = fmaxf(fmaxf(a[6], a[7]), s[0][3]);
-  float b3 = fmaxf(fmaxf(s[1][3], s[2][3]), s[3][3]);
-  float b4 = fmaxf(fmaxf(s[4][3], s[5][3]), s[6][3]);
-  asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3), "+v"(b4));
-  float c0 = fmaxf(fmaxf(b0, b1), b2);
-  float c1 = fmaxf(fmaxf(b3, b4), s[7][3]);
-  asm volatile("" : "+v"(c0), "+v"(c1));
-  return fmaxf(c0, c1);
-}
-
-// Online-softmax step of one query tile: row max, history factor alpha,
-// this lane's P~ block scale (X, e) and the offset kofs of the scaled
-// domain.  The history itself is rescaled by rescale_o.
+// Online-softmax statistics of one tile: history factor alpha, the change
+// delta of the reference max, and per P~ block s of this lane (keys
+// 64 s + 32 (l/32) ..) its E8M0 byte X and the offset kofs of the scaled
+// domain.
 struct TileStats {
-  float alpha, kofs;
-  int X;
+  float alpha, delta;
+  float kofs[2];
+  uint32_t X[2];
 };
-// PNQ: 0 = denominator from the unquantized p (OCP, UOS); 1 = PNQ; 2 = PNQ
-// with the exp-free EFQ codes.
-template <int D, int UOS, int PNQ>
-__device__ __forceinline__ TileStats tile_stats_nr(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
-  // row max: in-lane over this lane's 32-key block, then across the four
-  // lanes holding this query
-  const float bmax = block_max32(s);
+
+// First level of the block maxima: 10 v_max3 over 30 of a block's 32 values.
+__device__ __forceinline__ void bmax_l1(const v16f& a, const v16f& b, float (&o)[12]) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) o[k] = fmaxf(fmaxf(a[3 * k], a[3 * k + 1]), a[3 * k + 2]);
+  o[5] = fmaxf(fmaxf(a[15], b[0]), b[1]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[6 + k] = fmaxf(fmaxf(b[2 + 3 * k], b[3 + 3 * k]), b[4 + 3 * k]);
+  o[10] = b[14];
+  o[11] = b[15];
+}
+// Rest of the tree: 12 values to one (4 + 1 v_max3 and one max).
+__device__ __forceinline__ float bmax_l2(const float (&o)[12]) {
+  const float p0 = fmaxf(fmaxf(o[0], o[1]), o[2]);
+  const float p1 = fmaxf(fmaxf(o[3], o[4]), o[5]);
+  const float p2 = fmaxf(fmaxf(o[6], o[7]), o[8]);
+  const float p3 = fmaxf(fmaxf(o[9], o[10]), o[11]);
+  return fmaxf(fmaxf(p0, p1), fmaxf(p2, p3));
+}
+
+// delta, alpha and the running max from the row max of this tile; then the
+// scales of the lane's two blocks (block maxima b0, b1).
+template <int UOS, int PNQ>
+__device__ __forceinline__ float stats_delta(float& m, float& mref, float rowmax, float sl2, float& alpha) {
   // delta = new max - mref.  Before the first tile the running max is -inf
   // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
-  const float delta = fmaxf(w.m[u] - w.mref[u], xlane_max4(bmax));
-  TileStats r;
-  r.alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);  // 0 at first
-  w.m[u] = w.mref[u] + delta;
-  w.mref[u] = w.m[u];
-  // scale of this lane's P~ block (the block holding the row maximum gets
-  // x = 0 exactly); in the scaled domain
-  // log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
+  const float delta = fmaxf(m - mref, rowmax);
+  alpha = __builtin_amdgcn_exp2f((m - mref - delta) * sl2);  // 0 at the first tile
+  m = mref + delta;
+  mref = m;
+  return delta;
+}
+template <int UOS, int PNQ>
+__device__ __forceinline__ void block_scale(float bmax, float delta, float sl2, uint32_t& X, float& kofs) {
+  // the block holding the row maximum gets x = 0 exactly; in the scaled
+  // domain log2 v = (d - delta) * log2(e)/sqrt(D) - e = d*c - (delta*c + e)
   const float x = (bmax - delta) * sl2;
   const float e = PNQ == 2 ? efq_block_exp(x) : p_block_exp<UOS>(x);
-  r.X = static_cast<int>(e) + 127;
+  X = static_cast<uint32_t>(static_cast<int>(e) + 127);
   // EFQ: 2 r + beta = d * 2c + (beta - 2 (delta c + e)); else the exp2 offset
-  r.kofs = PNQ == 2 ? kEfqBeta - 2.0f * fmaf(delta, sl2, e) : fmaf(delta, sl2, e);
+  kofs = PNQ == 2 ? kEfqBeta - 2.0f * fmaf(delta, sl2, e) : fmaf(delta, sl2, e);
+}
+
+// All statistics of a tile at once (the short-query kernel).
+template <int UOS, int PNQ>
+__device__ __forceinline__ TileStats tile_stats(float& m, float& mref, const v16f (&s)[kSub], float sl2) {
+  float o0[12], o1[12];
+  bmax_l1(s[0], s[1], o0);
+  bmax_l1(s[2], s[3], o1);
+  const float b0 = bmax_l2(o0), b1 = bmax_l2(o1);
+  const float rowmax = xhalf_max(fmaxf(b0, b1));
+  TileStats r;
+  r.delta = stats_delta<UOS, PNQ>(m, mref, rowmax, sl2, r.alpha);
+  block_scale<UOS, PNQ>(b0, r.delta, sl2, r.X[0], r.kofs[0]);
+  block_scale<UOS, PNQ>(b1, r.delta, sl2, r.X[1], r.kofs[1]);
   return r;
 }
 
-// History rescale by alpha: alpha == 1 exactly leaves the history
-// unchanged, so the multiplies are skipped when that holds for the whole
-// wave (a uniform branch).
+// History rescale by alpha and the new accumulator input -mref.  Skipped
+// for the whole wave (a uniform branch) when no row's reference moved and
+// every alpha is exactly 1.
 template <int D, int PNQ>
-__device__ __forceinline__ void rescale_o(WaveState<D>& w, int u, float alpha) {
-  constexpr int NT = D / 16;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+__device__ __forceinline__ void rescale(WaveState<D>& w, const TileStats& ts) {
+  if (__builtin_amdgcn_ballot_w64(ts.alpha != 1.0f || ts.delta != 0.0f) != 0) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) w.oacc[u][n] *= alpha;
-    // the four lanes of a lacc column hold the same sum; only element 0 is
-    // read at the end, so only it is kept rescaled (the others stay finite)
-    if (PNQ) w.lacc[u][0] *= alpha;
+    for (int c = 0; c < D / 32; ++c) w.oacc[c] *= ts.alpha;
+    // the four elements of lacc hold the same sum; only element 0 is read at
+    // the end, so only it is kept rescaled (the others stay finite)
+    if (PNQ) w.lacc[0] *= ts.alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.cneg[r] = -w.mref;
   }
 }
 
-template <int D, int UOS, int PNQ>
-__device__ __forceinline__ TileStats tile_stats(WaveState<D>& w, int u, const v4f (&s)[kSub], float sl2) {
-  const TileStats r = tile_stats_nr<D, UOS, PNQ>(w, u, s, sl2);
-  rescale_o<D, PNQ>(w, u, r.alpha);
-  return r;
-}
-
-// P~ block of this lane: v = exp2(d*c - kofs) rounded to E2M1 (nearest
-// even, saturating), packed in MFMA operand order; vsum = sum of v.
-// EFQ (PNQ == 2): code = rne(d * 2c + kofs) by v_cvt_pk_u8_f32 (round half
-// to even, saturating at 0; below 7.5 by the choice of e), even and odd
-// elements into the bytes of two words, one shift-or per 8 codes.
-template <int PNQ>
-__device__ __forceinline__ uint4 p_tile(const v4f (&s)[kSub], float sl2, float kofs, float& vsum) {
-  uint32_t pw[4];
-  vsum = 0.0f;
-  if (PNQ == 2) {
-    const float c2 = 2.0f * sl2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float t[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = fmaf(s[2 * q + (i >> 2)][i & 3], c2, kofs);
-      // all four bytes of each word are written, so the chains may start anywhere
-      uint32_t a = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 0, __float_as_uint(t[0]));
-      a = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 1, a);
-      a = __builtin_amdgcn_cvt_pk_u8_f32(t[4], 2, a);
-      a = __builtin_amdgcn_cvt_pk_u8_f32(t[6], 3, a);
-      uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 0, __float_as_uint(t[1]));
-      b = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 1, b);
-      b = __builtin_amdgcn_cvt_pk_u8_f32(t[5], 2, b);
-      b = __builtin_amdgcn_cvt_pk_u8_f32(t[7], 3, b);
-      pw[q] = a | (b << 4);
-    }
-    return make_uint4(pw[0], pw[1], pw[2], pw[3]);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {  // dword q holds key subtiles 2q and 2q+1
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] = __builtin_amdgcn_exp2f(fmaf(s[2 * q + (i >> 2)][i & 3], sl2, -kofs));
-      if (!PNQ) vsum += v[i];
-    }
-    // all four bytes are written, so the chain may start from any value
-    uint32_t x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(v[0]), v[0], v[1], 1.0f, 0);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 1);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[4], v[5], 1.0f, 2);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[6], v[7], 1.0f, 3);
-    pw[q] = x;
-  }
-  return make_uint4(pw[0], pw[1], pw[2], pw[3]);
-}
-
-// Half h of dword q of p_tile's result: keys 8q + 4h .. 8q + 4h + 3 of this
-// lane's block (subtile 2q + h), into bytes 2h and 2h+1 of x (the other
-// half's bytes kept); vsum accumulates the unquantized v (non-PNQ modes).
-// EFQ writes its code bytes into a (even keys) and b (odd keys) instead.
-template <int PNQ, int h>
-__device__ __forceinline__ void p_half(const v4f (&s)[kSub], int q, float sl2, float kofs, uint32_t& x,
-                                       uint32_t& b, float& vsum) {
-  const v4f& sv = s[2 * q + h];
+// Four P~ values of this lane: registers r0..r0+3 of a subtile's S^T,
+// v = exp2(d*c - kofs) rounded to E2M1 (nearest even, saturating) into
+// bytes 2 HQ and 2 HQ + 1 of x (the other half's bytes kept); vsum
+// accumulates the unquantized v (non-PNQ modes).  EFQ (PNQ == 2): code =
+// rne(d * 2c + kofs) by v_cvt_pk_u8_f32 (round half to even, saturating at
+// 0; below 7.5 by the choice of e), even and odd elements into the bytes of
+// x and b, merged into nibbles (x |= b << 4) with the second half.
+template <int PNQ, int HQ>
+__device__ __forceinline__ void p_quad(const v16f& sv, int r0, float sl2, float kofs, uint32_t& x, uint32_t& b,
+                                       float& vsum) {
   if (PNQ == 2) {
     const float c2 = 2.0f * sl2;
     float t[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = fmaf(sv[i], c2, kofs);
+    for (int i = 0; i < 4; ++i) t[i] = fmaf(sv[r0 + i], c2, kofs);
     // all four bytes of each word are written over the two halves
-    x = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 2 * h, h ? x : __float_as_uint(t[0]));
-    x = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 2 * h + 1, x);
-    b = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 2 * h, h ? b : __float_as_uint(t[1]));
-    b = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 2 * h + 1, b);
-    if (h) x |= b << 4;
+    x = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 2 * HQ, HQ ? x : __float_as_uint(t[0]));
+    x = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 2 * HQ + 1, x);
+    b = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 2 * HQ, HQ ? b : __float_as_uint(t[1]));
+    b = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 2 * HQ + 1, b);
+    if (HQ) x |= b << 4;
     return;
   }
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -kofs));
+    v[i] = __builtin_amdgcn_exp2f(fmaf(sv[r0 + i], sl2, -kofs));
     if (!PNQ) vsum += v[i];
   }
   // all four bytes are written over the two halves, so the first write may
   // start from any value
-  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h ? x : __float_as_uint(v[0]), v[0], v[1], 1.0f, 2 * h);
-  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 2 * h + 1);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(HQ ? x : __float_as_uint(v[0]), v[0], v[1], 1.0f, 2 * HQ);
+  x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[2], v[3], 1.0f, 2 * HQ + 1);
+}
+// Eight values (registers 8 o .. 8 o + 7 of sv): one dword of P~ codes.
+template <int PNQ>
+__device__ __forceinline__ uint32_t p_oct(const v16f& sv, int o, float sl2, float kofs, float& vsum) {
+  uint32_t x = 0, b = 0;
+  p_quad<PNQ, 0>(sv, 8 * o, sl2, kofs, x, b, vsum);
+  p_quad<PNQ, 1>(sv, 8 * o + 4, sl2, kofs, x, b, vsum);
+  return x;
 }
 
-// Denominator and O^T += V~^T P~^T for one query tile.
+// Non-PNQ denominator: l = alpha l + sum of the unquantized p of the lane's
+// two blocks of this tile (v sums in their scaled domains).
 template <int D, int PNQ>
-__device__ __forceinline__ void pv_tile(WaveState<D>& w, int u, const uint4& pop, const TileStats& ts,
-                                        float vsum, const uint4 (&vop)[D / 16], const uint32_t* vsc) {
-  constexpr int NT = D / 16;
-  if (PNQ) {
-    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
-    w.lacc[u] = mfma_fp4<0>(ones, pop, w.lacc[u], 127, ts.X);
-  } else {
-    w.lsum[u] = fmaf(w.lsum[u], ts.alpha, __builtin_amdgcn_ldexpf(vsum, ts.X - 127));
-  }
-#pragma unroll
-  for (int n = 0; n < NT; ++n) w.oacc[u][n] = mfma_fp4_sel(vop[n], pop, w.oacc[u][n], vsc[n >> 2], n & 3, ts.X);
+__device__ __forceinline__ void l_plain(WaveState<D>& w, const TileStats& ts, float v0, float v1) {
+  if (!PNQ)
+    w.lsum = fmaf(w.lsum, ts.alpha, __builtin_amdgcn_ldexpf(v0, static_cast<int>(ts.X[0]) - 127) +
+                                        __builtin_amdgcn_ldexpf(v1, static_cast<int>(ts.X[1]) - 127));
 }
 
+// One O^T matrix instruction: channel tile c, key step s (P~ block pop of
+// scale X); vsc holds the V~ E8M0 bytes of the tile.
+template <int D>
+__device__ __forceinline__ void pv_one(WaveState<D>& w, int c, int s, const uint4& vop, const Sc<D>& vsc,
+                                       const uint4& pop, uint32_t X) {
+  w.oacc[c] = mfma32<0>(vop, pop, w.oacc[c], vsc.w[(2 * c + s) >> 2], (2 * c + s) & 3, X);
+}
+
+// P~ dump (tests): this lane's block of key step s.
 template <int DUMP>
-__device__ __forceinline__ void dump_tile(const MxAttnArgs& a, int64_t bh, int qrow, bool visit, int j0,
-                                          int grp, const uint4& pop, int X) {
+__device__ __forceinline__ void dump_block(const MxAttnArgs& a, int64_t bh, int qrow, bool visit, int kb0,
+                                           const uint4& pop, uint32_t X) {
   if (DUMP && visit && qrow < a.Sq) {
     const int slot = a.row_slot[bh * a.Sq + qrow];
     if (slot >= 0) {
-      *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) + (j0 + grp * 32) / 2) = pop;
-      a.p_scales[static_cast<int64_t>(slot) * (a.skv_ld / 32) + (j0 + grp * 32) / 32] = static_cast<uint8_t>(X);
+      *reinterpret_cast<uint4*>(a.p_codes + static_cast<int64_t>(slot) * (a.skv_ld / 2) + kb0 / 2) = pop;
+      a.p_scales[static_cast<int64_t>(slot) * (a.skv_ld / 32) + kb0 / 32] = static_cast<uint8_t>(X);
     }
   }
 }
@@ -387,86 +441,33 @@ __device__ __forceinline__ void dump_tile(const MxAttnArgs& a, int64_t bh, int q
 // (< D/32), quantized from the raw row; the dump variants also store it.
 template <int D, int UOS, int DUMP>
 __device__ __forceinline__ void quant_q_block(const MxAttnArgs& a, int64_t row, int grp, uint4& qop,
-                                              int& qsc) {
+                                              uint32_t& X) {
   const int64_t e0 = row * D + grp * 32;
   const void* src = a.q_bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.q) + e0)
                              : static_cast<const void*>(static_cast<const float*>(a.q) + e0);
-  uint32_t X;
   qop = quant_block32<UOS>(src, a.q_bf16 != 0, X);
-  qsc = static_cast<int>(X);
   if (DUMP) {
     *reinterpret_cast<uint4*>(a.qc + row * (D / 2) + grp * 16) = qop;
     a.qs[row * (D / 32) + grp] = static_cast<uint8_t>(X);
   }
 }
-
-// Interleave n matrix-core instructions with the vector work around them
-// (k vector or transcendental instructions after each), so that no wave
-// issues matrix instructions back to back: a wave waiting for a busy
-// matrix core holds up the other wave's vector instructions on its SIMD.
-template <int N, int K>
-__device__ __forceinline__ void interleave_mfma_valu() {
+// The lane's Q~ operands (query row qrow, valid below sq): d-blocks
+// 2 i + l/32 for d-half i; byte i of *qsc their E8M0 bytes.  Rows past the
+// sequence are zero codes under scale 1.
+template <int D, int UOS, int DUMP>
+__device__ __forceinline__ void load_q(const MxAttnArgs& a, int64_t row0, int qrow, bool valid, int half,
+                                       uint4 (&qop)[D / 64], uint32_t& qsc) {
+  qsc = 0x7F7F7F7Fu;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x402, K, 0);  // VALU or TRANS
+  for (int i = 0; i < D / 64; ++i) {
+    qop[i] = make_uint4(0, 0, 0, 0);
+    if (valid) {
+      uint32_t X;
+      quant_q_block<D, UOS, DUMP>(a, row0 + qrow, 2 * i + half, qop[i], X);
+      qsc = (qsc & ~(0xFFu << (8 * i))) | (X << (8 * i));
+    }
   }
 }
-
-// K~ and V~ operands of one KV tile, read from its LDS stage.
-template <int D>
-struct KOps {
-  uint4 op[kSub];
-  uint2 sc;
-};
-template <int D>
-struct VOps {
-  uint4 op[D / 16];
-  uint32_t sc[(D / 16 + 3) / 4];
-};
-template <int D>
-__device__ __forceinline__ void read_k(KOps<D>& k, const uint8_t* st, int lane) {
-#pragma unroll
-  for (int t = 0; t < kSub; ++t) k.op[t] = *reinterpret_cast<const uint4*>(st + kImgKc + t * 1024 + lane * 16);
-  k.sc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
-}
-template <int D>
-__device__ __forceinline__ void read_v(VOps<D>& v, const uint8_t* st, int lane) {
-  constexpr int NT = D / 16;
-#pragma unroll
-  for (int n = 0; n < NT; ++n) v.op[n] = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
-  if (NT == 8) {
-    const uint2 v2 = *reinterpret_cast<const uint2*>(st + img_vs(D) + lane * 8);
-    v.sc[0] = v2.x;
-    v.sc[(NT + 3) / 4 - 1] = v2.y;
-  } else {
-    v.sc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
-  }
-}
-
-// The two query tiles of a wave (A = 0, B = 1) run as a software pipeline
-// with B half a KV tile behind A, so that every group of matrix
-// instructions has independent vector work beside it.  For KV tile j:
-//   step 1: P~V of B for tile j-1          | row max and scales of A, tile j
-//   step 2: S^T of B for tile j            | P~ of A, tile j
-//   step 3: P~V of A for tile j            | row max and scales of B, tile j
-//   step 4: S^T of A for tile j+1          | P~ of B, tile j
-// The history of A is rescaled between steps 1 and 2, that of B between
-// steps 3 and 4 (a uniform branch, skipped when no row's max moved).  Each
-// step's operands are read from LDS one step ahead and kept in registers
-// while they are needed: V~ of tile j (read in step 2) serves steps 3 and
-// the next step 1, K~ of tile j+1 (read in step 3) steps 4 and the next
-// step 2.  At the last tile step 3 reads a stage with no pending loads and
-// step 4's S^T is unused.
-template <int D, int UOS, int PNQ>
-struct Pipe {
-  v4f sA[kSub], sB[kSub];  // S^T of A (tile j, from step 4 before) and of B
-  TileStats tA, tB;
-  uint4 pA, pB;            // P~ of A and B
-  float vA, vB;            // sums of the unquantized p (non-PNQ modes)
-  KOps<D> kk;              // K~ operands for steps 4 and 2
-  VOps<D> vv;              // V~ operands for steps 3 and 1
-};
 
 // One fenced scheduling region: the compiler may order instructions within
 // it but moves nothing across, so the interleave of matrix and vector work
@@ -480,158 +481,170 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ __forceinline__ void pin_out(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin_out(float& v) { asm volatile("" : "+v"(v)); }
 
-// One P~V matrix instruction of query tile u: channel tile n < D/16, or
-// (n == D/16, PNQ modes) the denominator against an all-ones operand.
-template <int D, int PNQ>
-__device__ __forceinline__ void pv_one(WaveState<D>& w, int u, int n, const uint4& pop, int X,
-                                       const VOps<D>& vv) {
-  constexpr int NT = D / 16;
-  if (n < NT) {
-    w.oacc[u][n] = mfma_fp4_sel(vv.op[n], pop, w.oacc[u][n], vv.sc[n >> 2], n & 3, X);
-  } else if (PNQ) {
-    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
-    w.lacc[u] = mfma_fp4<0>(ones, pop, w.lacc[u], 127, X);
-  }
-}
-// Non-PNQ denominator: l = alpha l + sum of the unquantized p of the tile.
-template <int D, int PNQ>
-__device__ __forceinline__ void l_plain(WaveState<D>& w, int u, const TileStats& ts, float vsum) {
-  if (!PNQ) w.lsum[u] = fmaf(w.lsum[u], ts.alpha, __builtin_amdgcn_ldexpf(vsum, ts.X - 127));
-}
-// One S^T matrix instruction: key subtile t of query tile with operand qop.
-__device__ __forceinline__ void s_one(v4f (&s)[kSub], int t, const uint4 (&kop)[kSub], const uint2& ksc,
-                                      const uint4& qop, int qsc, const v4f& cneg) {
-  s[t] = mfma_fp4_sel(kop[t], qop, cneg, t < 4 ? ksc.x : ksc.y, t & 3, qsc);
-}
+// Operands carried from one KV tile to the next: the second key step of
+// the previous tile's O^T product (its V~ operands and scales, P~ and scale).
+template <int D>
+struct Carry {
+  uint4 vop[D / 32];  // V~ of (channel tile c, key step 1)
+  Sc<D> vsc;          // V~ E8M0 bytes of that tile
+  uint4 pop;          // P~ of key step 1
+  uint32_t X;         // its scale
+};
 
-// Steps 1 / 3: P~V of the other tile (NPV matrix instructions) beside the
-// row max and block scales of tile u (a dependent chain of vector work).
-template <int D, int UOS, int PNQ, int MASK>
-__device__ __forceinline__ TileStats stats_step(WaveState<D>& w, int u, v4f (&s)[kSub], int lim, int uo,
-                                               const uint4& pop, const TileStats& to, float vo,
-                                               const VOps<D>& vv, float sl2) {
-  constexpr int NT = D / 16;
-  if (MASK) mask_tile(s, lim);
-  fence();
-  pv_one<D, PNQ>(w, uo, 0, pop, to.X, vv);
-  float a[kSub];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) a[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) pin_out(a[t]);
-  fence();
-  pv_one<D, PNQ>(w, uo, 1, pop, to.X, vv);
-#pragma unroll
-  for (int t = 4; t < 8; ++t) a[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
-#pragma unroll
-  for (int t = 4; t < 8; ++t) pin_out(a[t]);
-  fence();
-  pv_one<D, PNQ>(w, uo, 2, pop, to.X, vv);
-  float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  float b2 = fmaxf(fmaxf(a[6], a[7]), s[0][3]);
-  pin_out(b0);
-  pin_out(b1);
-  pin_out(b2);
-  fence();
-  pv_one<D, PNQ>(w, uo, 3, pop, to.X, vv);
-  const float b3 = fmaxf(fmaxf(s[1][3], s[2][3]), s[3][3]);
-  const float b4 = fmaxf(fmaxf(s[4][3], s[5][3]), s[6][3]);
-  const float c0 = fmaxf(fmaxf(b0, b1), b2);
-  const float c1 = fmaxf(fmaxf(b3, b4), s[7][3]);
-  float bmax = fmaxf(c0, c1);
-  pin_out(bmax);
-  fence();
-  if (NT > 4) pv_one<D, PNQ>(w, uo, 4, pop, to.X, vv);
-  // across the four lanes holding this query
-  auto x1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
-  float r1 = fmaxf(__uint_as_float(x1[0]), __uint_as_float(x1[1]));
-  pin_out(r1);
-  fence();
-  if (NT > 5) pv_one<D, PNQ>(w, uo, 5, pop, to.X, vv);
-  auto x2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1), __float_as_uint(r1), false, false);
-  const float rowmax = fmaxf(__uint_as_float(x2[0]), __uint_as_float(x2[1]));
-  // delta = new max - mref.  Before the first tile the running max is -inf
-  // (m - mref = -inf); afterwards m == mref, so delta = max(0, rowmax d).
-  float delta = fmaxf(w.m[u] - w.mref[u], rowmax);
-  pin_out(delta);
-  fence();
-  if (NT > 6) pv_one<D, PNQ>(w, uo, 6, pop, to.X, vv);
-  TileStats r;
-  r.alpha = __builtin_amdgcn_exp2f((w.m[u] - w.mref[u] - delta) * sl2);  // 0 at first
-  w.m[u] = w.mref[u] + delta;
-  w.mref[u] = w.m[u];
-  // scale of this lane's P~ block (the block holding the row maximum gets
-  // x = 0 exactly); log2 v = d*c - (delta*c + e) in the scaled domain
-  const float x = (bmax - delta) * sl2;
-  float e = PNQ == 2 ? efq_block_exp(x) : p_block_exp<UOS>(x);
-  pin_out(e);
-  fence();
-  if (NT > 7) pv_one<D, PNQ>(w, uo, 7, pop, to.X, vv);
-  r.X = static_cast<int>(e) + 127;
-  r.kofs = PNQ == 2 ? kEfqBeta - 2.0f * fmaf(delta, sl2, e) : fmaf(delta, sl2, e);
-  l_plain<D, PNQ>(w, uo, to, vo);
-  fence();
-  pv_one<D, PNQ>(w, uo, NT, pop, to.X, vv);
-  fence();
-  return r;
-}
-
-// Steps 2 / 4: S^T of query tile us (eight matrix instructions) beside P~
-// of tile u (per score one FMA, one exp2, half an FP4 conversion).
-template <int D, int PNQ>
-__device__ __forceinline__ uint4 ptile_step(v4f (&sn)[kSub], const KOps<D>& kk, const uint4& qop, int qsc,
-                                           float mref, const v4f (&s)[kSub], float sl2, float kofs,
-                                           float& vsum) {
-  const v4f cneg = {-mref, -mref, -mref, -mref};
-  uint32_t pw[4];
-  vsum = 0.0f;
-  fence();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t b = 0;
-    s_one(sn, 2 * q, kk.op, kk.sc, qop, qsc, cneg);
-    p_half<PNQ, 0>(s, q, sl2, kofs, pw[q], b, vsum);
-    pin_out(pw[q]);
-    if (PNQ == 2) pin_out(b);
-    if (!PNQ) pin_out(vsum);
-    fence();
-    s_one(sn, 2 * q + 1, kk.op, kk.sc, qop, qsc, cneg);
-    p_half<PNQ, 1>(s, q, sl2, kofs, pw[q], b, vsum);
-    pin_out(pw[q]);
-    if (!PNQ) pin_out(vsum);
-    fence();
-  }
-  return make_uint4(pw[0], pw[1], pw[2], pw[3]);
-}
-
+// One KV tile j of the prefill kernel, as six fenced steps, each pairing a
+// few matrix instructions with a slice of the vector work:
+//   1: statistics of tile j            | O^T of tile j-1, key step 1 (first half), PNQ sum
+//   2: P~ of subtile 0                 | O^T of tile j-1, key step 1 (second half)
+//      (uniform branch: history rescale by alpha, new -mref)
+//   3: P~ of subtile 1                 | S^T of tile j+1, subtile 0
+//   4: P~ of subtile 2                 | S^T subtile 1; O^T of tile j, key step 0 (first half)
+//   5: P~ of subtile 3                 | S^T subtile 2; O^T key step 0 (second half), PNQ sum
+//   6: non-PNQ sum, dump; V~ operands of key step 1 | S^T subtile 3
+// S^T of tile j+1 overwrites the registers of tile j subtile by subtile, after
+// P~ has read them.  Operands are read from LDS one step ahead of their use.
 template <int D, int UOS, int PNQ, int DUMP, int MASK>
-__device__ __forceinline__ void kv_step(WaveState<D>& w, Pipe<D, UOS, PNQ>& p, const uint8_t* st_cur,
-                                        const uint8_t* st_next, const uint4 (&qop)[kQT], const int (&qsc)[kQT],
-                                        const int (&qrow)[kQT], const int (&klim)[kQT], bool visit, int j0,
-                                        int lane, float sl2, const MxAttnArgs& a, int64_t bh) {
-  const int grp = lane >> 4;
+__device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<D>& cy, const uint8_t* st_cur,
+                                        const uint8_t* st_next, const uint4 (&qop)[D / 64], uint32_t qsc,
+                                        uint32_t ones, int lim, int lane, float sl2, bool visit, int j0,
+                                        const MxAttnArgs& a, int64_t bh, int qrow) {
+  constexpr int NC = D / 32;
+  constexpr int DH = D / 64;
+  constexpr int NH = NC / 2;  // channel tiles per half of a key step
+  const int half = lane >> 5;
 
-  // ---- step 1: P~V of B (tile j-1) | stats of A (tile j).  At tile 0, P~
-  // of B is all zero codes (alpha 1, sum 0): the products add nothing.
-  p.tA = stats_step<D, UOS, PNQ, MASK>(w, 0, p.sA, klim[0] - (j0 + grp * 32), 1, p.pB, p.tB, p.vB, p.vv,
-                                       sl2);
-  rescale_o<D, PNQ>(w, 0, p.tA.alpha);
+  // ---- step 1: statistics of tile j | O^T (tile j-1, key step 1), first half
+  if (MASK) mask_tile(S, lim);
+  fence();
+  TileStats ts;
+  float o0[12], o1[12];
+  pv_one<D>(w, 0, 1, cy.vop[0], cy.vsc, cy.pop, cy.X);
+  bmax_l1(S[0], S[1], o0);
+#pragma unroll
+  for (int k = 0; k < 12; ++k) pin_out(o0[k]);
+  fence();
+  if (NH > 1) pv_one<D>(w, 1, 1, cy.vop[1], cy.vsc, cy.pop, cy.X);
+  bmax_l1(S[2], S[3], o1);
+#pragma unroll
+  for (int k = 0; k < 12; ++k) pin_out(o1[k]);
+  fence();
+  if (PNQ) w.lacc = mfma_rowsum(ones, cy.pop, w.lacc, cy.X);
+  float b0 = bmax_l2(o0), b1 = bmax_l2(o1);
+  const float rowmax = xhalf_max(fmaxf(b0, b1));
+  ts.delta = stats_delta<UOS, PNQ>(w.m, w.mref, rowmax, sl2, ts.alpha);
+  block_scale<UOS, PNQ>(b0, ts.delta, sl2, ts.X[0], ts.kofs[0]);
+  block_scale<UOS, PNQ>(b1, ts.delta, sl2, ts.X[1], ts.kofs[1]);
+  pin_out(ts.kofs[0]);
+  pin_out(ts.kofs[1]);
+  pin_out(ts.X[0]);
+  pin_out(ts.X[1]);
+  pin_out(ts.alpha);
+  fence();
 
-  // ---- step 2: S^T of B (tile j) | P~ of A (tile j); V~ of tile j
-  read_v<D>(p.vv, st_cur, lane);
-  p.pA = ptile_step<D, PNQ>(p.sB, p.kk, qop[1], qsc[1], w.mref[1], p.sA, sl2, p.tA.kofs, p.vA);
-  dump_tile<DUMP>(a, bh, qrow[0], visit, j0, grp, p.pA, p.tA.X);
+  // ---- step 2: P~ of subtile 0 | O^T (tile j-1, key step 1), second half;
+  // K~ operands of subtile 0 of tile j+1 read ahead
+  uint4 kop[DH];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) kop[i] = k_op<D>(st_next, 0, i, lane);
+  const Sc<D> ksc = read_sc<D>(st_next, img_ks(D), lane);
+  uint32_t pw[2][4];
+  float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    if (NH + o < NC) pv_one<D>(w, NH + o, 1, cy.vop[NH + o], cy.vsc, cy.pop, cy.X);
+    pw[0][o] = p_oct<PNQ>(S[0], o, sl2, ts.kofs[0], v0);
+    pin_out(pw[0][o]);
+    if (!PNQ) pin_out(v0);
+    fence();
+  }
+  rescale<D, PNQ>(w, ts);
 
-  // ---- step 3: P~V of A (tile j) | stats of B (tile j); K~ of tile j+1
-  read_k<D>(p.kk, st_next, lane);
-  p.tB = stats_step<D, UOS, PNQ, MASK>(w, 1, p.sB, klim[1] - (j0 + grp * 32), 0, p.pA, p.tA, p.vA, p.vv,
-                                       sl2);
-  rescale_o<D, PNQ>(w, 1, p.tB.alpha);
+  // ---- step 3: P~ of subtile 1 | S^T (tile j+1) subtile 0; read K~ of
+  // subtile 1 and V~ of tile j, key step 0 (first half)
+  fence();
+  uint4 kop1[DH];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) kop1[i] = k_op<D>(st_next, 1, i, lane);
+  const Sc<D> vsc = read_sc<D>(st_cur, img_vs(D), lane);
+  uint4 vop0[NC];
+#pragma unroll
+  for (int c = 0; c < NH; ++c) vop0[c] = v_op<D>(st_cur, c, 0, lane);
+  {
+    v16f sn = s_part<D, 0>(0, kop[0], ksc, qop, qsc, w.cneg);
+    pw[0][2] = p_oct<PNQ>(S[1], 0, sl2, ts.kofs[0], v0);
+    pin_out(pw[0][2]);
+    if (!PNQ) pin_out(v0);
+    fence();
+    if constexpr (DH == 2) sn = s_part<D, 1>(0, kop[1], ksc, qop, qsc, sn);
+    pw[0][3] = p_oct<PNQ>(S[1], 1, sl2, ts.kofs[0], v0);
+    pin_out(pw[0][3]);
+    if (!PNQ) pin_out(v0);
+    S[0] = sn;
+    fence();
+  }
+  const uint4 p0 = make_uint4(pw[0][0], pw[0][1], pw[0][2], pw[0][3]);
 
-  // ---- step 4: S^T of A (tile j+1) | P~ of B (tile j)
-  p.pB = ptile_step<D, PNQ>(p.sA, p.kk, qop[0], qsc[0], w.mref[0], p.sB, sl2, p.tB.kofs, p.vB);
-  dump_tile<DUMP>(a, bh, qrow[1], visit, j0, grp, p.pB, p.tB.X);
+  // ---- step 4: P~ of subtile 2 | S^T subtile 1; O^T (tile j, key step 0)
+  // first half; read K~ of subtile 2 and the rest of V~ key step 0
+  uint4 kop2[DH];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) kop2[i] = k_op<D>(st_next, 2, i, lane);
+#pragma unroll
+  for (int c = NH; c < NC; ++c) vop0[c] = v_op<D>(st_cur, c, 0, lane);
+  {
+    v16f sn = s_part<D, 0>(1, kop1[0], ksc, qop, qsc, w.cneg);
+    pw[1][0] = p_oct<PNQ>(S[2], 0, sl2, ts.kofs[1], v1);
+    pin_out(pw[1][0]);
+    if (!PNQ) pin_out(v1);
+    fence();
+    if constexpr (DH == 2) sn = s_part<D, 1>(1, kop1[1], ksc, qop, qsc, sn);
+    pv_one<D>(w, 0, 0, vop0[0], vsc, p0, ts.X[0]);
+    pw[1][1] = p_oct<PNQ>(S[2], 1, sl2, ts.kofs[1], v1);
+    pin_out(pw[1][1]);
+    if (!PNQ) pin_out(v1);
+    S[1] = sn;
+    fence();
+  }
+  if (NH > 1) pv_one<D>(w, 1, 0, vop0[1], vsc, p0, ts.X[0]);
+  fence();
+
+  // ---- step 5: P~ of subtile 3 | S^T subtile 2; O^T key step 0 second
+  // half; PNQ sum of key step 0; read K~ of subtile 3
+  uint4 kop3[DH];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) kop3[i] = k_op<D>(st_next, 3, i, lane);
+  {
+    v16f sn = s_part<D, 0>(2, kop2[0], ksc, qop, qsc, w.cneg);
+    pw[1][2] = p_oct<PNQ>(S[3], 0, sl2, ts.kofs[1], v1);
+    pin_out(pw[1][2]);
+    if (!PNQ) pin_out(v1);
+    fence();
+    if constexpr (DH == 2) sn = s_part<D, 1>(2, kop2[1], ksc, qop, qsc, sn);
+    pv_one<D>(w, NH, 0, vop0[NH], vsc, p0, ts.X[0]);
+    pw[1][3] = p_oct<PNQ>(S[3], 1, sl2, ts.kofs[1], v1);
+    pin_out(pw[1][3]);
+    if (!PNQ) pin_out(v1);
+    S[2] = sn;
+    fence();
+  }
+  if (NH > 1) pv_one<D>(w, NH + 1, 0, vop0[NH + 1], vsc, p0, ts.X[0]);
+  if (PNQ) w.lacc = mfma_rowsum(ones, p0, w.lacc, ts.X[0]);
+  const uint4 p1 = make_uint4(pw[1][0], pw[1][1], pw[1][2], pw[1][3]);
+  fence();
+
+  // ---- step 6: S^T subtile 3 | non-PNQ sum, dump; V~ operands of key step
+  // 1 of tile j for the next tile's steps 1 and 2
+  {
+    S[3] = s_sub<D>(3, kop3, ksc, qop, qsc, w.cneg);
+  }
+  l_plain<D, PNQ>(w, ts, v0, v1);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) cy.vop[c] = v_op<D>(st_cur, c, 1, lane);
+  cy.vsc = vsc;
+  cy.pop = p1;
+  cy.X = ts.X[1];
+  dump_block<DUMP>(a, bh, qrow, visit, j0 + 32 * half, p0, ts.X[0]);
+  dump_block<DUMP>(a, bh, qrow, visit, j0 + 64 + 32 * half, p1, ts.X[1]);
+  fence();
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
@@ -642,14 +655,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[IMG];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[IMG];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[IMG];
-  static_assert(kStages == 3, "one LDS object per stage");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[IMG];
+  static_assert(kStages == 4, "one LDS object per stage");
   // stage of ring position i (a constant after unrolling)
   auto lds_stage = [&](int i) -> uint8_t* {
     const int r = i % kStages;
-    return r == 0 ? lds0 : r == 1 ? lds1 : lds2;
+    return r == 0 ? lds0 : r == 1 ? lds1 : r == 2 ? lds2 : lds3;
   };
-  constexpr int DC = D / 32;  // 32-element blocks per Q~ row
-  constexpr int NT = D / 16;  // output channel tiles
+  constexpr int NC = D / 32;  // output channel tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -657,12 +670,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin
   // over the 8 XCDs (each with its own L2), workgroup i to XCD i % 8.  Each
   // XCD is given a contiguous run of a list of (KV group, query head of the
-  // group, query tile or causal pair), so a KV head's K~/V~ tile images are fetched from
-  // HBM by one XCD (two at a run boundary) instead of all eight.  With
-  // per-sequence lengths the KV groups gg = b * Hkv + g are listed in the
-  // order of (gg % 8, gg / 8): each XCD then holds groups of every batch
-  // entry, which keeps the XCDs equally loaded when the entries' lengths
-  // differ (with equal lengths the plain order is kept).
+  // group, query tile or causal pair), so a KV head's K~/V~ tile images are
+  // fetched from HBM by one XCD (two at a run boundary) instead of all
+  // eight.  With per-sequence lengths the KV groups gg = b * Hkv + g are
+  // listed in the order of (gg % 8, gg / 8): each XCD then holds groups of
+  // every batch entry, which keeps the XCDs equally loaded when the entries'
+  // lengths differ (with equal lengths the plain order is kept).
   // Causal: one workgroup takes the query tiles p and nqb-1-p of a head
   // (nqb+1 KV tiles in all, the longer one first), so every workgroup of a
   // head does the same work and the fixed cost per workgroup is spread over
@@ -691,8 +704,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   const int h = g * G + rem / nslot;
   const int slot = rem % nslot;
   const int njobs = (CAUSAL && 2 * slot + 1 != nqb) ? 2 : 1;
-  const int col = lane & 15;   // query column within a 16-query tile
-  const int grp = lane >> 4;   // K-block / lane group
+  const int col = lane & 31;   // query column within the wave's 32
+  const int half = lane >> 5;  // K-block / row group
+  const uint32_t ones = rowsum_ones(lane);
 
   const int64_t bh = static_cast<int64_t>(b) * a.Hq + h;
   const int64_t bg = static_cast<int64_t>(b) * a.Hkv + g;
@@ -713,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     // the query tile of this job (causal: the longer one first)
     const int qb = CAUSAL ? (job == 0 ? nqb - 1 - slot : slot) : slot;
     const int q0 = qb * kMxQTile;
-    const int qw0 = q0 + wave * (kQT * 16);  // first query row of this wave
+    const int qw0 = q0 + wave * kQW;  // first query row of this wave
     if (q0 >= sq) continue;  // whole workgroup (uniform), before any barrier of the job
     // every wave is done with the previous job's stages before they refill
     if (job > 0) {
@@ -722,30 +736,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
       asm volatile("" ::: "memory");
     }
 
-    // Q~ operands (B of S^T): query column `col`, d-block `grp`, quantized
-    // here; rows past the sequence (and d-blocks past D) are zero codes.
-    uint4 qop[kQT];
-    int qsc[kQT];
-    int qrow[kQT];
-#pragma unroll
-    for (int t = 0; t < kQT; ++t) {
-      qrow[t] = qw0 + t * 16 + col;
-      qop[t] = make_uint4(0, 0, 0, 0);
-      qsc[t] = 127;
-      if (grp < DC && qrow[t] < sq)
-        quant_q_block<D, UOS, DUMP>(a, bh * a.Sq + qrow[t], grp, qop[t], qsc[t]);
-    }
+    // Q~ operands (B of S^T): query column `col`, d-blocks 2 i + half,
+    // quantized here; rows past the sequence are zero codes.
+    int qrow = qw0 + col;
+    uint4 qop[D / 64];
+    uint32_t qsc;
+    load_q<D, UOS, DUMP>(a, bh * a.Sq, qrow, qrow < sq, half, qop, qsc);
 
     WaveState<D> w;
-#pragma unroll
-    for (int t = 0; t < kQT; ++t) {
-      w.m[t] = -INFINITY;
-      w.mref[t] = 0.0f;
-      w.lsum[t] = 0.0f;
-      w.lacc[t] = v4f{0, 0, 0, 0};
-#pragma unroll
-      for (int n = 0; n < NT; ++n) w.oacc[t][n] = v4f{0, 0, 0, 0};
-    }
+    init_state<D>(w);
 
     const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
     const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
@@ -756,51 +755,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     // only up to its own last tile (the sequence end, or the causal limit of
     // its last row); a wave whose rows all lie past the sequence dumps none.
     const int nmain = CAUSAL ? min((q0 + koff + 1) / kKvTile, skv / kKvTile) : skv / kKvTile;
-    const int last_w = qw0 >= sq ? -1 : (CAUSAL ? min((qw0 + kQT * 16 - 1 + koff) / kKvTile, ntk - 1) : ntk - 1);
-    int klim[kQT];
-#pragma unroll
-    for (int t = 0; t < kQT; ++t) {
-      klim[t] = CAUSAL ? min(skv - 1, qrow[t] + koff) : skv - 1;
-      if (qrow[t] >= sq) qrow[t] = a.Sq;  // past the sequence: never dumped or stored
-    }
+    const int last_w = qw0 >= sq ? -1 : (CAUSAL ? min((qw0 + kQW - 1 + koff) / kKvTile, ntk - 1) : ntk - 1);
+    const int klim = CAUSAL ? min(skv - 1, qrow + koff) : skv - 1;
+    if (qrow >= sq) qrow = a.Sq;  // past the sequence: never dumped or stored
 
     // wave-uniform (the divisions above run on the vector unit): scalar
     // registers, so the tile loads take the scalar-base form
     const uint8_t* img = uniform_ptr(a.img + bg * nt * static_cast<int64_t>(IMG));
     const int nl = loads_per_tile<D>(wave);
 
-    // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  Tiles 0
-    // and 1 are requested up front, and S^T of A for tile 0 is formed once
-    // tile 0 has landed.  At the top of iteration jt the wave waits for all
-    // its loads (those of tile jt+1, requested an iteration earlier); the
-    // barrier then makes every wave's loads visible and tells that every wave
-    // has finished iteration jt-1, the last to read the stage of tile jt-1
-    // (its V~, in step 2), which the loads of tile jt+2 then refill.
+    // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  Tiles
+    // 0 and 1 are requested up front, and S^T of tile 0 is formed once it has
+    // landed.  At the top of iteration jt each wave waits for all its loads
+    // (those of tile jt+1, requested an iteration earlier); the barrier then
+    // makes every wave's loads visible and tells that every wave has finished
+    // iteration jt-1.  The loads of tile jt+2 then refill the stage of tile
+    // jt-2, whose last operands (V~ of key step 1, read in iteration jt-2)
+    // were consumed in iteration jt-1.  Stage 3 stands for tile -1: the
+    // second key step of its O^T product multiplies zero P~ codes, and only
+    // its V~ scale bytes must be finite (set to 1.0 here).
     issue_tile<D>(lds0, img, wave, lane);
+    if (ntiles > 1) issue_tile<D>(lds1, img + IMG, wave, lane);
+    for (int i = threadIdx.x; i < 64 * (D / 16) / 4; i += kThreads)
+      reinterpret_cast<uint32_t*>(lds3 + img_vs(D))[i] = 0x7F7F7F7Fu;
     if (ntiles > 1) {
-      issue_tile<D>(lds1, img + IMG, wave, lane);
-      if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else wait_vmcnt<3>();
+      if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else if (nl == 3) wait_vmcnt<3>(); else wait_vmcnt<2>();
     } else {
       wait_vmcnt<0>();
     }
+    wait_lgkm0();  // the scale bytes above, written before any wave reads them
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    Pipe<D, UOS, PNQ> p;
-    // P~ of B before tile 0: zero codes under scale 1 against zero V~ operands
-    p.pB = make_uint4(0, 0, 0, 0);
-    p.tB.alpha = 1.0f;
-    p.tB.kofs = 0.0f;
-    p.tB.X = 127;
-    p.vA = 0.0f;
-    p.vB = 0.0f;
+    v16f S[kSub];
+    {
+      const Sc<D> ksc = read_sc<D>(lds0, img_ks(D), lane);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) p.vv.op[n] = make_uint4(0, 0, 0, 0);
+      for (int t = 0; t < kSub; ++t) {
+        uint4 kop[D / 64];
 #pragma unroll
-    for (int n = 0; n < (NT + 3) / 4; ++n) p.vv.sc[n] = 0x7F7F7F7Fu;
-    read_k<D>(p.kk, lds0, lane);
-    s_tile(p.sA, p.kk.op, p.kk.sc, qop[0], qsc[0], w.mref[0]);
+        for (int i = 0; i < D / 64; ++i) kop[i] = k_op<D>(lds0, t, i, lane);
+        S[t] = s_sub<D>(t, kop, ksc, qop, qsc, w.cneg);
+      }
+    }
+    Carry<D> cy;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) cy.vop[c] = v_op<D>(lds3, c, 1, lane);
+    cy.vsc = read_sc<D>(lds3, img_vs(D), lane);
+    cy.pop = make_uint4(0, 0, 0, 0);
+    cy.X = 127;
 
     // tiles [0, nmain): no key masked; the ring position of each is a
     // compile-time constant (the loop is unrolled by the stage count)
@@ -815,8 +819,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
           asm volatile("" ::: "memory");
           if (jt + 2 < ntiles)
             issue_tile<D>(lds_stage(k + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
-          kv_step<D, UOS, PNQ, DUMP, 0>(w, p, lds_stage(k), lds_stage(k + 1), qop, qsc, qrow, klim,
-                                        jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
+          kv_iter<D, UOS, PNQ, DUMP, 0>(w, S, cy, lds_stage(k), lds_stage(k + 1), qop, qsc, ones,
+                                        klim - (jt * kKvTile + 32 * half), lane, sl2, jt <= last_w,
+                                        jt * kKvTile, a, bh, qrow);
         }
       }
     }
@@ -831,13 +836,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
         issue_tile<D>(lds_stage(jt + 2), img + static_cast<int64_t>(jt + 2) * IMG, wave, lane);
       // every load of the ring has landed here except tile jt+2's, which
       // targets neither stage read below
-      kv_step<D, UOS, PNQ, DUMP, 1>(w, p, lds_stage(jt), lds_stage(jt + 1), qop, qsc, qrow, klim,
-                                    jt <= last_w, jt * kKvTile, lane, sl2, a, bh);
+      kv_iter<D, UOS, PNQ, DUMP, 1>(w, S, cy, lds_stage(jt), lds_stage(jt + 1), qop, qsc, ones,
+                                    klim - (jt * kKvTile + 32 * half), lane, sl2, jt <= last_w,
+                                    jt * kKvTile, a, bh, qrow);
     }
-    // P~V of B for the last tile (its V~ still in registers)
+    // O^T of the last tile, key step 1 (its operands carried in registers)
 #pragma unroll
-    for (int n = 0; n <= NT; ++n) pv_one<D, PNQ>(w, 1, n, p.pB, p.tB.X, p.vv);
-    l_plain<D, PNQ>(w, 1, p.tB, p.vB);
+    for (int c = 0; c < NC; ++c) pv_one<D>(w, c, 1, cy.vop[c], cy.vsc, cy.pop, cy.X);
+    if (PNQ) w.lacc = mfma_rowsum(ones, cy.pop, w.lacc, cy.X);
 
     // The epilogue stores under a per-lane condition.  Pin the accumulators
     // here so that the matrix-core instructions producing them are not moved
@@ -845,26 +851,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     // would drop the operands of the disabled lanes, which other lanes' results
     // depend on.
 #pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[u][n]));
-      asm volatile("" : "+v"(w.lacc[u]));
-    }
+    for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(w.oacc[c]));
+    asm volatile("" : "+v"(w.lacc));
 
-    // ---- epilogue: O = O_acc / l ----
+    // ---- epilogue: O = O_acc / l; lane l holds channels 32 c + 8 g +
+    // 4 (l/32) + 0..3 of its query row ----
+    const float l = PNQ ? w.lacc[0] : xhalf_sum(w.lsum);
+    const float inv = 1.0f / l;
+    if (qrow < a.Sq) {
+      float* orow = a.o + (bh * a.Sq + qrow) * D;
 #pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-      const float l = PNQ ? w.lacc[u][0] : xlane_sum4(w.lsum[u]);
-      const float inv = 1.0f / l;
-      if (qrow[u] < a.Sq) {
-        float* orow = a.o + (bh * a.Sq + qrow[u]) * D;
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          float4 v = make_float4(w.oacc[u][n][0] * inv, w.oacc[u][n][1] * inv, w.oacc[u][n][2] * inv,
-                                 w.oacc[u][n][3] * inv);
-          *reinterpret_cast<float4*>(orow + n * 16 + grp * 4) = v;
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 v = make_float4(w.oacc[c][4 * gq] * inv, w.oacc[c][4 * gq + 1] * inv,
+                                       w.oacc[c][4 * gq + 2] * inv, w.oacc[c][4 * gq + 3] * inv);
+          *reinterpret_cast<float4*>(orow + 32 * c + 8 * gq + 4 * half) = v;
         }
-      }
     }
   }  // job
 }
@@ -899,41 +902,18 @@ hipError_t pick_mode(const MxAttnArgs& a, hipStream_t s) {
 
 // ---- short-query attention over key splits ----------------------------
 //
-// One wave per (b, KV head g, split): its 16 query columns are the G x Sq
-// queries of the GQA group (column c = h_local * Sq + i, G * Sq <= 16),
+// One wave per (b, KV head g, split): its 32 query columns are the G x Sq
+// queries of the GQA group (column c = h_local * Sq + i, G * Sq <= 32),
 // so the group's K~/V~ are read once per split.  The wave runs the same
 // tile step as above (S^T on the matrix core with -m as accumulator input,
 // block scales, P~, O^T += V~^T P~^T) over the split's KV tiles, with its
-// own running max from -inf, reading the tile images straight from global
-// memory into the operand registers (nothing is shared between waves), the
-// next tile's loads in flight during the current tile.  It leaves (m, l,
-// unnormalized O) per query column; the merge kernel combines the splits
-// in ascending order.  Columns with no visible key in the split leave
-// m = -inf, l = 0, O = 0.
-template <int D>
-struct TileOps {
-  uint4 kop[kSub];
-  uint2 ksc;
-  uint4 vop[D / 16];
-  uint32_t vsc[(D / 16 + 3) / 4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile_ops(TileOps<D>& t, const uint8_t* st, int lane) {
-  constexpr int NT = D / 16;
-#pragma unroll
-  for (int i = 0; i < kSub; ++i) t.kop[i] = *reinterpret_cast<const uint4*>(st + kImgKc + i * 1024 + lane * 16);
-  t.ksc = *reinterpret_cast<const uint2*>(st + img_ks(D) + lane * 8);
-#pragma unroll
-  for (int n = 0; n < NT; ++n) t.vop[n] = *reinterpret_cast<const uint4*>(st + kImgVc + n * 1024 + lane * 16);
-  if (NT == 8) {
-    const uint2 v2 = *reinterpret_cast<const uint2*>(st + img_vs(D) + lane * 8);
-    t.vsc[0] = v2.x;
-    t.vsc[(NT + 3) / 4 - 1] = v2.y;
-  } else {
-    t.vsc[0] = *reinterpret_cast<const uint32_t*>(st + img_vs(D) + lane * 4);
-  }
-}
+// own running max from -inf.  Each wave streams its tiles through an LDS
+// stage of its own (nothing is shared between waves): it reads a tile's
+// operands into registers and then requests the next tile into the stage,
+// whose loads are in flight during the rest of the tile's work.  It leaves
+// (m, l, unnormalized O) per query column; the merge kernel combines the
+// splits in ascending order.  Columns with no visible key in the split
+// leave m = -inf, l = 0, O = 0.
 
 // Splits of entry b: its keys in spans of split_tiles tiles (0 for an entry
 // with no key).
@@ -984,10 +964,12 @@ template <int D, int UOS, int PNQ, int DUMP, int COMPACT>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d, float sl2) {
   const MxAttnArgs& a = d.at;
   constexpr int IMG = img_bytes(D);
-  constexpr int NT = D / 16;
-  constexpr int DC = D / 32;
+  constexpr int NC = D / 32;
+  constexpr int DH = D / 64;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kWaves * IMG];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* st = lds + wave * IMG;  // this wave's stage
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   int b, g, sp;
   // (a compile-time choice: the scan left in the other form's code costs it
@@ -1007,21 +989,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   const int64_t bg = static_cast<int64_t>(b) * a.Hkv + g;
   const int64_t slot = bg * d.nsplit + sp;  // partial-state slot
   const int G = a.Hq / a.Hkv;
-  const int col = lane & 15, grp = lane >> 4;
+  const int col = lane & 31, half = lane >> 5;
+  const uint32_t ones = rowsum_ones(lane);
 
   // query of this column; unused columns multiply zero codes and see every key
   const bool cvalid = col < G * a.Sq;
   const int hl = cvalid ? col / a.Sq : 0, qi = cvalid ? col % a.Sq : 0;
   const int64_t bh = static_cast<int64_t>(b) * a.Hq + g * G + hl;
-  uint4 qop = make_uint4(0, 0, 0, 0);
-  int qsc = 127;
-  if (cvalid && grp < DC) {
-    // every split of a group quantizes the same rows; split 0 dumps them
-    if (DUMP && sp == 0)
-      quant_q_block<D, UOS, 1>(a, bh * a.Sq + qi, grp, qop, qsc);
-    else
-      quant_q_block<D, UOS, 0>(a, bh * a.Sq + qi, grp, qop, qsc);
-  }
+  uint4 qop[DH];
+  uint32_t qsc;
+  // every split of a group quantizes the same rows; split 0 dumps them
+  if (DUMP && sp == 0)
+    load_q<D, UOS, 1>(a, bh * a.Sq, qi, cvalid, half, qop, qsc);
+  else
+    load_q<D, UOS, 0>(a, bh * a.Sq, qi, cvalid, half, qop, qsc);
   // this sequence's keys: the padded extent, or its own length
   const int skv = a.lens_k ? min(max(__builtin_amdgcn_readfirstlane(a.lens_k[b]), 0), a.Skv) : a.Skv;
   // causal: end-aligned; a row with no visible key (klim < 0) stays empty
@@ -1037,48 +1018,77 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   const int first_masked = a.causal ? max(skv - a.Sq, 0) / kKvTile : skv / kKvTile;
 
   WaveState<D> w;
-  w.m[0] = -INFINITY;
-  w.mref[0] = 0.0f;
-  w.lsum[0] = 0.0f;
-  w.lacc[0] = v4f{0, 0, 0, 0};
-#pragma unroll
-  for (int n = 0; n < NT; ++n) w.oacc[0][n] = v4f{0, 0, 0, 0};
+  init_state<D>(w);
 
-  const uint8_t* img = a.img + bg * nt * static_cast<int64_t>(IMG);
-  TileOps<D> cur, nxt;
-  if (t_begin < t_end) load_tile_ops<D>(cur, img + static_cast<int64_t>(t_begin) * IMG, lane);
+  const uint8_t* img = uniform_ptr(a.img + bg * nt * static_cast<int64_t>(IMG));
+  if (t_begin < t_end) issue_rows<D, 1>(st, img + static_cast<int64_t>(t_begin) * IMG, 0, lane);
   for (int t = t_begin; t < t_end; ++t) {
-    if (t + 1 < t_end) load_tile_ops<D>(nxt, img + static_cast<int64_t>(t + 1) * IMG, lane);
+    wait_vmcnt<0>();  // this wave's loads of tile t have landed in its stage
+    asm volatile("" ::: "memory");
     const int j0 = t * kKvTile;
-    v4f s[kSub];
-    s_tile(s, cur.kop, cur.ksc, qop, qsc, w.mref[0]);
-    if (t >= first_masked) mask_tile(s, klim - (j0 + grp * 32));
-    const TileStats ts = tile_stats<D, UOS, PNQ>(w, 0, s, sl2);
-    float vsum;
-    const uint4 pop = p_tile<PNQ>(s, sl2, ts.kofs, vsum);
-    dump_tile<DUMP>(a, bh, qrow, j0 <= klim, j0, grp, pop, ts.X);
-    pv_tile<D, PNQ>(w, 0, pop, ts, vsum, cur.vop, cur.vsc);
-    if (t + 1 < t_end) cur = nxt;
+    v16f S[kSub];
+    {
+      const Sc<D> ksc = read_sc<D>(st, img_ks(D), lane);
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        uint4 kop[DH];
+#pragma unroll
+        for (int i = 0; i < DH; ++i) kop[i] = k_op<D>(st, u, i, lane);
+        S[u] = s_sub<D>(u, kop, ksc, qop, qsc, w.cneg);
+      }
+    }
+    uint4 vop[NC][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) vop[c][s] = v_op<D>(st, c, s, lane);
+    const Sc<D> vsc = read_sc<D>(st, img_vs(D), lane);
+    // every operand of tile t is in registers before the stage refills
+    asm volatile("" ::: "memory");
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+    if (t + 1 < t_end) issue_rows<D, 1>(st, img + static_cast<int64_t>(t + 1) * IMG, 0, lane);
+    if (t >= first_masked) mask_tile(S, klim - (j0 + 32 * half));
+    const TileStats ts = tile_stats<UOS, PNQ>(w.m, w.mref, S, sl2);
+    rescale<D, PNQ>(w, ts);
+    float v0 = 0.0f, v1 = 0.0f;
+    const uint4 p0 = make_uint4(p_oct<PNQ>(S[0], 0, sl2, ts.kofs[0], v0), p_oct<PNQ>(S[0], 1, sl2, ts.kofs[0], v0),
+                                p_oct<PNQ>(S[1], 0, sl2, ts.kofs[0], v0), p_oct<PNQ>(S[1], 1, sl2, ts.kofs[0], v0));
+    const uint4 p1 = make_uint4(p_oct<PNQ>(S[2], 0, sl2, ts.kofs[1], v1), p_oct<PNQ>(S[2], 1, sl2, ts.kofs[1], v1),
+                                p_oct<PNQ>(S[3], 0, sl2, ts.kofs[1], v1), p_oct<PNQ>(S[3], 1, sl2, ts.kofs[1], v1));
+    const bool visit = j0 <= klim;
+    dump_block<DUMP>(a, bh, qrow, visit, j0 + 32 * half, p0, ts.X[0]);
+    dump_block<DUMP>(a, bh, qrow, visit, j0 + 64 + 32 * half, p1, ts.X[1]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      pv_one<D>(w, c, 0, vop[c][0], vsc, p0, ts.X[0]);
+      pv_one<D>(w, c, 1, vop[c][1], vsc, p1, ts.X[1]);
+    }
+    if (PNQ) {
+      w.lacc = mfma_rowsum(ones, p0, w.lacc, ts.X[0]);
+      w.lacc = mfma_rowsum(ones, p1, w.lacc, ts.X[1]);
+    }
+    l_plain<D, PNQ>(w, ts, v0, v1);
   }
 
   // pin the accumulators ahead of the per-lane stores (see attn_mx_kernel)
 #pragma unroll
-  for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(w.oacc[0][n]));
-  asm volatile("" : "+v"(w.lacc[0]));
-  const float l = PNQ ? w.lacc[0][0] : xlane_sum4(w.lsum[0]);
+  for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(w.oacc[c]));
+  asm volatile("" : "+v"(w.lacc));
+  const float l = PNQ ? w.lacc[0] : xhalf_sum(w.lsum);
   const bool empty = klim < t_begin * kKvTile;  // no visible key in this split
   if (cvalid) {  // unused columns are never merged
-    float* pr = d.part + (slot * 16 + col) * (D + 2);
-    if (grp == 0) {
-      pr[0] = empty ? -INFINITY : w.m[0];
+    float* pr = d.part + (slot * kDecodeCols + col) * (D + 2);
+    if (half == 0) {
+      pr[0] = empty ? -INFINITY : w.m;
       pr[1] = empty ? 0.0f : l;
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const v4f v = empty ? v4f{0, 0, 0, 0} : w.oacc[0][n];
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[2 + 16 * n + 4 * grp + r] = v[r];
-    }
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[2 + 32 * c + 8 * gq + 4 * half + r] = empty ? 0.0f : w.oacc[c][4 * gq + r];
   }
 }
 
@@ -1115,8 +1125,8 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, 
   const int G = a.Hq / a.Hkv;
   const int64_t bg = static_cast<int64_t>(b) * a.Hkv + h / G;
   const int col = (h % G) * a.Sq + i;
-  const float* base = d.part + (bg * d.nsplit * 16 + col) * (D + 2);
-  const int64_t stride = 16 * static_cast<int64_t>(D + 2);
+  const float* base = d.part + (bg * d.nsplit * kDecodeCols + col) * (D + 2);
+  const int64_t stride = kDecodeCols * static_cast<int64_t>(D + 2);
   // per-sequence lengths: only the splits that hold the entry's keys were written
   const int ns = a.lens_k ? __builtin_amdgcn_readfirstlane(entry_splits(d, b)) : d.nsplit;
   constexpr int PER = D / 64;

@@ -226,7 +226,7 @@ int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D
   if (Hq % Hkv != 0) return MX_ERR_ARG;
   if (mode == MXATTN_FP16) return MX_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return MX_ERR_UNSUPPORTED;
-  if ((Hq / Hkv) * static_cast<int64_t>(Sq) > 16) return MX_ERR_UNSUPPORTED;
+  if ((Hq / Hkv) * static_cast<int64_t>(Sq) > mxk::kDecodeCols) return MX_ERR_UNSUPPORTED;
   if (causal && Sq > Skv) return MX_ERR_UNSUPPORTED;
   if (B > 65535 || Hq > 65535) return MX_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * Hkv * Skv * D > (int64_t(1) << 40)) return MX_ERR_UNSUPPORTED;
@@ -257,7 +257,7 @@ DecodeLayout make_decode_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, 
   // the Q~ regions of a decode shape are a few hundred bytes per query row:
   // always reserved, the partial states follow them
   dl.part = round_up(dl.L.total_dump, 256);
-  dl.total = dl.part + static_cast<size_t>(B) * Hkv * dl.nsplit * 16 * (D + 2) * sizeof(float);
+  dl.total = dl.part + static_cast<size_t>(B) * Hkv * dl.nsplit * mxk::kDecodeCols * (D + 2) * sizeof(float);
   return dl;
 }
 

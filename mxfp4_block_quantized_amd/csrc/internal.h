@@ -22,14 +22,20 @@ constexpr int kMxQTile = 128;
 // Keys per KV tile of the 16-bit (FP16-mode) attention kernel.
 constexpr int kF16KvTile = 64;
 
-// KV tile image: the quantized K~ and V~ of one 128-key tile, stored in
-// matrix-core operand order so that the attention kernel moves it to LDS
-// with contiguous 16-byte-per-lane loads (layout in include/mxattn.h).
-constexpr int kImgKc = 0;     // K~ codes: 8 subtiles x 64 lanes x 16 B
-constexpr int kImgVc = 8192;  // V~ codes: D/16 channel tiles x 64 lanes x 16 B
-__host__ __device__ constexpr int img_ks(int D) { return kImgVc + 64 * D; }  // [lane][8]
-__host__ __device__ constexpr int img_vs(int D) { return img_ks(D) + 512; }  // [lane][D/16]
-__host__ __device__ constexpr int img_bytes(int D) { return (img_vs(D) + 4 * D + 1023) / 1024 * 1024; }
+// KV tile image: the quantized K~ and V~ of one 128-key tile, stored in the
+// operand order of v_mfma_scale_f32_32x32x64_f8f6f4 so that the attention
+// kernels move it to LDS with contiguous 16-byte-per-lane loads (layout in
+// include/mxattn.h):
+//   K~ codes  [subtile 4][d-half D/64][lane 64][16 B]   at kImgKc
+//   V~ codes  [channel tile D/32][key step 2][lane][16 B] at img_vc(D)
+//   K~ scales [lane][subtile * D/64 + d-half]          at img_ks(D)
+//   V~ scales [lane][channel tile * 2 + key step]      at img_vs(D)
+// then zero padding to a whole number of KiB.
+constexpr int kImgKc = 0;
+__host__ __device__ constexpr int img_vc(int D) { return 64 * D; }
+__host__ __device__ constexpr int img_ks(int D) { return 128 * D; }
+__host__ __device__ constexpr int img_vs(int D) { return 132 * D; }
+__host__ __device__ constexpr int img_bytes(int D) { return (136 * D + 1023) / 1024 * 1024; }
 
 // 16-bit tile image of the FP16 mode (64 keys): K as [subtile 4][step D/32]
 // [lane 64][8 x 16-bit], then V^T (fp16) as [channel tile D/16][key group 2]
@@ -90,11 +96,11 @@ hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
 // Short-query attention over key splits: one wave per (b, KV head, split)
 // computes the partial softmax state of the (Hq/Hkv) x Sq queries of a GQA
-// group (at most 16) over its keys; a second kernel merges the splits in
+// group (at most kDecodeCols) over its keys; a second kernel merges the splits in
 // order into o.  Causal queries are aligned to the end of the keys.
 struct MxDecodeArgs {
   MxAttnArgs at;      // Q~, KV images, o, dump, shapes, mode (at.causal: end-aligned)
-  float* part;        // [B*Hkv*nsplit][16][D + 2]: m, l, unnormalized O per query slot
+  float* part;        // [B*Hkv*nsplit][kDecodeCols][D + 2]: m, l, unnormalized O per query slot
   int split_tiles;    // KV tiles (128 keys) per split
   int nsplit;
   // per-sequence lengths only (at.lens_k set, B <= kCompactMaxB): waves take
@@ -102,6 +108,8 @@ struct MxDecodeArgs {
   // (b, KV head, split) of the padded extent
   int compact;
 };
+// Query columns of one short-query wave (one 32 x 32 matrix-core tile).
+constexpr int kDecodeCols = 32;
 // Largest batch for which the short-query kernel numbers its busy splits
 // (each wave scans the B lengths).
 constexpr int kCompactMaxB = 256;

@@ -135,17 +135,29 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
 }
 
 // KV tile images (layout in include/mxattn.h).  Rows at or past `rows` are
-// quantized as zeros (codes 0, E8M0 byte 0), as are the unused upper
-// contraction lanes of K~ for D = 64.
+// quantized as zeros (codes 0, E8M0 byte 0).
 //
+// Key order inside a tile: accumulator lane l, register r of the S^T product
+// of key subtile t (32 keys) holds row 8(r/4) + 4(l/32) + r%4 of that
+// subtile; the subtile's rows are the keys
+//   64 (t/2) + 32 (row/4 % 2) + 16 (t%2) + 4 (row/8) + row%4,
+// so that register r of lane l, over the subtiles 2s and 2s+1, runs through
+// the 32 keys 64 s + 32 (l/32) + 16 (t%2) + r: one whole P~ block of the
+// lane's query, in key order.  Inverting it, key kk of a tile sits in
+// subtile 2 (kk/64) + (kk%32)/16 at row 8 ((kk%16)/4) + 4 ((kk%64)/32) + kk%4.
+__device__ __forceinline__ int kimg_subtile(int kk) { return 2 * (kk >> 6) + ((kk & 31) >> 4); }
+__device__ __forceinline__ int kimg_row(int kk) { return 8 * ((kk & 15) >> 2) + 4 * ((kk & 63) >> 5) + (kk & 3); }
+
 // K~: octet-per-lane as in quant_rows_kernel; block (row kr, d-block c)
-// lands in subtile t = (kr % 128 / 4) % 8, lane 16c + 4((kr % 128) / 32) +
-// kr % 4 of its tile, the operand order of the S^T product.
+// lands in subtile kimg_subtile, d-half c/2, lane kimg_row + 32 (c%2) of its
+// tile, the A-operand order of the S^T product (lane l: row l%32, d-block
+// 2 (d-half) + l/32).
 template <typename In, int UOS, int D>
 __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
     const In* __restrict__ x, int rows, int ntiles, int blocks_per_batch,
     uint8_t* __restrict__ img, const int32_t* __restrict__ lens, int per_len) {
   constexpr int OPR = D / 8;  // octets per row
+  constexpr int DH = D / 64;  // d-halves (one 64-wide contraction each)
   constexpr int IMG = img_bytes(D);
   const int bgi = blockIdx.x / blocks_per_batch;
   // octet index within this (b, KV head): up to ntiles * 128 * D/8, past
@@ -170,15 +182,12 @@ __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
   const uint32_t r = pack8(f, inv_scale_of(X));
   const int c = w >> 2, part = w & 3;
   const int kk = kr % kKvTile;
-  const int t = (kk >> 2) & 7;
-  const int l = 16 * c + 4 * (kk >> 5) + (kk & 3);
+  const int t = kimg_subtile(kk);
+  const int l = kimg_row(kk) + 32 * (c & 1);
+  const int op = t * DH + (c >> 1);  // operand index of (subtile, d-half)
   uint8_t* base = img + (static_cast<int64_t>(bgi) * ntiles + kr / kKvTile) * IMG;
-  *reinterpret_cast<uint32_t*>(base + kImgKc + t * 1024 + l * 16 + part * 4) = r;
-  if (part == 0) base[img_ks(D) + l * 8 + t] = static_cast<uint8_t>(X);
-  if (D == 64) {  // upper half of the contraction: zero operands
-    *reinterpret_cast<uint32_t*>(base + kImgKc + t * 1024 + (l + 32) * 16 + part * 4) = 0u;
-    if (part == 0) base[img_ks(D) + (l + 32) * 8 + t] = 0;
-  }
+  *reinterpret_cast<uint32_t*>(base + kImgKc + op * 1024 + l * 16 + part * 4) = r;
+  if (part == 0) base[img_ks(D) + l * (D / 16) + op] = static_cast<uint8_t>(X);
   // zero the padding at the end of the image
   constexpr int kPadOff = img_vs(D) + 4 * D;
   const int pi = kk * OPR + w;
@@ -188,8 +197,9 @@ __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
 // V~: blocks of 32 consecutive rows per channel.  A thread owns one 32-row
 // block of 16 bytes' worth of channels (8 bf16 or 4 fp32): 32 row loads of
 // 16 bytes, each wave instruction covering whole rows.  Block (channel d,
-// row block kb) lands in channel tile d / 16, lane 16 (kb % 4) + d % 16 of
-// tile kb / 4, the operand order of the O^T product.
+// row block kb; b = kb % 4 within its tile) lands in channel tile d / 32,
+// key step b / 2, lane d % 32 + 32 (b % 2): the A-operand order of the O^T
+// product (lane l: channel l%32, keys 64 (step) + 32 (l/32) .. +31).
 template <typename In>
 __device__ __forceinline__ uint32_t lane_bits(const uint4& r, int ch);
 template <>
@@ -208,7 +218,6 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
     uint8_t* __restrict__ img, const int32_t* __restrict__ lens, int per_len) {
   constexpr int CPT = 16 / static_cast<int>(sizeof(In));  // channels per thread
   constexpr int NCG = D / CPT;
-  constexpr int NT = D / 16;
   constexpr int IMG = img_bytes(D);
   const int bgi = blockIdx.x / blocks_per_batch;
   const int64_t i = static_cast<int64_t>(blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
@@ -226,7 +235,8 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
       r[k] = make_uint4(0u, 0u, 0u, 0u);
     }
   uint8_t* base = img + (static_cast<int64_t>(bgi) * ntiles + kb / (kKvTile / kBlock)) * IMG;
-  const int c = kb % (kKvTile / kBlock);
+  const int bt = kb % (kKvTile / kBlock);  // block within the tile
+  const int step = bt >> 1;
 #pragma unroll
   for (int ch = 0; ch < CPT; ++ch) {
     uint32_t f[kBlock];
@@ -244,9 +254,10 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
     out.z = pack8(f + 16, inv);
     out.w = pack8(f + 24, inv);
     const int d = cg * CPT + ch;
-    const int l = 16 * c + (d & 15);
-    *reinterpret_cast<uint4*>(base + kImgVc + (d >> 4) * 1024 + l * 16) = out;
-    base[img_vs(D) + l * NT + (d >> 4)] = static_cast<uint8_t>(X);
+    const int l = (d & 31) + 32 * (bt & 1);
+    const int op = (d >> 5) * 2 + step;  // operand index of (channel tile, key step)
+    *reinterpret_cast<uint4*>(base + img_vc(D) + op * 1024 + l * 16) = out;
+    base[img_vs(D) + l * (D / 16) + op] = static_cast<uint8_t>(X);
   }
 }
 

@@ -74,33 +74,35 @@ def decode_kv_images(w, off, B, Hkv, Skv, D):
     include/mxattn.h) back into plain arrays: K~ codes [B*Hkv][rows][D/2],
     K~ scales [B*Hkv][rows][D/32], V~^T codes [B*Hkv][D][rows/2], V~^T
     scales [B*Hkv][D][rows/32] with rows = Skv rounded up to 128, plus the
-    K~ bytes of the unused contraction lanes (D = 64), which must be zero."""
+    padding bytes at the end of each image, which must be zero."""
     BG, IMG = B * Hkv, off[3]
     nt = (Skv + 127) // 128
-    NT = D // 16
-    ks_off = 8192 + 64 * D
-    vs_off = ks_off + 512
+    DH, NC = D // 64, D // 32
     im = w[off[2]:off[2] + BG * nt * IMG].reshape(BG, nt, IMG)
-    T, t, l = np.meshgrid(np.arange(nt), np.arange(8), np.arange(64), indexing="ij")
-    krow = T * 128 + 32 * ((l % 16) // 4) + 4 * t + l % 4
-    kblk = l // 16
-    kc = im[:, :, :8192].reshape(BG, nt, 8, 64, 16)
-    ksc = im[:, :, ks_off:ks_off + 512].reshape(BG, nt, 64, 8)
-    k_codes = np.zeros((BG, nt * 128, 4, 16), np.uint8)
-    k_scales = np.zeros((BG, nt * 128, 4), np.uint8)
-    k_codes[:, krow, kblk, :] = kc[:, T, t, l, :]
-    k_scales[:, krow, kblk] = ksc[:, T, l, t]
-    dc = D // 32
-    unused = np.concatenate([k_codes[:, :, dc:, :].ravel(), k_scales[:, :, dc:].ravel()])
-    T, n, l = np.meshgrid(np.arange(nt), np.arange(NT), np.arange(64), indexing="ij")
-    ch = 16 * n + l % 16
-    vblk = T * 4 + l // 16
-    vc = im[:, :, 8192:8192 + 64 * D].reshape(BG, nt, NT, 64, 16)
-    vsc = im[:, :, vs_off:vs_off + 4 * D].reshape(BG, nt, 64, NT)
+    # K~: [subtile t][d-half i][lane l][16]; lane l of (t, i) holds the key
+    # 64 (t/2) + 32 (R/4 % 2) + 16 (t%2) + 4 (R/8) + R%4 (R = l%32) of the
+    # tile, elements 32 (2 i + l/32) .. +31
+    T, t, i, l = np.meshgrid(np.arange(nt), np.arange(4), np.arange(DH), np.arange(64), indexing="ij")
+    R = l % 32
+    krow = T * 128 + 64 * (t // 2) + 32 * ((R // 4) % 2) + 16 * (t % 2) + 4 * (R // 8) + R % 4
+    kblk = 2 * i + l // 32
+    kc = im[:, :, :64 * D].reshape(BG, nt, 4, DH, 64, 16)
+    ksc = im[:, :, 128 * D:132 * D].reshape(BG, nt, 64, D // 16)
+    k_codes = np.zeros((BG, nt * 128, D // 32, 16), np.uint8)
+    k_scales = np.zeros((BG, nt * 128, D // 32), np.uint8)
+    k_codes[:, krow, kblk, :] = kc[:, T, t, i, l, :]
+    k_scales[:, krow, kblk] = ksc[:, T, l, t * DH + i]
+    # V~^T: [channel tile c][key step s][lane l][16]; lane l holds channel
+    # 32 c + l%32, keys 64 s + 32 (l/32) .. +31 of the tile
+    T, c, s_, l = np.meshgrid(np.arange(nt), np.arange(NC), np.arange(2), np.arange(64), indexing="ij")
+    ch = 32 * c + l % 32
+    vblk = T * 4 + 2 * s_ + l // 32
+    vc = im[:, :, 64 * D:128 * D].reshape(BG, nt, NC, 2, 64, 16)
+    vsc = im[:, :, 132 * D:136 * D].reshape(BG, nt, 64, D // 16)
     vt_codes = np.zeros((BG, D, nt * 4, 16), np.uint8)
     vt_scales = np.zeros((BG, D, nt * 4), np.uint8)
-    vt_codes[:, ch, vblk, :] = vc[:, T, n, l, :]
-    vt_scales[:, ch, vblk] = vsc[:, T, l, n]
-    pad = im[:, :, vs_off + 4 * D:]
-    return (k_codes[:, :, :dc, :].reshape(BG, nt * 128, D // 2), k_scales[:, :, :dc],
-            vt_codes.reshape(BG, D, nt * 64), vt_scales, unused, pad)
+    vt_codes[:, ch, vblk, :] = vc[:, T, c, s_, l, :]
+    vt_scales[:, ch, vblk] = vsc[:, T, l, 2 * c + s_]
+    pad = im[:, :, 136 * D:]
+    return (k_codes.reshape(BG, nt * 128, D // 2), k_scales,
+            vt_codes.reshape(BG, D, nt * 64), vt_scales, pad)

@@ -89,7 +89,7 @@ def test_workspace_and_tile_queries():
     assert L.mxattn_workspace_bytes(1, 2, 1, 64, 64, 96, 1, 3) == 0
     nb = L.mxattn_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
     # K~ + V~^T tile images: 17408 bytes per 128 keys (0.53125 B per element
-    # each, rounded up to 1 KiB per image); the Q~ regions only in the dump size
+    # each); the Q~ regions only in the dump size
     assert nb == 40 * 256 * 17408
     nd = L.mxattn_dump_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
     assert nd >= nb + 40 * 32760 * 128 * 17 // 32
@@ -99,7 +99,7 @@ def test_workspace_and_tile_queries():
     assert off[1] + 40 * 32760 * 4 <= nd
     assert L.mxattn_dump_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 0) == 0  # FP16
     off64, _ = mx.workspace_layout(1, 2, 2, 100, 100, 64, "f32", "ocp")
-    assert off64[3] == 13312
+    assert off64[3] == 9216  # 8704 bytes for D = 64, rounded up to 1 KiB
     with pytest.raises(mx.MxError):
         mx.workspace_layout(1, 2, 2, 64, 64, 128, "bf16", "fp16")
     # K/V element count past 2^40 (its image size would overflow): rejected
@@ -156,7 +156,7 @@ def test_decode_rejects_bad_args():
     def d(dtype=1, B=1, Hq=8, Hkv=2, Sq=1, Skv=1000, D=128, causal=0, mode=3, ws=P, wsb=big, q=P):
         return L.mxattn_decode(q, P, P, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode, P, ws, wsb, None)
     assert d(mode=0) == -2                 # FP16 mode: use mxattn_fwd
-    assert d(Sq=5) == -2                   # (Hq/Hkv) * Sq > 16
+    assert d(Sq=9) == -2                   # (Hq/Hkv) * Sq > 32
     assert d(D=96) == -2
     assert d(causal=1, Sq=4, Skv=3) == -2  # causal needs Sq <= Skv
     assert d(Hq=6, Hkv=4) == -1
@@ -194,7 +194,7 @@ def test_varlen_rejects_bad_args():
     assert d(lk=None) == -1
     assert d(lk=odd) == -5
     assert d(pc=P) == -1
-    assert d(Sq=5) == -2            # (Hq/Hkv) * Sq > 16
+    assert d(Sq=9) == -2            # (Hq/Hkv) * Sq > 32
     assert d(mode=0) == -2
     assert L.mxattn_prepare_varlen(P, P, P, 1, 2, 8, 2, 1, 4000, 128, None, 3, P, big, None) == -1
     assert L.mxattn_prepare_varlen(P, P, P, 1, 2, 8, 2, 1, 4000, 128, P, 0, P, big, None) == -2

@@ -32,9 +32,9 @@ def check_workspace(mx, ws, q, k, v, mode, with_q):
         rc, rs = oracle.quantize(q, rule)
         assert np.array_equal(w[off[0]:off[0] + rc.size], rc)
         assert np.array_equal(w[off[1]:off[1] + rs.size], rs)
-    kc, ks, vc, vs, unused, pad = decode_kv_images(w, off, B, Hkv, Skv, D)
+    kc, ks, vc, vs, pad = decode_kv_images(w, off, B, Hkv, Skv, D)
     assert skv_ld == kc.shape[1]
-    assert not unused.any() and not pad.any()
+    assert not pad.any()
     pad32 = (Skv + 31) // 32 * 32
     for bg in range(B * Hkv):
         rc, rs = oracle.quantize(k.reshape(B * Hkv, Skv, D)[bg], rule)

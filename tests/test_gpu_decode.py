@@ -65,6 +65,8 @@ SMALL = [
     (1, 16, 2, 2, 2049, 128, True),     # 16 query columns, ragged keys
     (1, 8, 8, 16, 4097, 128, True),     # last split (key 4096) empty for rows 0..14
     (3, 6, 2, 5, 1300, 64, True),       # 15 columns
+    (1, 32, 4, 4, 1500, 128, True),     # 32 query columns (the whole tile)
+    (2, 8, 1, 3, 900, 64, False),       # 24 columns, one KV head
 ]
 
 
