@@ -291,23 +291,22 @@ struct TileStats {
   uint32_t X[2];
 };
 
-// First level of the block maxima: 10 v_max3 over 30 of a block's 32 values.
-__device__ __forceinline__ void bmax_l1(const v16f& a, const v16f& b, float (&o)[12]) {
+// First level of the block maxima: 10 v_max3 over 30 of a block's 32
+// values (a = its first 16 keys, b = the next 16).
+__device__ __forceinline__ void bmax_l1(const v16f& a, const v16f& b, float (&o)[10]) {
 #pragma unroll
   for (int k = 0; k < 5; ++k) o[k] = fmaxf(fmaxf(a[3 * k], a[3 * k + 1]), a[3 * k + 2]);
   o[5] = fmaxf(fmaxf(a[15], b[0]), b[1]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) o[6 + k] = fmaxf(fmaxf(b[2 + 3 * k], b[3 + 3 * k]), b[4 + 3 * k]);
-  o[10] = b[14];
-  o[11] = b[15];
 }
-// Rest of the tree: 12 values to one (4 + 1 v_max3 and one max).
-__device__ __forceinline__ float bmax_l2(const float (&o)[12]) {
+// Rest of the tree: the 10 values and b's last two to one (5 v_max3, one max).
+__device__ __forceinline__ float bmax_l2(const float (&o)[10], const v16f& b) {
   const float p0 = fmaxf(fmaxf(o[0], o[1]), o[2]);
   const float p1 = fmaxf(fmaxf(o[3], o[4]), o[5]);
   const float p2 = fmaxf(fmaxf(o[6], o[7]), o[8]);
-  const float p3 = fmaxf(fmaxf(o[9], o[10]), o[11]);
-  return fmaxf(fmaxf(p0, p1), fmaxf(p2, p3));
+  const float p3 = fmaxf(fmaxf(o[9], b[14]), b[15]);
+  return fmaxf(fmaxf(fmaxf(p0, p1), p2), p3);
 }
 
 // delta, alpha and the running max from the row max of this tile; then the
@@ -336,10 +335,10 @@ __device__ __forceinline__ void block_scale(float bmax, float delta, float sl2, 
 // All statistics of a tile at once (the short-query kernel).
 template <int UOS, int PNQ>
 __device__ __forceinline__ TileStats tile_stats(float& m, float& mref, const v16f (&s)[kSub], float sl2) {
-  float o0[12], o1[12];
+  float o0[10], o1[10];
   bmax_l1(s[0], s[1], o0);
   bmax_l1(s[2], s[3], o1);
-  const float b0 = bmax_l2(o0), b1 = bmax_l2(o1);
+  const float b0 = bmax_l2(o0, s[1]), b1 = bmax_l2(o1, s[3]);
   const float rowmax = xhalf_max(fmaxf(b0, b1));
   TileStats r;
   r.delta = stats_delta<UOS, PNQ>(m, mref, rowmax, sl2, r.alpha);
@@ -407,6 +406,53 @@ __device__ __forceinline__ uint32_t p_oct(const v16f& sv, int o, float sl2, floa
   return x;
 }
 
+// Half HQ of both P~ dwords of one subtile (registers 4 HQ .. +3 and
+// 8 + 4 HQ .. +3 of sv), the two conversion chains interleaved so that no
+// conversion waits on the one just before it.
+template <int PNQ, int HQ>
+__device__ __forceinline__ void p_pair(const v16f& sv, float sl2, float kofs, uint32_t& x0, uint32_t& x1,
+                                       uint32_t& b0, uint32_t& b1, float& vsum) {
+  if (PNQ == 2) {
+    const float c2 = 2.0f * sl2;
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[i] = fmaf(sv[4 * HQ + i], c2, kofs);
+      t[4 + i] = fmaf(sv[8 + 4 * HQ + i], c2, kofs);
+    }
+    // all four bytes of each word are written over the two halves
+    x0 = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 2 * HQ, HQ ? x0 : __float_as_uint(t[0]));
+    x1 = __builtin_amdgcn_cvt_pk_u8_f32(t[4], 2 * HQ, HQ ? x1 : __float_as_uint(t[4]));
+    b0 = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 2 * HQ, HQ ? b0 : __float_as_uint(t[1]));
+    b1 = __builtin_amdgcn_cvt_pk_u8_f32(t[5], 2 * HQ, HQ ? b1 : __float_as_uint(t[5]));
+    x0 = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 2 * HQ + 1, x0);
+    x1 = __builtin_amdgcn_cvt_pk_u8_f32(t[6], 2 * HQ + 1, x1);
+    b0 = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 2 * HQ + 1, b0);
+    b1 = __builtin_amdgcn_cvt_pk_u8_f32(t[7], 2 * HQ + 1, b1);
+    if (HQ) {
+      x0 |= b0 << 4;
+      x1 |= b1 << 4;
+    }
+    return;
+  }
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = __builtin_amdgcn_exp2f(fmaf(sv[4 * HQ + i], sl2, -kofs));
+    v[4 + i] = __builtin_amdgcn_exp2f(fmaf(sv[8 + 4 * HQ + i], sl2, -kofs));
+  }
+  if (!PNQ) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vsum += v[i];
+  }
+  // all four bytes are written over the two halves, so the first write may
+  // start from any value
+  x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(HQ ? x0 : __float_as_uint(v[0]), v[0], v[1], 1.0f, 2 * HQ);
+  x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(HQ ? x1 : __float_as_uint(v[4]), v[4], v[5], 1.0f, 2 * HQ);
+  x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x0, v[2], v[3], 1.0f, 2 * HQ + 1);
+  x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x1, v[6], v[7], 1.0f, 2 * HQ + 1);
+}
+
 // Non-PNQ denominator: l = alpha l + sum of the unquantized p of the lane's
 // two blocks of this tile (v sums in their scaled domains).
 template <int D, int PNQ>
@@ -437,34 +483,30 @@ __device__ __forceinline__ void dump_block(const MxAttnArgs& a, int64_t bh, int 
   }
 }
 
-// Q~ operand of one lane: query row `row` (global row index), d-block grp
-// (< D/32), quantized from the raw row; the dump variants also store it.
-template <int D, int UOS, int DUMP>
-__device__ __forceinline__ void quant_q_block(const MxAttnArgs& a, int64_t row, int grp, uint4& qop,
-                                              uint32_t& X) {
-  const int64_t e0 = row * D + grp * 32;
-  const void* src = a.q_bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.q) + e0)
-                             : static_cast<const void*>(static_cast<const float*>(a.q) + e0);
-  qop = quant_block32<UOS>(src, a.q_bf16 != 0, X);
-  if (DUMP) {
-    *reinterpret_cast<uint4*>(a.qc + row * (D / 2) + grp * 16) = qop;
-    a.qs[row * (D / 32) + grp] = static_cast<uint8_t>(X);
-  }
-}
 // The lane's Q~ operands (query row qrow, valid below sq): d-blocks
 // 2 i + l/32 for d-half i; byte i of *qsc their E8M0 bytes.  Rows past the
-// sequence are zero codes under scale 1.
+// sequence are zero codes under scale 1.  The dump variants also store the
+// codes and bytes.
 template <int D, int UOS, int DUMP>
 __device__ __forceinline__ void load_q(const MxAttnArgs& a, int64_t row0, int qrow, bool valid, int half,
                                        uint4 (&qop)[D / 64], uint32_t& qsc) {
   qsc = 0x7F7F7F7Fu;
+  const int64_t row = row0 + qrow;
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
     qop[i] = make_uint4(0, 0, 0, 0);
     if (valid) {
+      const int grp = 2 * i + half;
+      const int64_t e0 = row * D + grp * 32;
+      const void* src = a.q_bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.q) + e0)
+                                 : static_cast<const void*>(static_cast<const float*>(a.q) + e0);
       uint32_t X;
-      quant_q_block<D, UOS, DUMP>(a, row0 + qrow, 2 * i + half, qop[i], X);
+      qop[i] = quant_block32<UOS>(src, a.q_bf16 != 0, X);
       qsc = (qsc & ~(0xFFu << (8 * i))) | (X << (8 * i));
+      if (DUMP) {
+        *reinterpret_cast<uint4*>(a.qc + row * (D / 2) + grp * 16) = qop[i];
+        a.qs[row * (D / 32) + grp] = static_cast<uint8_t>(X);
+      }
     }
   }
 }
@@ -516,19 +558,19 @@ __device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<
   if (MASK) mask_tile(S, lim);
   fence();
   TileStats ts;
-  float o0[12], o1[12];
+  float o0[10], o1[10];
   pv_one<D>(w, 0, 1, cy.vop[0], cy.vsc, cy.pop, cy.X);
   bmax_l1(S[0], S[1], o0);
 #pragma unroll
-  for (int k = 0; k < 12; ++k) pin_out(o0[k]);
+  for (int k = 0; k < 10; ++k) pin_out(o0[k]);
   fence();
   if (NH > 1) pv_one<D>(w, 1, 1, cy.vop[1], cy.vsc, cy.pop, cy.X);
   bmax_l1(S[2], S[3], o1);
 #pragma unroll
-  for (int k = 0; k < 12; ++k) pin_out(o1[k]);
+  for (int k = 0; k < 10; ++k) pin_out(o1[k]);
   fence();
   if (PNQ) w.lacc = mfma_rowsum(ones, cy.pop, w.lacc, cy.X);
-  float b0 = bmax_l2(o0), b1 = bmax_l2(o1);
+  float b0 = bmax_l2(o0, S[1]), b1 = bmax_l2(o1, S[3]);
   const float rowmax = xhalf_max(fmaxf(b0, b1));
   ts.delta = stats_delta<UOS, PNQ>(w.m, w.mref, rowmax, sl2, ts.alpha);
   block_scale<UOS, PNQ>(b0, ts.delta, sl2, ts.X[0], ts.kofs[0]);
@@ -546,16 +588,24 @@ __device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<
 #pragma unroll
   for (int i = 0; i < DH; ++i) kop[i] = k_op<D>(st_next, 0, i, lane);
   const Sc<D> ksc = read_sc<D>(st_next, img_ks(D), lane);
-  uint32_t pw[2][4];
+  uint32_t pw[2][4], pb[2][4];
   float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-  for (int o = 0; o < 2; ++o) {
-    if (NH + o < NC) pv_one<D>(w, NH + o, 1, cy.vop[NH + o], cy.vsc, cy.pop, cy.X);
-    pw[0][o] = p_oct<PNQ>(S[0], o, sl2, ts.kofs[0], v0);
-    pin_out(pw[0][o]);
-    if (!PNQ) pin_out(v0);
-    fence();
+  pv_one<D>(w, NH, 1, cy.vop[NH], cy.vsc, cy.pop, cy.X);
+  p_pair<PNQ, 0>(S[0], sl2, ts.kofs[0], pw[0][0], pw[0][1], pb[0][0], pb[0][1], v0);
+  pin_out(pw[0][0]);
+  pin_out(pw[0][1]);
+  if (PNQ == 2) {
+    pin_out(pb[0][0]);
+    pin_out(pb[0][1]);
   }
+  if (!PNQ) pin_out(v0);
+  fence();
+  if (NH > 1) pv_one<D>(w, NH + 1, 1, cy.vop[NH + 1], cy.vsc, cy.pop, cy.X);
+  p_pair<PNQ, 1>(S[0], sl2, ts.kofs[0], pw[0][0], pw[0][1], pb[0][0], pb[0][1], v0);
+  pin_out(pw[0][0]);
+  pin_out(pw[0][1]);
+  if (!PNQ) pin_out(v0);
+  fence();
   rescale<D, PNQ>(w, ts);
 
   // ---- step 3: P~ of subtile 1 | S^T (tile j+1) subtile 0; read K~ of
@@ -570,12 +620,18 @@ __device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<
   for (int c = 0; c < NH; ++c) vop0[c] = v_op<D>(st_cur, c, 0, lane);
   {
     v16f sn = s_part<D, 0>(0, kop[0], ksc, qop, qsc, w.cneg);
-    pw[0][2] = p_oct<PNQ>(S[1], 0, sl2, ts.kofs[0], v0);
+    p_pair<PNQ, 0>(S[1], sl2, ts.kofs[0], pw[0][2], pw[0][3], pb[0][2], pb[0][3], v0);
     pin_out(pw[0][2]);
+    pin_out(pw[0][3]);
+    if (PNQ == 2) {
+      pin_out(pb[0][2]);
+      pin_out(pb[0][3]);
+    }
     if (!PNQ) pin_out(v0);
     fence();
     if constexpr (DH == 2) sn = s_part<D, 1>(0, kop[1], ksc, qop, qsc, sn);
-    pw[0][3] = p_oct<PNQ>(S[1], 1, sl2, ts.kofs[0], v0);
+    p_pair<PNQ, 1>(S[1], sl2, ts.kofs[0], pw[0][2], pw[0][3], pb[0][2], pb[0][3], v0);
+    pin_out(pw[0][2]);
     pin_out(pw[0][3]);
     if (!PNQ) pin_out(v0);
     S[0] = sn;
@@ -592,13 +648,19 @@ __device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<
   for (int c = NH; c < NC; ++c) vop0[c] = v_op<D>(st_cur, c, 0, lane);
   {
     v16f sn = s_part<D, 0>(1, kop1[0], ksc, qop, qsc, w.cneg);
-    pw[1][0] = p_oct<PNQ>(S[2], 0, sl2, ts.kofs[1], v1);
+    p_pair<PNQ, 0>(S[2], sl2, ts.kofs[1], pw[1][0], pw[1][1], pb[1][0], pb[1][1], v1);
     pin_out(pw[1][0]);
+    pin_out(pw[1][1]);
+    if (PNQ == 2) {
+      pin_out(pb[1][0]);
+      pin_out(pb[1][1]);
+    }
     if (!PNQ) pin_out(v1);
     fence();
     if constexpr (DH == 2) sn = s_part<D, 1>(1, kop1[1], ksc, qop, qsc, sn);
     pv_one<D>(w, 0, 0, vop0[0], vsc, p0, ts.X[0]);
-    pw[1][1] = p_oct<PNQ>(S[2], 1, sl2, ts.kofs[1], v1);
+    p_pair<PNQ, 1>(S[2], sl2, ts.kofs[1], pw[1][0], pw[1][1], pb[1][0], pb[1][1], v1);
+    pin_out(pw[1][0]);
     pin_out(pw[1][1]);
     if (!PNQ) pin_out(v1);
     S[1] = sn;
@@ -614,13 +676,19 @@ __device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<
   for (int i = 0; i < DH; ++i) kop3[i] = k_op<D>(st_next, 3, i, lane);
   {
     v16f sn = s_part<D, 0>(2, kop2[0], ksc, qop, qsc, w.cneg);
-    pw[1][2] = p_oct<PNQ>(S[3], 0, sl2, ts.kofs[1], v1);
+    p_pair<PNQ, 0>(S[3], sl2, ts.kofs[1], pw[1][2], pw[1][3], pb[1][2], pb[1][3], v1);
     pin_out(pw[1][2]);
+    pin_out(pw[1][3]);
+    if (PNQ == 2) {
+      pin_out(pb[1][2]);
+      pin_out(pb[1][3]);
+    }
     if (!PNQ) pin_out(v1);
     fence();
     if constexpr (DH == 2) sn = s_part<D, 1>(2, kop2[1], ksc, qop, qsc, sn);
     pv_one<D>(w, NH, 0, vop0[NH], vsc, p0, ts.X[0]);
-    pw[1][3] = p_oct<PNQ>(S[3], 1, sl2, ts.kofs[1], v1);
+    p_pair<PNQ, 1>(S[3], sl2, ts.kofs[1], pw[1][2], pw[1][3], pb[1][2], pb[1][3], v1);
+    pin_out(pw[1][2]);
     pin_out(pw[1][3]);
     if (!PNQ) pin_out(v1);
     S[2] = sn;
@@ -645,6 +713,20 @@ __device__ __forceinline__ void kv_iter(WaveState<D>& w, v16f (&S)[kSub], Carry<
   dump_block<DUMP>(a, bh, qrow, visit, j0 + 32 * half, p0, ts.X[0]);
   dump_block<DUMP>(a, bh, qrow, visit, j0 + 64 + 32 * half, p1, ts.X[1]);
   fence();
+}
+
+// Store a finished 32-column tile's O rows (lane l: its query row, channels
+// 32 c + 8 g + 4 (l/32) + 0..3); nothing when orow is null.
+template <int D>
+__device__ __forceinline__ void store_o(float* orow, const v16f (&o)[D / 32], int half) {
+  if (orow) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        *reinterpret_cast<float4*>(orow + 32 * c + 8 * gq + 4 * half) =
+            make_float4(o[c][4 * gq], o[c][4 * gq + 1], o[c][4 * gq + 2], o[c][4 * gq + 3]);
+  }
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
@@ -723,12 +805,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   }
   const int koff = CAUSAL ? skv - sq : 0;  // causal: row i sees keys j <= i + koff
 
+  // The finished O rows of a job are held in registers until the next job
+  // of the workgroup has requested its first KV tiles and Q rows: stores
+  // count in the same in-order vector-memory counter as loads, so storing
+  // first would make the next job's first waits wait for the stores too.
+  v16f ofin[NC];
+  float* orow = nullptr;  // this lane's pending row (null: none)
   for (int job = 0; job < njobs; ++job) {
     // the query tile of this job (causal: the longer one first)
     const int qb = CAUSAL ? (job == 0 ? nqb - 1 - slot : slot) : slot;
     const int q0 = qb * kMxQTile;
     const int qw0 = q0 + wave * kQW;  // first query row of this wave
-    if (q0 >= sq) continue;  // whole workgroup (uniform), before any barrier of the job
+    if (q0 >= sq) {  // whole workgroup (uniform), before any barrier of the job
+      store_o<D>(orow, ofin, half);
+      orow = nullptr;
+      continue;
+    }
     // every wave is done with the previous job's stages before they refill
     if (job > 0) {
       asm volatile("" ::: "memory");
@@ -736,16 +828,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
       asm volatile("" ::: "memory");
     }
 
-    // Q~ operands (B of S^T): query column `col`, d-blocks 2 i + half,
-    // quantized here; rows past the sequence are zero codes.
     int qrow = qw0 + col;
-    uint4 qop[D / 64];
-    uint32_t qsc;
-    load_q<D, UOS, DUMP>(a, bh * a.Sq, qrow, qrow < sq, half, qop, qsc);
-
-    WaveState<D> w;
-    init_state<D>(w);
-
+    const bool qvalid = qrow < sq;
     const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
     const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
     // tiles this workgroup visits: all, or up to its last causal diagonal tile
@@ -757,37 +841,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     const int nmain = CAUSAL ? min((q0 + koff + 1) / kKvTile, skv / kKvTile) : skv / kKvTile;
     const int last_w = qw0 >= sq ? -1 : (CAUSAL ? min((qw0 + kQW - 1 + koff) / kKvTile, ntk - 1) : ntk - 1);
     const int klim = CAUSAL ? min(skv - 1, qrow + koff) : skv - 1;
-    if (qrow >= sq) qrow = a.Sq;  // past the sequence: never dumped or stored
 
     // wave-uniform (the divisions above run on the vector unit): scalar
     // registers, so the tile loads take the scalar-base form
     const uint8_t* img = uniform_ptr(a.img + bg * nt * static_cast<int64_t>(IMG));
-    const int nl = loads_per_tile<D>(wave);
 
     // Ring of kStages LDS stages: tile jt lives in stage jt % kStages.  Tiles
-    // 0 and 1 are requested up front, and S^T of tile 0 is formed once it has
-    // landed.  At the top of iteration jt each wave waits for all its loads
-    // (those of tile jt+1, requested an iteration earlier); the barrier then
-    // makes every wave's loads visible and tells that every wave has finished
-    // iteration jt-1.  The loads of tile jt+2 then refill the stage of tile
+    // 0 and 1 are requested first, then this lane's Q rows; the previous
+    // job's O rows are stored only once all of these have landed, so that
+    // the stores drain while this job starts (the wait at the top of
+    // iteration 0 is skipped: it would wait for them).  The barrier makes
+    // every wave's loads visible.  At the top of iteration jt > 0 each wave
+    // waits for its loads of tile jt+1 (requested an iteration earlier) and
+    // the barrier tells that every wave has finished iteration jt-1.  The loads of tile jt+2 then refill the stage of tile
     // jt-2, whose last operands (V~ of key step 1, read in iteration jt-2)
     // were consumed in iteration jt-1.  Stage 3 stands for tile -1: the
     // second key step of its O^T product multiplies zero P~ codes, and only
     // its V~ scale bytes must be finite (set to 1.0 here).
     issue_tile<D>(lds0, img, wave, lane);
     if (ntiles > 1) issue_tile<D>(lds1, img + IMG, wave, lane);
+    // Q~ operands (B of S^T): query column `col`, d-blocks 2 i + half;
+    // rows past the sequence are zero codes.
+    uint4 qop[D / 64];
+    uint32_t qsc;
+    load_q<D, UOS, DUMP>(a, bh * a.Sq, qrow, qvalid, half, qop, qsc);
+    if (!qvalid) qrow = a.Sq;  // past the sequence: never dumped or stored
+    wait_vmcnt<0>();  // tiles 0 and 1 (and Q) have landed
+    asm volatile("" ::: "memory");
+    store_o<D>(orow, ofin, half);
+    orow = nullptr;
     for (int i = threadIdx.x; i < 64 * (D / 16) / 4; i += kThreads)
       reinterpret_cast<uint32_t*>(lds3 + img_vs(D))[i] = 0x7F7F7F7Fu;
-    if (ntiles > 1) {
-      if (nl == 5) wait_vmcnt<5>(); else if (nl == 4) wait_vmcnt<4>(); else if (nl == 3) wait_vmcnt<3>(); else wait_vmcnt<2>();
-    } else {
-      wait_vmcnt<0>();
-    }
     wait_lgkm0();  // the scale bytes above, written before any wave reads them
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
+    WaveState<D> w;
+    init_state<D>(w);
     v16f S[kSub];
     {
       const Sc<D> ksc = read_sc<D>(lds0, img_ks(D), lane);
@@ -813,7 +904,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
       for (int k = 0; k < kStages; ++k) {
         const int jt = jb + k;
         if (jt < nmain) {
-          wait_vmcnt<0>();
+          if (jt > 0) wait_vmcnt<0>();  // tile 1 was waited for in the prologue
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
@@ -828,7 +919,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     // tiles [nmain, ntiles): the sequence end or the causal diagonal (one or
     // two tiles), keys masked per row; stages picked at run time
     for (int jt = nmain; jt < ntiles; ++jt) {
-      wait_vmcnt<0>();
+      if (jt > 0) wait_vmcnt<0>();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -845,31 +936,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
     for (int c = 0; c < NC; ++c) pv_one<D>(w, c, 1, cy.vop[c], cy.vsc, cy.pop, cy.X);
     if (PNQ) w.lacc = mfma_rowsum(ones, cy.pop, w.lacc, cy.X);
 
-    // The epilogue stores under a per-lane condition.  Pin the accumulators
-    // here so that the matrix-core instructions producing them are not moved
-    // into that divergent region: an MFMA issued with part of EXEC disabled
-    // would drop the operands of the disabled lanes, which other lanes' results
+    // The stores run under a per-lane condition.  Pin the accumulators here
+    // so that the matrix-core instructions producing them are not moved into
+    // that divergent region: an MFMA issued with part of EXEC disabled would
+    // drop the operands of the disabled lanes, which other lanes' results
     // depend on.
 #pragma unroll
     for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(w.oacc[c]));
     asm volatile("" : "+v"(w.lacc));
 
-    // ---- epilogue: O = O_acc / l; lane l holds channels 32 c + 8 g +
-    // 4 (l/32) + 0..3 of its query row ----
+    // O = O_acc / l; lane l holds channels 32 c + 8 g + 4 (l/32) + 0..3 of
+    // its query row
     const float l = PNQ ? w.lacc[0] : xhalf_sum(w.lsum);
     const float inv = 1.0f / l;
-    if (qrow < a.Sq) {
-      float* orow = a.o + (bh * a.Sq + qrow) * D;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 v = make_float4(w.oacc[c][4 * gq] * inv, w.oacc[c][4 * gq + 1] * inv,
-                                       w.oacc[c][4 * gq + 2] * inv, w.oacc[c][4 * gq + 3] * inv);
-          *reinterpret_cast<float4*>(orow + 32 * c + 8 * gq + 4 * half) = v;
-        }
-    }
+    for (int c = 0; c < NC; ++c) ofin[c] = w.oacc[c] * inv;
+    orow = qrow < a.Sq ? a.o + (bh * a.Sq + qrow) * D : nullptr;
   }  // job
+  store_o<D>(orow, ofin, half);
 }
 
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>

@@ -52,26 +52,44 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t f[8], float inv) {
   return r;
 }
 
-// One 32-element block of a row (bf16 when in_bf16, else fp32) to 16 bytes
-// of codes (returned) and its E8M0 byte.
+// The raw bits of one 32-element block of a row: 4 (bf16) or 8 (fp32)
+// 16-byte loads.  Split from the conversion so that a kernel can issue the
+// loads early and convert later.
+struct RawBlock32 {
+  uint4 v[8];
+};
+__device__ __forceinline__ RawBlock32 load_block32(const void* src, bool in_bf16) {
+  RawBlock32 r;
+  const uint4* p = static_cast<const uint4*>(src);
+  if (in_bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = p[i];
+#pragma unroll
+    for (int i = 4; i < 8; ++i) r.v[i] = make_uint4(0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.v[i] = p[i];
+  }
+  return r;
+}
+
+// A loaded block to 16 bytes of codes (returned) and its E8M0 byte.
 template <int UOS>
-__device__ __forceinline__ uint4 quant_block32(const void* src, bool in_bf16, uint32_t& X) {
+__device__ __forceinline__ uint4 quant_raw32(const RawBlock32& r, bool in_bf16, uint32_t& X) {
   uint32_t f[32];
   if (in_bf16) {
-    const uint4* p = static_cast<const uint4*>(src);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 v = p[i];
+      const uint4 v = r.v[i];
       f[8 * i + 0] = v.x << 16; f[8 * i + 1] = v.x & 0xFFFF0000u;
       f[8 * i + 2] = v.y << 16; f[8 * i + 3] = v.y & 0xFFFF0000u;
       f[8 * i + 4] = v.z << 16; f[8 * i + 5] = v.z & 0xFFFF0000u;
       f[8 * i + 6] = v.w << 16; f[8 * i + 7] = v.w & 0xFFFF0000u;
     }
   } else {
-    const uint4* p = static_cast<const uint4*>(src);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint4 v = p[i];
+      const uint4 v = r.v[i];
       f[4 * i + 0] = v.x; f[4 * i + 1] = v.y; f[4 * i + 2] = v.z; f[4 * i + 3] = v.w;
     }
   }
@@ -81,6 +99,13 @@ __device__ __forceinline__ uint4 quant_block32(const void* src, bool in_bf16, ui
   X = e8m0_of_amax<UOS>(m);
   const float inv = inv_scale_of(X);
   return make_uint4(pack8(f, inv), pack8(f + 8, inv), pack8(f + 16, inv), pack8(f + 24, inv));
+}
+
+// One 32-element block of a row (bf16 when in_bf16, else fp32) to 16 bytes
+// of codes (returned) and its E8M0 byte.
+template <int UOS>
+__device__ __forceinline__ uint4 quant_block32(const void* src, bool in_bf16, uint32_t& X) {
+  return quant_raw32<UOS>(load_block32(src, in_bf16), in_bf16, X);
 }
 
 }  // namespace mxk
