@@ -363,7 +363,8 @@ int mxq_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, int o
   if (n < 0 || n % mxk::kBlock != 0) return MX_ERR_ARG;
   if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_ARG;
   if (n == 0) return MX_OK;
-  if (n / 8 + 256 > kMaxItems) return MX_ERR_UNSUPPORTED;  // one thread per 8 elements
+  // at most one work item per 8 elements (the kernel takes 32 per thread)
+  if (n / 8 + 256 > kMaxItems) return MX_ERR_UNSUPPORTED;
   if (!codes || !scales || !y) return MX_ERR_ARG;
   if (!aligned(codes, 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
   return to_status(mxk::launch_dequant(codes, scales, n, out_dtype == MX_BF16, y,

@@ -261,7 +261,11 @@ __global__ __launch_bounds__(kThreads) void quant_vimg_kernel(
   }
 }
 
-// Dequantize: each lane expands one dword of codes (8 elements).
+// Dequantize: each lane expands UNROLL dwords of codes (8 elements each), a
+// workgroup's lanes taking consecutive dwords in each of UNROLL rounds, so
+// every wave instruction reads 256 contiguous bytes of codes and writes
+// 1 KiB (bf16) or 2 KiB (fp32) of contiguous output; all loads of a lane
+// are issued before its first store.
 // Magnitudes times 2: {0,1,2,3,4,6,8,12} packed as nibbles.
 __device__ __forceinline__ float dq(uint32_t code, int ex) {
   uint32_t m2 = (0xC8643210u >> (4u * (code & 7u))) & 0xFu;
@@ -269,30 +273,44 @@ __device__ __forceinline__ float dq(uint32_t code, int ex) {
   return (code & 8u) ? -v : v;
 }
 
-template <int OUT_BF16>
+template <int OUT_BF16, int UNROLL>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     int64_t n_oct, void* __restrict__ y) {
-  int64_t o = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (o >= n_oct) return;
-  uint32_t c = __builtin_nontemporal_load(codes + o);
-  const uint32_t X = scales[o >> 2];
-  int ex = static_cast<int>(X) - 128;  // magnitude*2 * 2^(X-128)
-  float v[8];
+  uint32_t c[UNROLL], X[UNROLL];
+  int64_t o[UNROLL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (X == 255u) ? __builtin_nanf("") : dq((c >> (4 * i)) & 0xFu, ex);
-  if (OUT_BF16) {
-    uint4 w;
-    w.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
-    w.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
-    w.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
-    w.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
-    const u32x4 wv = {w.x, w.y, w.z, w.w};
-    __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(y) + o);
-  } else {
-    float4* p = reinterpret_cast<float4*>(y) + 2 * o;
-    p[0] = make_float4(v[0], v[1], v[2], v[3]);
-    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  for (int u = 0; u < UNROLL; ++u) {
+    o[u] = (static_cast<int64_t>(blockIdx.x) * UNROLL + u) * kThreads + threadIdx.x;
+    c[u] = 0;
+    X[u] = 127;
+    if (o[u] < n_oct) {
+      c[u] = __builtin_nontemporal_load(codes + o[u]);
+      X[u] = scales[o[u] >> 2];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    if (o[u] >= n_oct) continue;
+    const int ex = static_cast<int>(X[u]) - 128;  // magnitude*2 * 2^(X-128)
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (X[u] == 255u) ? __builtin_nanf("") : dq((c[u] >> (4 * i)) & 0xFu, ex);
+    if (OUT_BF16) {
+      uint4 w;
+      w.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
+      w.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
+      w.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
+      w.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
+      const u32x4 wv = {w.x, w.y, w.z, w.w};
+      __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(y) + o[u]);
+    } else {
+      u32x4* p = reinterpret_cast<u32x4*>(y) + 2 * o[u];
+      const u32x4 w0 = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+      const u32x4 w1 = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+      __builtin_nontemporal_store(w0, p);
+      __builtin_nontemporal_store(w1, p + 1);
+    }
   }
 }
 
@@ -388,13 +406,15 @@ hipError_t launch_quant_cols(const void* x, int64_t batch, int64_t rows,
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
                           int out_bf16, void* y, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
+  constexpr int U = 4;
   const int64_t n_oct = n / 8;
-  dim3 grid(static_cast<unsigned>((n_oct + kThreads - 1) / kThreads));
+  const int64_t per_block = static_cast<int64_t>(kThreads) * U;
+  dim3 grid(static_cast<unsigned>((n_oct + per_block - 1) / per_block));
   const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
   if (out_bf16)
-    hipLaunchKernelGGL((dequant_kernel<1>), grid, dim3(kThreads), 0, stream, c32, scales, n_oct, y);
+    hipLaunchKernelGGL((dequant_kernel<1, U>), grid, dim3(kThreads), 0, stream, c32, scales, n_oct, y);
   else
-    hipLaunchKernelGGL((dequant_kernel<0>), grid, dim3(kThreads), 0, stream, c32, scales, n_oct, y);
+    hipLaunchKernelGGL((dequant_kernel<0, U>), grid, dim3(kThreads), 0, stream, c32, scales, n_oct, y);
   return hipGetLastError();
 }
 
