@@ -33,13 +33,14 @@ def sources():
 # are finite; masking uses -inf), so max/min need no NaN-quieting
 # canonicalisation of the matrix-core results.
 EXTRA_FLAGS = {
-    # the MXFP4 attention kernels interleave matrix and vector work in fenced
+    # both attention kernels interleave matrix and vector work in fenced
     # regions that follow the source order: instruction selection keeps that
     # order, and machine sinking would move matrix instructions across the
     # uniform branches between the regions
     "attn_mx.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-pre-RA-sched=source",
                     "-mllvm", "-disable-machine-sink"],
-    "attn_f16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "attn_f16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-pre-RA-sched=source",
+                     "-mllvm", "-disable-machine-sink"],
 }
 
 
