@@ -62,7 +62,15 @@ def run_case(q, k, v, causal, mode, rows=None, check_ws=True, label=""):
     if check_ws and mode != "fp16":
         check_workspace(mx, ws, q, k, v, mode, with_q=False)
     bc = mx.kv_tile(D, mode)
-    ref = oracle.attn_rows(q, k, v, causal=causal, mode=MODE_IDS[mode], bc=bc, rows=rows,
+    rq, rk, rv = q, k, v
+    if mode == "fp16" and q.dtype == np.float32:
+        # FP16 mode's operands are 16-bit: fp32 inputs enter as fp16 Q, K and
+        # V, so the reference takes the same rounded operands (the remaining
+        # difference is P's fp16 rounding and the accumulation order); bf16
+        # inputs are used as they are (V's bf16 -> fp16 conversion is exact
+        # in fp16's normal range)
+        rq, rk, rv = (a.astype(np.float16).astype(np.float32) for a in (q, k, v))
+    ref = oracle.attn_rows(rq, rk, rv, causal=causal, mode=MODE_IDS[mode], bc=bc, rows=rows,
                            want_p=(mode != "fp16"))
     got = o.reshape(-1, D)[torch.from_numpy(rows).to(o.device)].double().cpu().numpy()
     err = np.abs(got - ref["o"])
@@ -116,15 +124,28 @@ def test_d64_bf16(mode):
     run_case(q, k, v, True, mode, label="d64")
 
 
-@pytest.mark.parametrize("mode", MX_MODES)
+@pytest.mark.parametrize("mode", ALL_MODES)
 def test_fp32_d128(mode):
-    """fp32 inputs at D = 128 (the kernel quantizes fp32 query rows; ragged
-    query and key ends)."""
+    """fp32 inputs at D = 128 (the MX kernels quantize fp32 query rows; FP16
+    mode converts Q and K to fp16 and runs S^T on the fp16 matrix cores;
+    ragged query and key ends)."""
     rng = np.random.default_rng(15)
     q = (rng.standard_normal((1, 2, 190, 128)) * 1.4).astype(np.float32)
     k = (rng.standard_normal((1, 2, 261, 128)) * 1.4).astype(np.float32)
     v = rng.standard_normal((1, 2, 261, 128)).astype(np.float32)
     run_case(q, k, v, False, mode, label="fp32_d128")
+
+
+@pytest.mark.parametrize("mode", ALL_MODES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_causal(mode, D):
+    """fp32 inputs, causal, GQA, a ragged length that leaves a partial last
+    query tile and a partial last KV tile."""
+    rng = np.random.default_rng(16 + D)
+    q = (rng.standard_normal((1, 4, 333, D)) * 1.2).astype(np.float32)
+    k = (rng.standard_normal((1, 2, 333, D)) * 1.2).astype(np.float32)
+    v = rng.standard_normal((1, 2, 333, D)).astype(np.float32)
+    run_case(q, k, v, True, mode, label=f"fp32_causal_d{D}")
 
 
 @pytest.mark.parametrize("shape", [(1, 1), (5, 1), (1, 1000), (33, 33), (129, 129)])
