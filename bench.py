@@ -473,7 +473,7 @@ def main():
         if not args.no_gemm:
             res["gemm"] = bench_gemm(torch, mx, reps=3)
         if not args.no_decode:
-            res["decode"] = bench_decode(torch, mx, reps=3, varlen=not args.no_varlen)
+            res["decode"] = bench_decode(torch, mx, reps=20, varlen=not args.no_varlen)
         print(json.dumps(res), flush=True)
         return
 

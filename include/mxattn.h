@@ -117,7 +117,9 @@ int mxq_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n,
  * Workspace needed by mxattn_fwd (and mxattn_prepare, mxattn_fwd_prepared,
  * mxattn_fwd_varlen without a dump) for these sizes and mode (bytes; 0 for
  * invalid arguments).  The workspace holds the quantized K/V operands (MX
- * modes: the KV tile images) or the 16-bit operands (FP16 mode).
+ * modes: the KV tile images, followed by one 32-bit arrival counter per
+ * (b, KV head) that the short-query calls use; mxattn_prepare and
+ * mxattn_prepare_varlen set them to 0) or the 16-bit operands (FP16 mode).
  * mxattn_dump_workspace_bytes: the larger workspace of the dump entry points
  * (mxattn_fwd_dump, mxattn_fwd_varlen with a dump), which also receives the
  * kernel's Q~; 0 for the FP16 mode, which has no dump.
@@ -258,9 +260,16 @@ int mxattn_fwd_dump(const void *q, const void *k, const void *v, int dtype,
  * workspace holds mxattn_decode_workspace_bytes(...) bytes (the
  * mxattn_prepare layout followed by the per-split partial states).
  * Q is quantized inside the split kernel (as in mxattn_fwd).
- * mxattn_decode_prepared runs the split and merge kernels on a workspace
- * that mxattn_prepare filled, for the queries q (k, v are not taken: a
- * quantized KV cache is reused across calls; q must not be NULL).
+ * One kernel: each wave leaves its split's (m, l, unnormalized O) in the
+ * workspace and counts itself in its group's arrival counter; the wave that
+ * completes the count merges the group's splits into o and returns the
+ * counter to 0, so the next call on the workspace finds it cleared (no
+ * memset: the calls can be captured into a graph and replayed).  Calls that
+ * overlap on one workspace race.
+ * mxattn_decode_prepared runs that kernel on a workspace that
+ * mxattn_prepare filled (which also cleared the counters), for the queries
+ * q (k, v are not taken: a quantized KV cache is reused across calls; q
+ * must not be NULL).
  * mxattn_decode_dump also writes the P~ codes and E8M0 bytes of selected
  * rows, and the kernel's Q~, as mxattn_fwd_dump.
  * mxattn_decode_split returns MX_ERR_ARG, and the workspace size 0, for bad
@@ -315,8 +324,9 @@ int mxattn_decode_dump(const void *q, const void *k, const void *v, int dtype,
  * mxattn_decode_varlen, for a KV cache quantized once and read by many
  * calls (as mxattn_prepare / mxattn_decode_prepared): the first writes the
  * KV tile images with keys past seqlens_k[b] quantized as zero (MX modes;
- * q is checked, not read); the second runs the split and merge kernels for
- * the queries q with the same seqlens_k (k and v are not taken).
+ * q is checked, not read; the arrival counters cleared); the second runs
+ * the short-query kernel for the queries q with the same seqlens_k (k and v
+ * are not taken).
  */
 int mxattn_fwd_varlen(const void *q, const void *k, const void *v, int dtype,
                       int B, int Hq, int Hkv, int Sq, int Skv, int D,

@@ -1002,9 +1002,9 @@ hipError_t pick_mode(const MxAttnArgs& a, hipStream_t s) {
 // stage of its own (nothing is shared between waves): it reads a tile's
 // operands into registers and then requests the next tile into the stage,
 // whose loads are in flight during the rest of the tile's work.  It leaves
-// (m, l, unnormalized O) per query column; the merge kernel combines the
-// splits in ascending order.  Columns with no visible key in the split
-// leave m = -inf, l = 0, O = 0.
+// (m, l, unnormalized O) per query column; the last wave of the group to
+// finish merges the splits in ascending order.  Columns with no
+// visible key in the split leave m = -inf, l = 0, O = 0.
 
 // Splits of entry b: its keys in spans of split_tiles tiles (0 for an entry
 // with no key).
@@ -1051,6 +1051,98 @@ __device__ bool busy_unit(const MxDecodeArgs& d, int u, int& b, int& g, int& sp)
   return false;
 }
 
+// Merge of one (b, KV group) by the wave that finished it last.  Column c of
+// the group is query (head g G + c / Sq, row c % Sq).  Each lane takes one
+// column and CH channels of it, four columns per pass; the splits are folded
+// in ascending order into the running (M, L, O), each rescaled to the larger
+// max (O = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s); a split
+// that saw no key (m = -inf) adds nothing, and a column that no split saw
+// stays unwritten.  The loads of kMergeChunk splits are issued together.
+constexpr int kMergeChunk = 16;
+
+// Partial states cross XCDs, whose L2 caches are not coherent with one
+// another: they are stored and loaded with the device-scope coherence bit
+// (the encoding the compiler gives agent-scope atomic stores and loads), so
+// the stores write through to the coherent level and the loads read from
+// it, and only the arrival counter needs ordering (a wait for the stores
+// before the atomic increment).
+constexpr int kCoherent = 16;  // cache-policy operand: sc1
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over split slot `slot` of the partial states (offsets
+// within a group's splits stay far below 2^32 bytes).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const MxDecodeArgs& d, int64_t slot) {
+  float* p = d.part + slot * kDecodeCols * decode_slot(D);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0xFFFFFFFFu, 0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ void merge_group(const MxDecodeArgs& d, int b, int g, int64_t bg, float sl2,
+                                            int lane) {
+  const MxAttnArgs& a = d.at;
+  constexpr int CH = D / 16;  // channels per lane: 16 lanes per column
+  constexpr int SL = decode_slot(D);
+  const int ncol = (a.Hq / a.Hkv) * a.Sq;
+  const int ns = a.lens_k ? entry_splits(d, b) : d.nsplit;
+  constexpr int sstride = kDecodeCols * SL;  // floats between splits
+  const int ch = (lane & 15) * CH;
+#pragma unroll 1
+  for (int c0 = 0; c0 < ncol; c0 += 4) {
+    const int c = c0 + (lane >> 4);
+    const bool act = c < ncol;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc<D>(d, bg * d.nsplit);  // split 0 of the group
+    const int cb = (act ? c : 0) * SL * 4;
+    float M = -INFINITY, L = 0.0f;
+    float acc[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) acc[k] = 0.0f;
+#pragma unroll 1
+    for (int s0 = 0; s0 < ns; s0 += kMergeChunk) {
+      float2 ml[kMergeChunk];
+      float4 ov[kMergeChunk][CH / 4];
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u) {
+        // past the last split: reload the last one, taken as empty
+        const int off = cb + min(s0 + u, ns - 1) * sstride * 4;
+        const float2 t = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCoherent));
+        ml[u] = make_float2(s0 + u < ns ? t.x : -INFINITY, t.y);
+#pragma unroll
+        for (int k = 0; k < CH / 4; ++k)
+          ov[u][k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * (4 + ch + 4 * k), 0, kCoherent));
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeChunk; ++u) {
+        // branch-free, so that no load is sunk into a conditional block
+        const float m = ml[u].x;
+        const bool has = m != -INFINITY;
+        const float Mn = has ? fmaxf(M, m) : M;
+        const float wa = has ? __builtin_amdgcn_exp2f((M - Mn) * sl2) : 1.0f;  // 0 while M = -inf
+        const float wb = has ? __builtin_amdgcn_exp2f((m - Mn) * sl2) : 0.0f;
+        L = fmaf(L, wa, ml[u].y * wb);
+#pragma unroll
+        for (int k = 0; k < CH / 4; ++k) {
+          acc[4 * k] = fmaf(acc[4 * k], wa, ov[u][k].x * wb);
+          acc[4 * k + 1] = fmaf(acc[4 * k + 1], wa, ov[u][k].y * wb);
+          acc[4 * k + 2] = fmaf(acc[4 * k + 2], wa, ov[u][k].z * wb);
+          acc[4 * k + 3] = fmaf(acc[4 * k + 3], wa, ov[u][k].w * wb);
+        }
+        M = Mn;
+      }
+    }
+    if (act && M != -INFINITY) {
+      const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * (a.Hq / a.Hkv) + c / a.Sq) * a.Sq + c % a.Sq;
+      const float inv = 1.0f / L;
+      float* out = a.o + row * D + ch;
+#pragma unroll
+      for (int k = 0; k < CH / 4; ++k)
+        *reinterpret_cast<float4*>(out + 4 * k) =
+            make_float4(acc[4 * k] * inv, acc[4 * k + 1] * inv, acc[4 * k + 2] * inv, acc[4 * k + 3] * inv);
+    }
+  }
+}
+
 template <int D, int UOS, int PNQ, int DUMP, int COMPACT>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d, float sl2) {
   const MxAttnArgs& a = d.at;
@@ -1087,6 +1179,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   const bool cvalid = col < G * a.Sq;
   const int hl = cvalid ? col / a.Sq : 0, qi = cvalid ? col % a.Sq : 0;
   const int64_t bh = static_cast<int64_t>(b) * a.Hq + g * G + hl;
+  // this sequence's keys: the padded extent, or its own length
+  const int skv = a.lens_k ? min(max(__builtin_amdgcn_readfirstlane(a.lens_k[b]), 0), a.Skv) : a.Skv;
+  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
+  const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
+  const int t_begin = sp * d.split_tiles;
+  const int t_end = min(t_begin + d.split_tiles, ntk);
+  // the first tile is requested before the Q rows, so that the two first
+  // touches of memory overlap
+  const uint8_t* img = uniform_ptr(a.img + bg * nt * static_cast<int64_t>(IMG));
+  if (t_begin < t_end) issue_rows<D, 1>(st, img + static_cast<int64_t>(t_begin) * IMG, 0, lane);
   uint4 qop[DH];
   uint32_t qsc;
   // every split of a group quantizes the same rows; split 0 dumps them
@@ -1094,16 +1196,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
     load_q<D, UOS, 1>(a, bh * a.Sq, qi, cvalid, half, qop, qsc);
   else
     load_q<D, UOS, 0>(a, bh * a.Sq, qi, cvalid, half, qop, qsc);
-  // this sequence's keys: the padded extent, or its own length
-  const int skv = a.lens_k ? min(max(__builtin_amdgcn_readfirstlane(a.lens_k[b]), 0), a.Skv) : a.Skv;
   // causal: end-aligned; a row with no visible key (klim < 0) stays empty
   const int klim = (cvalid && a.causal) ? qi + (skv - a.Sq) : skv - 1;
   const int qrow = cvalid ? qi : a.Sq;  // rows >= Sq are never dumped
-
-  const int nt = static_cast<int>(a.skv_ld / kKvTile);  // tiles per (b, KV head) image run
-  const int ntk = (skv + kKvTile - 1) / kKvTile;          // tiles holding this sequence's keys
-  const int t_begin = sp * d.split_tiles;
-  const int t_end = min(t_begin + d.split_tiles, ntk);
   // tiles needing the per-key mask: past the key end, or past the first
   // causal limit (skv - Sq)
   const int first_masked = a.causal ? max(skv - a.Sq, 0) / kKvTile : skv / kKvTile;
@@ -1111,8 +1206,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   WaveState<D> w;
   init_state<D>(w);
 
-  const uint8_t* img = uniform_ptr(a.img + bg * nt * static_cast<int64_t>(IMG));
-  if (t_begin < t_end) issue_rows<D, 1>(st, img + static_cast<int64_t>(t_begin) * IMG, 0, lane);
   for (int t = t_begin; t < t_end; ++t) {
     wait_vmcnt<0>();  // this wave's loads of tile t have landed in its stage
     asm volatile("" ::: "memory");
@@ -1169,116 +1262,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   const float l = PNQ ? w.lacc[0] : xhalf_sum(w.lsum);
   const bool empty = klim < t_begin * kKvTile;  // no visible key in this split
   if (cvalid) {  // unused columns are never merged
-    float* pr = d.part + (slot * kDecodeCols + col) * (D + 2);
+    // device-coherent stores (see part_rsrc): slot base in the resource,
+    // byte offsets within the slot
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc<D>(d, slot);
+    const int cb = col * decode_slot(D) * 4;
     if (half == 0) {
-      pr[0] = empty ? -INFINITY : w.m;
-      pr[1] = empty ? 0.0f : l;
+      const float2 ml = make_float2(empty ? -INFINITY : w.m, empty ? 0.0f : l);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), rs, cb, 0, kCoherent);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[2 + 32 * c + 8 * gq + 4 * half + r] = empty ? 0.0f : w.oacc[c][4 * gq + r];
+      for (int gq = 0; gq < 4; ++gq) {
+        float4 ov = make_float4(w.oacc[c][4 * gq], w.oacc[c][4 * gq + 1], w.oacc[c][4 * gq + 2], w.oacc[c][4 * gq + 3]);
+        if (empty) ov = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), rs,
+                                               cb + 4 * (4 + 32 * c + 8 * gq + 4 * half), 0, kCoherent);
+      }
   }
-}
 
-// One wave per query row: O = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s,
-// M the largest m_s, splits in ascending order.  The partial outputs of the
-// first kMergeChunk splits are loaded together with the splits' (m, l), so a
-// row costs one memory round trip when nsplit <= kMergeChunk; the lanes take
-// (m, l) in parallel (wave max and sum) and leave each split's weight in
-// LDS; each lane then accumulates its channels over the splits in order.
-constexpr int kMaxSplits = 1024;
-constexpr int kMergeChunk = 32;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_decode_merge_kernel(MxDecodeArgs d, float sl2) {
-  __shared__ float wts[4][kMaxSplits];
-  const MxAttnArgs& a = d.at;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wv;  // (b*Hq + h)*Sq + i
-  if (row >= static_cast<int64_t>(a.B) * a.Hq * a.Sq) return;  // whole wave; no block barrier
-  const int i = static_cast<int>(row % a.Sq);
-  const int64_t bh = row / a.Sq;
-  const int h = static_cast<int>(bh % a.Hq), b = static_cast<int>(bh / a.Hq);
-  const int G = a.Hq / a.Hkv;
-  const int64_t bg = static_cast<int64_t>(b) * a.Hkv + h / G;
-  const int col = (h % G) * a.Sq + i;
-  const float* base = d.part + (bg * d.nsplit * kDecodeCols + col) * (D + 2);
-  const int64_t stride = kDecodeCols * static_cast<int64_t>(D + 2);
-  // per-sequence lengths: only the splits that hold the entry's keys were written
-  const int ns = a.lens_k ? __builtin_amdgcn_readfirstlane(entry_splits(d, b)) : d.nsplit;
-  constexpr int PER = D / 64;
-  const int n0 = min(ns, kMergeChunk);
-  float o0[kMergeChunk][PER];
-#pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u)
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o0[u][k] = u < n0 ? base[u * stride + 2 + lane + 64 * k] : 0.0f;
-  float ms = -INFINITY, ls = 0.0f;
-  if (lane < ns) {
-    ms = base[lane * stride];
-    ls = base[lane * stride + 1];
-  }
-  float M = ms;
-  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, base[s * stride]);
-  M = wave_max(M);
-  if (M == -INFINITY) return;  // no split saw a key: the row is left unwritten
-  float L = 0.0f;
-  if (lane < ns) {
-    const float wgt = __builtin_amdgcn_exp2f((ms - M) * sl2);  // 0 when the split is empty
-    wts[wv][lane] = wgt;
-    L = fmaf(wgt, ls, L);
-  }
-  for (int s = lane + 64; s < ns; s += 64) {
-    const float wgt = __builtin_amdgcn_exp2f((base[s * stride] - M) * sl2);
-    wts[wv][s] = wgt;
-    L = fmaf(wgt, base[s * stride + 1], L);
-  }
-  L = wave_sum(L);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u) {
-    if (u < n0) {
-#pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][u], o0[u][k], acc[k]);
-    }
-  }
-  int s = kMergeChunk;
-  for (; s + 8 <= ns; s += 8) {
-    float o[8][PER];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[u][k] = base[(s + u) * stride + 2 + lane + 64 * k];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][s + u], o[u][k], acc[k]);
-  }
-  for (; s < ns; ++s)
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wts[wv][s], base[s * stride + 2 + lane + 64 * k], acc[k]);
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) a.o[row * D + lane + 64 * k] = acc[k] * inv;
+  // Arrival: once this wave's partial-state stores have completed (they
+  // are written through to the device-coherent level), it is counted; the
+  // wave that brings the group's count to its number of units (the splits
+  // of the padded extent, or those holding the entry's keys) merges the
+  // group, reading the partial states at that same level, and leaves the
+  // counter at 0 for the next call.  (An agent-scope release fence would
+  // also write back the whole L2 of the XCD, once per wave.)
+  wait_vmcnt<0>();
+  uint32_t before = 0;
+  if (lane == 0) before = __hip_atomic_fetch_add(d.cnt + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  const int units = COMPACT ? entry_splits(d, b) : d.nsplit;
+  if (static_cast<int>(before) != units - 1) return;
+  merge_group<D>(d, b, g, bg, sl2, lane);
+  if (lane == 0) __hip_atomic_store(d.cnt + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int UOS, int PNQ, int DUMP, int COMPACT>
@@ -1287,11 +1304,6 @@ hipError_t launch_decode_t(const MxDecodeArgs& d, hipStream_t s) {
   const int64_t nunits = static_cast<int64_t>(d.at.B) * d.at.Hkv * d.nsplit;
   hipLaunchKernelGGL((attn_decode_kernel<D, UOS, PNQ, DUMP, COMPACT>), dim3(static_cast<unsigned>((nunits + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, d, sl2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t rows = static_cast<int64_t>(d.at.B) * d.at.Hq * d.at.Sq;
-  hipLaunchKernelGGL((attn_decode_merge_kernel<D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s,
-                     d, sl2);
   return hipGetLastError();
 }
 

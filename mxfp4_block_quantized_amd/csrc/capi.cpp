@@ -19,10 +19,13 @@ int to_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Byte layout of the workspace used by mxattn_fwd.  MX modes: the KV tile
-// images first, then the Q~ codes and E8M0 bytes that only the dump
-// variants write (total: images only; total_dump: with Q~).
+// images first, then one arrival counter per (b, KV head) for the
+// short-query kernel (zeroed with the images), then the Q~ codes and E8M0
+// bytes that only the dump variants write (total: images and counters;
+// total_dump: with Q~).
 struct Layout {
   size_t off[6];  // MX: qc qs images img-bytes | FP16: images, q16
+  size_t cnt;     // MX: the arrival counters
   size_t total;
   size_t total_dump;
   int64_t skv_ld;
@@ -85,6 +88,7 @@ Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, in
     L.total = L.total_dump = cur;
   } else {
     L.off[2] = take(static_cast<size_t>(B) * Hkv * (skv_ld / mxk::kKvTile) * mxk::img_bytes(D));
+    L.cnt = take(static_cast<size_t>(B) * Hkv * sizeof(uint32_t));
     L.total = cur;
     // the kernel's Q~ (dump variants only), one row per query row
     const size_t q_rows = static_cast<size_t>(B) * Hq * Sq;
@@ -134,7 +138,8 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
   // MX modes: Q is quantized inside the attention kernels
   const int uos = (mode == MXATTN_OCP) ? 0 : 1;
   e = mxk::launch_quant_kv_images(k, v, static_cast<int64_t>(B) * Hkv, Skv, D, dt, uos,
-                                  w + L.off[2], lens_k, Hkv, s);
+                                  w + L.off[2], lens_k, Hkv,
+                                  reinterpret_cast<uint32_t*>(w + L.cnt), s);
   return to_status(e);
 }
 
@@ -206,13 +211,15 @@ int attn_common(const void* q, const void* k, const void* v, int dtype, int B, i
 
 // KV tiles per split: at least 4 (the per-split partial state is small next
 // to the keys it covers), more when the (b, KV head) groups alone give
-// about 2048 waves (8 per CU).
+// about 1024 waves (one workgroup of 4 waves per CU: the one-tile-ahead
+// stream of each wave still covers the memory latency, and a group's merge
+// reads half the partial states of 2048 waves).
 int decode_split_tiles(int B, int Hkv, int Skv) {
   const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kKvTile - 1) / mxk::kKvTile;
   const int64_t groups = static_cast<int64_t>(B) * Hkv;
-  int64_t st = (nt * groups + 2047) / 2048;
+  int64_t st = (nt * groups + 1023) / 1024;
   if (st < 4) st = 4;
-  if (st < (nt + 1023) / 1024) st = (nt + 1023) / 1024;  // at most 1024 splits (merge kernel)
+  if (st < (nt + 1023) / 1024) st = (nt + 1023) / 1024;  // at most 1024 splits per group
   if (st > nt) st = nt;
   return static_cast<int>(st);
 }
@@ -257,7 +264,7 @@ DecodeLayout make_decode_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, 
   // the Q~ regions of a decode shape are a few hundred bytes per query row:
   // always reserved, the partial states follow them
   dl.part = round_up(dl.L.total_dump, 256);
-  dl.total = dl.part + static_cast<size_t>(B) * Hkv * dl.nsplit * mxk::kDecodeCols * (D + 2) * sizeof(float);
+  dl.total = dl.part + static_cast<size_t>(B) * Hkv * dl.nsplit * mxk::kDecodeCols * mxk::decode_slot(D) * sizeof(float);
   return dl;
 }
 
@@ -300,6 +307,7 @@ int decode_common(const void* q, const void* k, const void* v, int dtype, int B,
   d.at.causal = causal;
   d.at.mode = mode;
   d.part = reinterpret_cast<float*>(w + dl.part);
+  d.cnt = reinterpret_cast<uint32_t*>(w + dl.L.cnt);
   d.split_tiles = dl.split_tiles;
   d.nsplit = dl.nsplit;
   // the busy splits numbered on the device (unit numbers are int there)

@@ -63,9 +63,12 @@ hipError_t launch_quant_cols(const void* x, int64_t batch, int64_t rows,
 // ntiles = ceil(rows / kKvTile); rows past the end are quantized as zeros.
 // lens (device, may be null): entry e of the batch holds lens[e / per_len]
 // valid rows (clamped to [0, rows]); its rows past that are zeros too.
+// cnt (device, may be null): batch words set to 0 (the short-query kernel's
+// arrival counters, one per (b, KV head)).
 hipError_t launch_quant_kv_images(const void* k, const void* v, int64_t batch, int rows,
                                   int D, Dtype dt, int uos, uint8_t* img,
-                                  const int32_t* lens, int per_len, hipStream_t stream);
+                                  const int32_t* lens, int per_len, uint32_t* cnt,
+                                  hipStream_t stream);
 
 // Dequantize n elements to fp32 (out_bf16 == 0) or bf16.
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n,
@@ -96,11 +99,13 @@ hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
 // Short-query attention over key splits: one wave per (b, KV head, split)
 // computes the partial softmax state of the (Hq/Hkv) x Sq queries of a GQA
-// group (at most kDecodeCols) over its keys; a second kernel merges the splits in
-// order into o.  Causal queries are aligned to the end of the keys.
+// group (at most kDecodeCols) over its keys; the last wave of a group to
+// finish (counted in cnt) merges the group's splits in order into o and sets
+// its counter back to 0.  Causal queries are aligned to the end of the keys.
 struct MxDecodeArgs {
   MxAttnArgs at;      // Q~, KV images, o, dump, shapes, mode (at.causal: end-aligned)
-  float* part;        // [B*Hkv*nsplit][kDecodeCols][D + 2]: m, l, unnormalized O per query slot
+  float* part;        // [B*Hkv*nsplit][kDecodeCols][decode_slot(D)]: m, l, 2 unused, unnormalized O
+  uint32_t* cnt;      // [B*Hkv] arrival counters, 0 on entry (left at 0)
   int split_tiles;    // KV tiles (128 keys) per split
   int nsplit;
   // per-sequence lengths only (at.lens_k set, B <= kCompactMaxB): waves take
@@ -110,6 +115,8 @@ struct MxDecodeArgs {
 };
 // Query columns of one short-query wave (one 32 x 32 matrix-core tile).
 constexpr int kDecodeCols = 32;
+// Floats per query column of a split's partial state (O 16-byte aligned).
+__host__ __device__ constexpr int decode_slot(int D) { return D + 4; }
 // Largest batch for which the short-query kernel numbers its busy splits
 // (each wave scans the B lengths).
 constexpr int kCompactMaxB = 256;

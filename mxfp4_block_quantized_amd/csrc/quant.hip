@@ -155,7 +155,8 @@ __device__ __forceinline__ int kimg_row(int kk) { return 8 * ((kk & 15) >> 2) + 
 template <typename In, int UOS, int D>
 __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
     const In* __restrict__ x, int rows, int ntiles, int blocks_per_batch,
-    uint8_t* __restrict__ img, const int32_t* __restrict__ lens, int per_len) {
+    uint8_t* __restrict__ img, const int32_t* __restrict__ lens, int per_len,
+    uint32_t* __restrict__ cnt) {
   constexpr int OPR = D / 8;  // octets per row
   constexpr int DH = D / 64;  // d-halves (one 64-wide contraction each)
   constexpr int IMG = img_bytes(D);
@@ -163,6 +164,8 @@ __global__ __launch_bounds__(kThreads) void quant_kimg_kernel(
   // octet index within this (b, KV head): up to ntiles * 128 * D/8, past
   // 32 bits for the longest key extents
   const int64_t o = static_cast<int64_t>(blockIdx.x % blocks_per_batch) * kThreads + threadIdx.x;
+  // the short-query kernel's arrival counter of this (b, KV head) starts at 0
+  if (cnt && o == 0) cnt[bgi] = 0u;
   if (o >= static_cast<int64_t>(ntiles) * kKvTile * OPR) return;  // whole quads: OPR is a multiple of 4
   const int kr = static_cast<int>(o / OPR);
   const int w = static_cast<int>(o % OPR);
@@ -317,13 +320,13 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 template <typename In, int UOS, int D>
 hipError_t launch_kv_images_t(const void* k, const void* v, int64_t batch, int rows,
                               int ntiles, uint8_t* img, const int32_t* lens, int per_len,
-                              hipStream_t stream) {
+                              uint32_t* cnt, hipStream_t stream) {
   // work items per (b, KV head) in 64 bits; the C ABI has checked that
   // batch * per-batch blocks fits the grid's 32-bit dimension
   const int64_t kper = (static_cast<int64_t>(ntiles) * kKvTile * (D / 8) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((quant_kimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * kper)),
                      dim3(kThreads), 0, stream, static_cast<const In*>(k), rows, ntiles, static_cast<int>(kper), img,
-                     lens, per_len);
+                     lens, per_len, cnt);
   constexpr int CPT = 16 / static_cast<int>(sizeof(In));
   const int64_t vper = (static_cast<int64_t>(ntiles) * (kKvTile / kBlock) * (D / CPT) + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((quant_vimg_kernel<In, UOS, D>), dim3(static_cast<unsigned>(batch * vper)),
@@ -335,23 +338,24 @@ hipError_t launch_kv_images_t(const void* k, const void* v, int64_t batch, int r
 template <typename In, int UOS>
 hipError_t launch_kv_images_d(const void* k, const void* v, int64_t batch, int rows, int D,
                               int ntiles, uint8_t* img, const int32_t* lens, int per_len,
-                              hipStream_t stream) {
-  return D == 64 ? launch_kv_images_t<In, UOS, 64>(k, v, batch, rows, ntiles, img, lens, per_len, stream)
-                 : launch_kv_images_t<In, UOS, 128>(k, v, batch, rows, ntiles, img, lens, per_len, stream);
+                              uint32_t* cnt, hipStream_t stream) {
+  return D == 64 ? launch_kv_images_t<In, UOS, 64>(k, v, batch, rows, ntiles, img, lens, per_len, cnt, stream)
+                 : launch_kv_images_t<In, UOS, 128>(k, v, batch, rows, ntiles, img, lens, per_len, cnt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quant_kv_images(const void* k, const void* v, int64_t batch, int rows,
                                   int D, Dtype dt, int uos, uint8_t* img,
-                                  const int32_t* lens, int per_len, hipStream_t stream) {
+                                  const int32_t* lens, int per_len, uint32_t* cnt,
+                                  hipStream_t stream) {
   if (batch <= 0 || rows <= 0) return hipSuccess;
   const int ntiles = (rows + kKvTile - 1) / kKvTile;
   if (dt == Dtype::BF16)
-    return uos ? launch_kv_images_d<uint16_t, 1>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream)
-               : launch_kv_images_d<uint16_t, 0>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream);
-  return uos ? launch_kv_images_d<float, 1>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream)
-             : launch_kv_images_d<float, 0>(k, v, batch, rows, D, ntiles, img, lens, per_len, stream);
+    return uos ? launch_kv_images_d<uint16_t, 1>(k, v, batch, rows, D, ntiles, img, lens, per_len, cnt, stream)
+               : launch_kv_images_d<uint16_t, 0>(k, v, batch, rows, D, ntiles, img, lens, per_len, cnt, stream);
+  return uos ? launch_kv_images_d<float, 1>(k, v, batch, rows, D, ntiles, img, lens, per_len, cnt, stream)
+             : launch_kv_images_d<float, 0>(k, v, batch, rows, D, ntiles, img, lens, per_len, cnt, stream);
 }
 
 hipError_t launch_quant_rows(const void* x, int64_t n, int64_t n_write, Dtype dt,

@@ -89,8 +89,9 @@ def test_workspace_and_tile_queries():
     assert L.mxattn_workspace_bytes(1, 2, 1, 64, 64, 96, 1, 3) == 0
     nb = L.mxattn_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
     # K~ + V~^T tile images: 17408 bytes per 128 keys (0.53125 B per element
-    # each); the Q~ regions only in the dump size
-    assert nb == 40 * 256 * 17408
+    # each), then one 4-byte arrival counter per (b, KV head) rounded to 256
+    # bytes; the Q~ regions only in the dump size
+    assert nb == 40 * 256 * 17408 + 256
     nd = L.mxattn_dump_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
     assert nd >= nb + 40 * 32760 * 128 * 17 // 32
     off, ld = mx.workspace_layout(1, 40, 40, 32760, 32760, 128, "bf16", "uos_pnq")

@@ -113,6 +113,53 @@ def test_decode_deterministic():
     assert torch.equal(a, b)
 
 
+def test_decode_arrival_counters():
+    """The split kernel counts each group's finished splits in the workspace
+    and the last one merges.  The counters are cleared with the KV images
+    (so a workspace filled with junk beforehand works) and left at zero by
+    every call, so consecutive prepared calls on one workspace, including
+    per-entry lengths with an empty entry (no split of it, nothing counted),
+    equal the same calls on fresh workspaces bit for bit; the largest split
+    count (1024 splits, 64 merge chunks) is covered too."""
+    torch, mx = gpu()
+    q, k, v = mxsynth.llm_decode(53, B=3, Hq=8, Hkv=2, Sq=2, Skv=5000, D=128)
+    qt, kt, vt = to_torch(q), to_torch(k), to_torch(v)
+    print("[case] decode counters: junk workspace, consecutive prepared calls", flush=True)
+    ws = mx.alloc_decode_workspace(qt, kt, "uos_pnq")
+    ws.fill_(0xFF)
+    ref = mx.attn_decode(qt, kt, vt, causal=True, mode="uos_pnq")
+    assert torch.equal(mx.attn_decode(qt, kt, vt, causal=True, mode="uos_pnq", workspace=ws), ref)
+    for i in range(3):
+        qi = to_torch(mxsynth.llm_decode(54 + i, B=3, Hq=8, Hkv=2, Sq=2, Skv=5000, D=128)[0])
+        want = mx.attn_decode(qi, kt, vt, causal=i % 2 == 0, mode="uos_pnq")
+        got = mx.attn_decode_prepared(qi, kt, ws, causal=i % 2 == 0, mode="uos_pnq")
+        assert torch.equal(got, want), f"prepared call {i}"
+    lens = [0, 3001, 5000]
+    wsv = mx.alloc_decode_workspace(qt, kt, "uos_efq")
+    wsv.fill_(0xFF)
+    mx.attn_prepare_varlen(qt, kt, vt, lens, mode="uos_efq", workspace=wsv)
+    want = mx.attn_decode_varlen(qt, kt, vt, lens, causal=True, mode="uos_efq")
+    for i in range(3):
+        got = mx.attn_decode_varlen_prepared(qt, kt, wsv, lens, causal=True, mode="uos_efq")
+        assert torch.equal(got, want), f"prepared per-entry-length call {i}"
+    assert not got[0].any(), "the entry with no key wrote rows"
+    # one group over 1024 splits of 8 tiles
+    q1, k1, v1 = mxsynth.llm_decode(57, B=1, Hq=4, Hkv=1, Sq=1, Skv=1 << 20, D=64)
+    q1t, k1t, v1t = to_torch(q1), to_torch(k1), to_torch(v1)
+    assert mx.decode_split(1, 1, 1 << 20) == 1024
+    print("[case] decode counters: 1024 splits", flush=True)
+    a = mx.attn_decode(q1t, k1t, v1t, causal=False, mode="uos_pnq")
+    ws1 = mx.attn_prepare(q1t, k1t, v1t, mode="uos_pnq",
+                          workspace=mx.alloc_decode_workspace(q1t, k1t, "uos_pnq"))
+    for i in range(2):
+        assert torch.equal(mx.attn_decode_prepared(q1t, k1t, ws1, mode="uos_pnq"), a)
+    rows = np.arange(4, dtype=np.int64)
+    ref1 = oracle.attn_rows(q1, k1, v1, causal=False, mode=MODE_IDS["uos_pnq"], bc=128,
+                            rows=rows, split=mx.decode_split(1, 1, 1 << 20))
+    err = np.abs(a.reshape(-1, 64).double().cpu().numpy() - ref1["o"])
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
 @functools.lru_cache(maxsize=1)
 def full_inputs(name):
     c = mxsynth.DECODE_CONFIGS[name]

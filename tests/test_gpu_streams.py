@@ -107,6 +107,13 @@ def test_graph_capture_and_replay():
     lk_d = torch.tensor([2500, 1333], dtype=torch.int32, device="cuda")
     ws_v = mx.alloc_workspace(q, k, "uos_pnq")
     ws_dv = mx.alloc_decode_workspace(qd, kd, "uos_efq")
+    # KV caches quantized once, outside the graph: the captured short-query
+    # calls then rely on their arrival counters returning to 0 after each call
+    ws_dp = mx.attn_prepare(qd, kd, vd, mode="uos_pnq",
+                            workspace=mx.alloc_decode_workspace(qd, kd, "uos_pnq"))
+    ws_dvp = mx.attn_prepare_varlen(qd, kd, vd, lk_d, mode="uos_pnq")
+    odp = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    odvp = torch.zeros(qd.shape, dtype=torch.float32, device="cuda")
     ov = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
     odv = torch.zeros(qd.shape, dtype=torch.float32, device="cuda")
     xc = torch.empty(M * K // 2, dtype=torch.uint8, device="cuda")
@@ -123,8 +130,12 @@ def test_graph_capture_and_replay():
                            workspace=ws_v, stream=stream)
         mx.attn_decode_varlen(qd, kd, vd, lk_d, causal=True, mode="uos_efq", out=odv,
                               workspace=ws_dv, stream=stream)
+        mx.attn_decode_prepared(qd, kd, ws_dp, causal=True, mode="uos_pnq", out=odp,
+                                stream=stream)
+        mx.attn_decode_varlen_prepared(qd, kd, ws_dvp, lk_d, causal=True, mode="uos_pnq",
+                                       out=odvp, stream=stream)
 
-    outs = (o, od, xc, xs, y, ov, odv)
+    outs = (o, od, xc, xs, y, ov, odv, odp, odvp)
     work()
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs]
