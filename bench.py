@@ -398,6 +398,9 @@ def cpu_baseline(q, k, v, c, name):
     flops = 4.0 * rows.size * c["S"] * c["D"] * (0.5 if c["causal"] else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "cpu_model": cpu_model(), "kind": "oracle", "seconds": dt,
+            # an extrapolation, not a measurement: the whole workload at the
+            # sample's rate
+            "full_problem_seconds_extrapolated": attn_flops(c) / (flops / dt),
             "sample": f"{name} UOS+PNQ, {rows.size} seeded query rows ({rows_per_head} from each "
                       f"of the {c['B'] * c['Hq']} heads) against all {c['S']} keys, binary64, "
                       f"including the K/V quantization of those heads"}
