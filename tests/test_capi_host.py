@@ -171,6 +171,29 @@ def test_decode_rejects_bad_args():
     assert L.mxattn_decode_workspace_bytes(1, 8, 2, 1, 1000, 128, 1, 3) > 0
 
 
+def test_decode_split_and_workspace_sizes():
+    """Split size: whole 128-key tiles, at least 4, about 1024 waves over
+    all (b, KV head) groups, at most 1024 splits per group, never more than
+    the keys.  Workspace: the prepare layout (KV images, one arrival counter
+    per (b, KV head) rounded to 256 bytes, the Q~ regions) followed by the
+    partial states, 32 query columns of D + 4 floats per split."""
+    L = mx.lib()
+    assert L.mxattn_decode_split(8, 8, 32768) == 16 * 128    # 64 groups x 16 splits
+    assert L.mxattn_decode_split(1, 8, 32768) == 4 * 128     # the 4-tile floor
+    assert L.mxattn_decode_split(1, 1, 1 << 20) == 8 * 128   # 1024 splits
+    assert L.mxattn_decode_split(1, 1, 300) == 3 * 128       # all the keys
+    for B, Hq, Hkv, Sq, Skv, D in ((8, 32, 8, 1, 32768, 128), (3, 8, 2, 2, 5000, 64)):
+        split = L.mxattn_decode_split(B, Hkv, Skv)
+        nsplit = -(-((Skv + 127) // 128 * 128) // split)
+        dump = L.mxattn_dump_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, 1, 3)
+        part = B * Hkv * nsplit * 32 * (D + 4) * 4
+        got = L.mxattn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, 1, 3)
+        assert got == (dump + 255) // 256 * 256 + part, (B, Skv, got, dump, part)
+        nb = L.mxattn_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, 1, 3)
+        img = B * Hkv * ((Skv + 127) // 128) * (17408 if D == 128 else 9216)
+        assert nb == img + (B * Hkv * 4 + 255) // 256 * 256
+
+
 def test_varlen_rejects_bad_args():
     L = mx.lib()
     P = FAKE
