@@ -329,7 +329,67 @@ def bench_prefill_varlen(torch, mx, reps=5, name="llm_prefill_varlen"):
             "frac_fp4_peak": flops / ms / 1e9 / FP4_PEAK_TFLOPS}
 
 
-def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
+def library_scaled_mm(torch, xc, xs, wc, ws, M, N, K, y, timed):
+    """The same MXFP4 operands (codes two E2M1 per byte, low nibble first;
+    E8M0 bytes per 32 along K) through torch's block-scaled matrix product
+    (hipBLASLt on this GPU), for comparison only: its time and its largest
+    difference from this library's bf16 output."""
+    # the library call takes whole 128-row blocks: a is padded with zero rows
+    Mp = (M + 127) // 128 * 128
+    ap = torch.zeros((Mp, K // 2), dtype=torch.uint8, device=xc.device)
+    ap[:M] = xc.view(M, K // 2)
+    sp = torch.full((Mp, K // 32), 127, dtype=torch.uint8, device=xc.device)
+    sp[:M] = xs.view(M, K // 32)
+    a4 = ap.view(torch.float4_e2m1fn_x2)
+    b4 = wc.view(N, K // 2).view(torch.float4_e2m1fn_x2)
+    sa = sp.view(torch.float8_e8m0fnu)
+    sb = ws.view(N, K // 32).view(torch.float8_e8m0fnu)
+    try:
+        r = torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+    except Exception as e:  # an unsupported shape or build: reported, not fatal
+        return {"error": repr(e)[:300]}
+    diff = (r[:M].float() - y.float()).abs().max().item()
+    ymax = y.float().abs().max().item()
+    del r
+    ms = timed(lambda: torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=torch.bfloat16))
+    return {"call": "torch._scaled_mm (float4_e2m1fn_x2 operands, float8_e8m0fnu scales, bf16 out)",
+            "rows": Mp, "ms": ms, "tflops": 2.0 * Mp * N * K / ms / 1e9,
+            "max_abs_diff_vs_library": diff, "max_abs_output": ymax}
+
+
+def library_attention(torch, qt, kt, vt, c, steps):
+    """torch's fused bf16 attention (the flash backend only, so that no
+    unfused fallback runs) on the same bf16 q, k, v, for comparison only."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    G = c["Hq"] // c["Hkv"]
+    kk = kt if G == 1 else kt.repeat_interleave(G, dim=1).contiguous()
+    vv = vt if G == 1 else vt.repeat_interleave(G, dim=1).contiguous()
+    fn = lambda: F.scaled_dot_product_attention(qt, kk, vv, is_causal=bool(c["causal"]))  # noqa: E731
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            o = fn()
+            torch.cuda.synchronize()
+            finite = bool(torch.isfinite(o).all().item())
+            del o
+            warm(torch, fn)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+    except Exception as e:  # no fused kernel for this build or shape: reported, not fatal
+        return {"error": repr(e)[:300]}
+    ms = e0.elapsed_time(e1) / steps
+    f = attn_flops(c)
+    return {"call": "torch.nn.functional.scaled_dot_product_attention, flash backend, bf16",
+            "ms": ms, "tflops": f / ms / 1e9, "frac_bf16_peak": f / ms / 1e9 / BF16_PEAK_TFLOPS,
+            "finite": finite}
+
+
+def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up", library=False):
     import mxsynth
     g = mxsynth.GEMM_CONFIGS[name]
     M, N, K = g["M"], g["N"], g["K"]
@@ -361,13 +421,17 @@ def bench_gemm(torch, mx, reps=10, name="dit14_ffn_up"):
     lin_ms = timed(lambda: (mx.quantize(xt, "uos", xc, xs),
                             mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=work)))
     alg_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
-    return {"workload": f"{name}: x [{M}, {K}] bf16 (N(0,1), 1% channels x20) times UOS-MXFP4 "
-                        f"weight [{N}, {K}] (Student-t(3)*0.02, 0.1% x50), bf16 output",
-            "flops": flops, "algorithmic_bytes": alg_bytes,
-            "traffic": read_traffic(kernel_source_sha(GEMM_SOURCES), name, "gemm_mx_kernel"),
-            "gemm_ms": gemm_ms, "gemm_tflops": flops / gemm_ms / 1e9,
-            "gemm_frac_fp4_peak": flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS,
-            "linear_w4a4_ms": lin_ms, "linear_w4a4_tflops": flops / lin_ms / 1e9}
+    res = {"workload": f"{name}: x [{M}, {K}] bf16 (N(0,1), 1% channels x20) times UOS-MXFP4 "
+                       f"weight [{N}, {K}] (Student-t(3)*0.02, 0.1% x50), bf16 output",
+           "flops": flops, "algorithmic_bytes": alg_bytes,
+           "traffic": read_traffic(kernel_source_sha(GEMM_SOURCES), name, "gemm_mx_kernel"),
+           "gemm_ms": gemm_ms, "gemm_tflops": flops / gemm_ms / 1e9,
+           "gemm_frac_fp4_peak": flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS,
+           "linear_w4a4_ms": lin_ms, "linear_w4a4_tflops": flops / lin_ms / 1e9}
+    if library:
+        mx.gemm(xc, xs, wc, ws, M, N, K, out=y, workspace=work)
+        res["library_scaled_mm"] = library_scaled_mm(torch, xc, xs, wc, ws, M, N, K, y, timed)
+    return res
 
 
 def cpu_model() -> str:
@@ -444,6 +508,12 @@ def main():
                     help="only the standalone quantizer, the GEMM and the decode sections "
                          "(for profiling them alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--library-attention", action="store_true",
+                    help="also time torch's fused bf16 attention on the headline workload "
+                         "(a comparison, off by default)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch's block-scaled MXFP4 matrix product on the same "
+                         "GEMM operands (a comparison, off by default)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size "
                          "reference for hardware byte counters)")
@@ -474,7 +544,7 @@ def main():
         if not args.no_quantizer:
             res["quantizer"] = bench_quantizer(torch, mx, reps=3)
         if not args.no_gemm:
-            res["gemm"] = bench_gemm(torch, mx, reps=3)
+            res["gemm"] = bench_gemm(torch, mx, reps=3, library=args.library_gemm)
         if not args.no_decode:
             res["decode"] = bench_decode(torch, mx, reps=20, varlen=not args.no_varlen)
         print(json.dumps(res), flush=True)
@@ -490,6 +560,8 @@ def main():
                                args.warmup)
     along = bench_attention(torch, mx, args.workload, qt, kt, vt, modes[1:],
                             max(3, args.steps // 2), max(1, args.warmup // 2)) if modes[1:] else None
+    library = library_attention(torch, qt, kt, vt, c, max(3, args.steps // 2)) \
+        if args.library_attention else None
     del qt, kt, vt
     torch.cuda.empty_cache()
     hr = headline["modes"][head]
@@ -521,6 +593,8 @@ def main():
         "roofline": roofline,
         "alongside": along["modes"] if along else {},
     }
+    if library is not None:
+        out["library_attention"] = library
     sections = [w for w in args.sections.split(",") if w and w != args.workload]
     if sections:
         out["attention"] = {}
@@ -535,7 +609,7 @@ def main():
         out["quantizer"] = bench_quantizer(torch, mx)
         log(f"[bench] quantizer: {out['quantizer']}")
     if not args.no_gemm:
-        out["gemm"] = bench_gemm(torch, mx)
+        out["gemm"] = bench_gemm(torch, mx, library=args.library_gemm)
         log(f"[bench] gemm: {out['gemm']}")
     if not args.no_decode:
         out["decode"] = bench_decode(torch, mx, varlen=not args.no_varlen)
