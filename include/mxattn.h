@@ -134,7 +134,8 @@ size_t mxattn_dump_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv,
  * array `off` of 6 entries):
  *   off[2] KV tile images [B][Hkv][skv_ld/128][off[3]], at offset 0
  *   off[0] Q~ codes [B][Hq][Sq][D/2]      off[1] Q~ scales [B][Hq][Sq][D/32]
- *          after the images, inside the dump workspace only (written only
+ *          after the images and the arrival counters (B*Hkv 32-bit words
+ *          rounded to 256 bytes), inside the dump workspace only (written only
  *          by the dump entry points: the attention kernels quantize Q
  *          themselves, and the dump variants store that Q~ here; the
  *          short-query workspace always holds these regions)
