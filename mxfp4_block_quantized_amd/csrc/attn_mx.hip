@@ -1288,13 +1288,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(MxDecodeArgs d
   // group, reading the partial states at that same level, and leaves the
   // counter at 0 for the next call.  (An agent-scope release fence would
   // also write back the whole L2 of the XCD, once per wave.)
+  // (the empty asm statements keep the compiler from moving memory
+  // operations across the wait and the increment)
+  asm volatile("" ::: "memory");
   wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
   uint32_t before = 0;
   if (lane == 0) before = __hip_atomic_fetch_add(d.cnt + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   const int units = COMPACT ? entry_splits(d, b) : d.nsplit;
   if (static_cast<int>(before) != units - 1) return;
+  asm volatile("" ::: "memory");
   merge_group<D>(d, b, g, bg, sl2, lane);
+  asm volatile("" ::: "memory");
   if (lane == 0) __hip_atomic_store(d.cnt + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
