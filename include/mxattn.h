@@ -118,8 +118,10 @@ int mxq_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n,
  * mxattn_fwd_varlen without a dump) for these sizes and mode (bytes; 0 for
  * invalid arguments).  The workspace holds the quantized K/V operands (MX
  * modes: the KV tile images, followed by one 32-bit arrival counter per
- * (b, KV head) that the short-query calls use; mxattn_prepare and
- * mxattn_prepare_varlen set them to 0) or the 16-bit operands (FP16 mode).
+ * (b, KV head) that the short-query calls use (mxattn_prepare and
+ * mxattn_prepare_varlen set them to 0) and the prefill kernel's 8-word work
+ * queue (cleared by every attention call before its kernel)) or the 16-bit
+ * operands (FP16 mode).
  * mxattn_dump_workspace_bytes: the larger workspace of the dump entry points
  * (mxattn_fwd_dump, mxattn_fwd_varlen with a dump), which also receives the
  * kernel's Q~; 0 for the FP16 mode, which has no dump.
@@ -134,8 +136,9 @@ size_t mxattn_dump_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv,
  * array `off` of 6 entries):
  *   off[2] KV tile images [B][Hkv][skv_ld/128][off[3]], at offset 0
  *   off[0] Q~ codes [B][Hq][Sq][D/2]      off[1] Q~ scales [B][Hq][Sq][D/32]
- *          after the images and the arrival counters (B*Hkv 32-bit words
- *          rounded to 256 bytes), inside the dump workspace only (written only
+ *          after the images, the arrival counters (B*Hkv 32-bit words
+ *          rounded to 256 bytes) and the work queue (256 bytes), inside the
+ *          dump workspace only (written only
  *          by the dump entry points: the attention kernels quantize Q
  *          themselves, and the dump variants store that Q~ here; the
  *          short-query workspace always holds these regions)
@@ -213,7 +216,9 @@ int mxattn_fwd(const void *q, const void *k, const void *v, int dtype,
  * inputs, else fp16; V fp16), and fp16 Q for fp32 inputs.
  * mxattn_fwd_prepared: the fused attention kernel alone, reading the
  * operands a previous mxattn_prepare with the same sizes, dtype and mode
- * left in the workspace, and q (quantized in the kernel in the MX modes,
+ * left in the workspace (in the MX modes it also writes the workspace's
+ * small work-queue region, which schedules the kernel's query tiles over
+ * the XCDs: calls that overlap on one workspace race), and q (quantized in the kernel in the MX modes,
  * read directly in FP16 mode with bf16 inputs; only FP16 mode with fp32
  * inputs does not read it, and then it may be NULL).  k is not read and may
  * be NULL.  Arguments as for mxattn_fwd.  mxattn_fwd == mxattn_prepare followed by mxattn_fwd_prepared.
@@ -223,7 +228,7 @@ int mxattn_prepare(const void *q, const void *k, const void *v, int dtype,
                    void *workspace, size_t ws_bytes, void *stream);
 int mxattn_fwd_prepared(const void *q, const void *k, int dtype, int B,
                         int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                        int mode, float *o, const void *workspace,
+                        int mode, float *o, void *workspace,
                         size_t ws_bytes, void *stream);
 
 /*

@@ -769,10 +769,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   // (nqb+1 KV tiles in all, the longer one first), so every workgroup of a
   // head does the same work and the fixed cost per workgroup is spread over
   // twice the tiles.
+  // The list is cut into 8 runs, run x for XCD x; the first 7/8 of run x
+  // go to its workgroups by index, and the rest through its work-queue
+  // counter, which the XCD's later workgroups (the grid holds spares) pop
+  // until the run is done and then turn to the other runs' counters, so
+  // that no XCD idles while another still has items (the XCDs' speeds
+  // differ by a few percent).  A workgroup that finds every run done exits.
   const int nslot = CAUSAL ? (nqb + 1) / 2 : nqb;  // workgroups per query head
-  const int nwg = gridDim.x;
+  const int nitems = nslot * a.Hq * a.B;
   const int xcd = blockIdx.x & 7;
-  const int gi = (nwg >> 3) * xcd + min(xcd, nwg & 7) + (static_cast<int>(blockIdx.x) >> 3);
+  const int per = nitems >> 3, extra = nitems & 7;
+  const int cnt_x = per + (xcd < extra ? 1 : 0);
+  const int j = static_cast<int>(blockIdx.x) >> 3;
+  int gi;
+  if (j < cnt_x - cnt_x / 8) {
+    gi = per * xcd + min(xcd, extra) + j;
+  } else {
+    __shared__ int s_item;
+    if (threadIdx.x == 0) {
+      int item = -1;
+      for (int v = 0; v < 8; ++v) {
+        const int y = (xcd + v) & 7;
+        const int cy = per + (y < extra ? 1 : 0);
+        const uint32_t k = __hip_atomic_fetch_add(a.queue + y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (k < static_cast<uint32_t>(cy / 8)) {
+          item = per * y + min(y, extra) + (cy - cy / 8) + static_cast<int>(k);
+          break;
+        }
+      }
+      s_item = item;
+    }
+    __syncthreads();
+    gi = s_item;
+    if (gi < 0) return;  // whole workgroup: every item is taken
+  }
   const int G = a.Hq / a.Hkv;
   const int per_group = G * nslot;
   const int ngroups = a.B * a.Hkv;
@@ -963,13 +993,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mx_kernel(MxAttnArgs a, floa
   store_o<D>(orow, ofin, half);
 }
 
+// Clears the prefill kernel's work-queue counters (a kernel, not a memset,
+// so that captured graphs replay it faithfully).
+__global__ void clear_queue_kernel(uint32_t* q) {
+  if (threadIdx.x < kQueueWords) q[threadIdx.x] = 0u;
+}
+
 template <int D, int UOS, int PNQ, int CAUSAL, int DUMP>
 hipError_t launch_t(const MxAttnArgs& a, hipStream_t s) {
   const int nqb = (a.Sq + kMxQTile - 1) / kMxQTile;
   // causal: query tiles in pairs (see attn_mx_kernel)
-  dim3 grid(static_cast<unsigned>(CAUSAL ? (nqb + 1) / 2 : nqb) * a.Hq * a.B);
+  const int64_t nitems = static_cast<int64_t>(CAUSAL ? (nqb + 1) / 2 : nqb) * a.Hq * a.B;
+  hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, s, a.queue);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
-  hipLaunchKernelGGL((attn_mx_kernel<D, UOS, PNQ, CAUSAL, DUMP>), grid, dim3(kThreads), 0, s, a, sl2);
+  hipLaunchKernelGGL((attn_mx_kernel<D, UOS, PNQ, CAUSAL, DUMP>), dim3(static_cast<unsigned>(prefill_grid(nitems))),
+                     dim3(kThreads), 0, s, a, sl2);
   return hipGetLastError();
 }
 

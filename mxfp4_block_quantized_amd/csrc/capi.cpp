@@ -20,12 +20,14 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Byte layout of the workspace used by mxattn_fwd.  MX modes: the KV tile
 // images first, then one arrival counter per (b, KV head) for the
-// short-query kernel (zeroed with the images), then the Q~ codes and E8M0
-// bytes that only the dump variants write (total: images and counters;
-// total_dump: with Q~).
+// short-query kernel (zeroed with the images), the prefill kernel's work
+// queue (cleared before each launch), then the Q~ codes and E8M0 bytes that
+// only the dump variants write (total: images and counters; total_dump:
+// with Q~).
 struct Layout {
   size_t off[6];  // MX: qc qs images img-bytes | FP16: images, q16
   size_t cnt;     // MX: the arrival counters
+  size_t queue;   // MX: the work-queue counters
   size_t total;
   size_t total_dump;
   int64_t skv_ld;
@@ -42,6 +44,10 @@ constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;
 bool attn_grids_fit(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, int mode) {
   const int64_t qt = mode == MXATTN_FP16 ? mxk::kQTile : mxk::kMxQTile;
   if (static_cast<int64_t>(B) * Hq * ((Sq + qt - 1) / qt) * 256 > kMaxItems) return false;
+  // the MX prefill grid adds its per-XCD spares
+  if (mode != MXATTN_FP16 &&
+      mxk::prefill_grid(static_cast<int64_t>(B) * Hq * ((Sq + qt - 1) / qt)) * 256 > kMaxItems)
+    return false;
   if (mode == MXATTN_FP16) {
     const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kF16KvTile - 1) / mxk::kF16KvTile;
     if (static_cast<int64_t>(B) * Hkv * nt * 256 > kMaxItems) return false;
@@ -89,6 +95,7 @@ Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, in
   } else {
     L.off[2] = take(static_cast<size_t>(B) * Hkv * (skv_ld / mxk::kKvTile) * mxk::img_bytes(D));
     L.cnt = take(static_cast<size_t>(B) * Hkv * sizeof(uint32_t));
+    L.queue = take(mxk::kQueueWords * sizeof(uint32_t));
     L.total = cur;
     // the kernel's Q~ (dump variants only), one row per query row
     const size_t q_rows = static_cast<size_t>(B) * Hq * Sq;
@@ -146,10 +153,10 @@ int run_prepare(const void* q, const void* k, const void* v, int dtype, int B, i
 // The fused attention kernel on a prepared workspace.
 int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int Sq,
                   int Skv, int D, int causal, int mode, float* o, const Layout& L,
-                  const void* ws, const int32_t* row_slot, uint8_t* p_codes,
+                  void* ws, const int32_t* row_slot, uint8_t* p_codes,
                   uint8_t* p_scales, hipStream_t s, const int32_t* lens_q = nullptr,
                   const int32_t* lens_k = nullptr) {
-  const uint8_t* w = static_cast<const uint8_t*>(ws);
+  uint8_t* w = static_cast<uint8_t*>(ws);
   if (mode == MXATTN_FP16) {
     mxk::F16AttnArgs a{};
     if (dtype == MX_F32) {
@@ -171,9 +178,9 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
   a.q_bf16 = dtype == MX_BF16;
   a.lens_q = lens_q;
   a.lens_k = lens_k;
-  // written only by the dump variant, whose workspace is writable
-  a.qc = const_cast<uint8_t*>(w + L.off[0]);
-  a.qs = const_cast<uint8_t*>(w + L.off[1]);
+  // written only by the dump variant
+  a.qc = w + L.off[0];
+  a.qs = w + L.off[1];
   a.img = w + L.off[2];
   a.o = o;
   a.row_slot = row_slot;
@@ -183,6 +190,7 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
   a.skv_ld = L.skv_ld;
   a.causal = causal;
   a.mode = mode;
+  a.queue = reinterpret_cast<uint32_t*>(w + L.queue);
   return to_status(mxk::launch_attn_mx(a, s));
 }
 
@@ -429,7 +437,7 @@ int mxattn_prepare(const void* q, const void* k, const void* v, int dtype, int B
 
 int mxattn_fwd_prepared(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                         int Sq, int Skv, int D, int causal, int mode, float* o,
-                        const void* workspace, size_t ws_bytes, void* stream) {
+                        void* workspace, size_t ws_bytes, void* stream) {
   Layout L;
   int st = check_attn_call(q, k, nullptr, dtype, B, Hq, Hkv, Sq, Skv, D, causal, mode,
                            workspace, ws_bytes, false, false, &L);

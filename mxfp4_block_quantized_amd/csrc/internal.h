@@ -94,8 +94,23 @@ struct MxAttnArgs {
   int64_t skv_ld;
   int causal;
   int mode;  // 1 OCP, 2 UOS, 3 UOS+PNQ, 4 UOS+EFQ
+  // the prefill kernel's work-queue counters (kQueueWords words; the
+  // launcher clears them before the kernel)
+  uint32_t* queue;
 };
 hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
+
+// Work queue of the prefill kernel: its items (query tiles, or causal pairs
+// of them) are listed in 8 runs, one per XCD; a workgroup on XCD x takes
+// item j of run x when j falls in the run's first 7/8, and otherwise pops
+// the run's remaining items from counter x, then the other runs' (so the
+// XCDs that run faster take over the ends of the slower ones).  The grid
+// holds per-XCD spares for that.
+constexpr int kQueueWords = 8;
+__host__ __device__ constexpr int64_t prefill_items_per_xcd(int64_t nitems) { return (nitems + 7) / 8; }
+__host__ __device__ constexpr int64_t prefill_grid(int64_t nitems) {
+  return 8 * (prefill_items_per_xcd(nitems) + prefill_items_per_xcd(nitems) / 16 + 2);
+}
 
 // Short-query attention over key splits: one wave per (b, KV head, split)
 // computes the partial softmax state of the (Hq/Hkv) x Sq queries of a GQA

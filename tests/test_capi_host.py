@@ -90,8 +90,9 @@ def test_workspace_and_tile_queries():
     nb = L.mxattn_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
     # K~ + V~^T tile images: 17408 bytes per 128 keys (0.53125 B per element
     # each), then one 4-byte arrival counter per (b, KV head) rounded to 256
-    # bytes; the Q~ regions only in the dump size
-    assert nb == 40 * 256 * 17408 + 256
+    # bytes and the prefill work queue (8 words, 256 bytes); the Q~ regions
+    # only in the dump size
+    assert nb == 40 * 256 * 17408 + 256 + 256
     nd = L.mxattn_dump_workspace_bytes(1, 40, 40, 32760, 32760, 128, 1, 3)
     assert nd >= nb + 40 * 32760 * 128 * 17 // 32
     off, ld = mx.workspace_layout(1, 40, 40, 32760, 32760, 128, "bf16", "uos_pnq")
@@ -176,7 +177,8 @@ def test_decode_split_and_workspace_sizes():
     all (b, KV head) groups, at most 1024 splits per group, never more than
     the keys.  Workspace: the prepare layout (KV images, one arrival counter
     per (b, KV head) rounded to 256 bytes, the Q~ regions) followed by the
-    partial states, 32 query columns of D + 4 floats per split."""
+    partial states, 32 query columns of D + 4 floats per split; the prefill
+    work queue (8 words) after the counters."""
     L = mx.lib()
     assert L.mxattn_decode_split(8, 8, 32768) == 16 * 128    # 64 groups x 16 splits
     assert L.mxattn_decode_split(1, 8, 32768) == 4 * 128     # the 4-tile floor
@@ -191,7 +193,7 @@ def test_decode_split_and_workspace_sizes():
         assert got == (dump + 255) // 256 * 256 + part, (B, Skv, got, dump, part)
         nb = L.mxattn_workspace_bytes(B, Hq, Hkv, Sq, Skv, D, 1, 3)
         img = B * Hkv * ((Skv + 127) // 128) * (17408 if D == 128 else 9216)
-        assert nb == img + (B * Hkv * 4 + 255) // 256 * 256
+        assert nb == img + (B * Hkv * 4 + 255) // 256 * 256 + 256
 
 
 def test_varlen_rejects_bad_args():
