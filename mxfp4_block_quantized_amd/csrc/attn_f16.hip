@@ -271,11 +271,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f16_kernel(F16AttnArgs a, fl
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nqb = (a.Sq + kQTile - 1) / kQTile;
   // workgroup -> (head, query tile): a contiguous run of heads per XCD
-  // (workgroups are dispatched round-robin over the 8 XCDs); causal: the
-  // longest query tiles of a head first
-  const int nwg = gridDim.x;
+  // (workgroups are dispatched round-robin over the 8 XCDs), the last 1/8
+  // of each run through its work-queue counter, which the other XCDs also
+  // drain once their own runs are done (as in the MXFP4 kernel); causal:
+  // the longest query tiles of a head first
+  const int nitems = nqb * a.Hq * a.B;
   const int xcd = blockIdx.x & 7;
-  const int gi = (nwg >> 3) * xcd + min(xcd, nwg & 7) + (static_cast<int>(blockIdx.x) >> 3);
+  const int per = nitems >> 3, extra = nitems & 7;
+  const int cnt_x = per + (xcd < extra ? 1 : 0);
+  const int j = static_cast<int>(blockIdx.x) >> 3;
+  int gi;
+  if (j < cnt_x - cnt_x / 8) {
+    gi = per * xcd + min(xcd, extra) + j;
+  } else {
+    __shared__ int s_item;
+    if (threadIdx.x == 0) {
+      int item = -1;
+      for (int v = 0; v < 8; ++v) {
+        const int y = (xcd + v) & 7;
+        const int cy = per + (y < extra ? 1 : 0);
+        const uint32_t k = __hip_atomic_fetch_add(a.queue + y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (k < static_cast<uint32_t>(cy / 8)) {
+          item = per * y + min(y, extra) + (cy - cy / 8) + static_cast<int>(k);
+          break;
+        }
+      }
+      s_item = item;
+    }
+    __syncthreads();
+    gi = s_item;
+    if (gi < 0) return;  // whole workgroup: every item is taken
+  }
   const int hb = gi / nqb;
   const int qb = CAUSAL ? nqb - 1 - gi % nqb : gi % nqb;
   const int h = hb % a.Hq;
@@ -466,9 +492,18 @@ __global__ __launch_bounds__(256) void f32_to_f16_kernel(const float* __restrict
   if (i < n_write) y[i] = to_f16(i < n ? x[i] : 0.0f);
 }
 
+// Clears the work-queue counters (a kernel, so that graphs replay it).
+__global__ void clear_f16_queue_kernel(uint32_t* q) {
+  if (threadIdx.x < kQueueWords) q[threadIdx.x] = 0u;
+}
+
 template <int D, int QK_F16>
 hipError_t launch_c(const F16AttnArgs& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((a.Sq + kQTile - 1) / kQTile) * a.Hq * a.B);
+  const int64_t nitems = static_cast<int64_t>((a.Sq + kQTile - 1) / kQTile) * a.Hq * a.B;
+  dim3 grid(static_cast<unsigned>(prefill_grid(nitems)));
+  hipLaunchKernelGGL(clear_f16_queue_kernel, dim3(1), dim3(64), 0, s, a.queue);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const float sl2 = static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(D)));
   if (a.causal)
     hipLaunchKernelGGL((attn_f16_kernel<D, QK_F16, 1>), grid, dim3(kThreads), 0, s, a, sl2);

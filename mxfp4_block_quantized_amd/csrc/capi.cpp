@@ -44,9 +44,8 @@ constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;
 bool attn_grids_fit(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, int mode) {
   const int64_t qt = mode == MXATTN_FP16 ? mxk::kQTile : mxk::kMxQTile;
   if (static_cast<int64_t>(B) * Hq * ((Sq + qt - 1) / qt) * 256 > kMaxItems) return false;
-  // the MX prefill grid adds its per-XCD spares
-  if (mode != MXATTN_FP16 &&
-      mxk::prefill_grid(static_cast<int64_t>(B) * Hq * ((Sq + qt - 1) / qt)) * 256 > kMaxItems)
+  // the prefill grids add their per-XCD spares
+  if (mxk::prefill_grid(static_cast<int64_t>(B) * Hq * ((Sq + qt - 1) / qt)) * 256 > kMaxItems)
     return false;
   if (mode == MXATTN_FP16) {
     const int64_t nt = (static_cast<int64_t>(Skv) + mxk::kF16KvTile - 1) / mxk::kF16KvTile;
@@ -91,6 +90,7 @@ Layout make_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, in
     const size_t nt = (static_cast<size_t>(Skv) + mxk::kF16KvTile - 1) / mxk::kF16KvTile;
     L.off[0] = take(static_cast<size_t>(B) * Hkv * nt * mxk::f16_img_bytes(D));  // K / V^T images
     if (dtype == MX_F32) L.off[1] = take(static_cast<size_t>(B) * Hq * Sq * D * 2);  // Q fp16
+    L.queue = take(mxk::kQueueWords * sizeof(uint32_t));
     L.total = L.total_dump = cur;
   } else {
     L.off[2] = take(static_cast<size_t>(B) * Hkv * (skv_ld / mxk::kKvTile) * mxk::img_bytes(D));
@@ -171,6 +171,7 @@ int run_attention(const void* q, const void* k, int dtype, int B, int Hq, int Hk
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Skv = Skv; a.D = D;
     a.skv_ld = L.skv_ld;
     a.causal = causal;
+    a.queue = reinterpret_cast<uint32_t*>(w + L.queue);
     return to_status(mxk::launch_attn_f16(a, s));
   }
   mxk::MxAttnArgs a{};

@@ -100,8 +100,8 @@ struct MxAttnArgs {
 };
 hipError_t launch_attn_mx(const MxAttnArgs& a, hipStream_t stream);
 
-// Work queue of the prefill kernel: its items (query tiles, or causal pairs
-// of them) are listed in 8 runs, one per XCD; a workgroup on XCD x takes
+// Work queue of the prefill kernels (both attention kernels): their items
+// (query tiles, or causal pairs of them) are listed in 8 runs, one per XCD; a workgroup on XCD x takes
 // item j of run x when j falls in the run's first 7/8, and otherwise pops
 // the run's remaining items from counter x, then the other runs' (so the
 // XCDs that run faster take over the ends of the slower ones).  The grid
@@ -159,6 +159,7 @@ struct F16AttnArgs {
   int64_t skv_ld;
   int causal;
   int qk_f16;  // 1: q/k are fp16, 0: bf16
+  uint32_t* queue;  // work-queue counters as for the MXFP4 prefill kernel
 };
 hipError_t launch_attn_f16(const F16AttnArgs& a, hipStream_t stream);
 
